@@ -1,0 +1,126 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail a pin.
+
+Each mutant is a copy of oracle/moe_ep_oracle.c with one plausible mistake
+(a wrong order, a dropped term, a wrong index, a fused multiply-add, the
+wrong tie rule ...), compiled with gcc into a temporary directory. The pins
+of test_oracle_pins.py are run against it; at least one must fail. This
+shows the pins are tight enough to catch what a plausible bug would change.
+"""
+import multiprocessing as mp
+import subprocess
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import test_oracle_pins as pins
+
+MUTANTS = {
+    "slots_descending_tokens": (
+        "        for (int64_t t = 0; t < T; ++t) {\n            /* entries of token t",
+        "        for (int64_t t = T - 1; t >= 0; --t) {\n            /* entries of token t"),
+    "picks_reverse_router_order": (
+        "            int32_t j = 0;\n            for (int32_t k = 0; k < K; ++k) {",
+        "            int32_t j = 0;\n            for (int32_t k = K - 1; k >= 0; --k) {"),
+    "padding_not_filtered": (
+        "                if (id < 0 || id >= E)\n                    continue;\n                if (id / e_local == d)",
+        "                if (id >= E)\n                    continue;\n                if (id / e_local == d)"),
+    "global_instead_of_local_id": (
+        "send_eloc[meta + j] = id - d * e_local;",
+        "send_eloc[meta + j] = id;"),
+    "weight_of_wrong_pick": (
+        "send_w[meta + j] = topk_weights[t * K + k];",
+        "send_w[meta + j] = topk_weights[t * K + (k + 1) % K];"),
+    "batch_sources_descending": (
+        "    for (int32_t s = 0; s < W; ++s) {\n        int64_t cnt = recv_cnt[s * cnt_rank_stride];\n        if (cnt < 0 || cnt > cap) {\n            err |= ORACLE_ERR_CNT;\n            cnt = cnt < 0 ? 0 : cap;\n        }\n        for (int64_t slot = 0; slot < cnt; ++slot) {\n            for (int32_t j = 0; j < slots; ++j) {\n                int32_t e = recv_eloc",
+        "    for (int32_t s = W - 1; s >= 0; --s) {\n        int64_t cnt = recv_cnt[s * cnt_rank_stride];\n        if (cnt < 0 || cnt > cap) {\n            err |= ORACLE_ERR_CNT;\n            cnt = cnt < 0 ? 0 : cap;\n        }\n        for (int64_t slot = 0; slot < cnt; ++slot) {\n            for (int32_t j = 0; j < slots; ++j) {\n                int32_t e = recv_eloc"),
+    "reduce_fused_multiply_add": (
+        "                    float prod = y * wgt;\n                    acc = acc + prod;",
+        "                    acc = __builtin_fmaf(y, wgt, acc);"),
+    "reduce_drops_last_pick": (
+        "                for (int32_t j = 0; j < slots; ++j) {\n                    int64_t at",
+        "                for (int32_t j = 0; j < slots - 1; ++j) {\n                    int64_t at"),
+    "reduce_weight_ignored": (
+        "                    float prod = y * wgt;",
+        "                    float prod = y;"),
+    "round_half_up": (
+        "(dropped == 0x8000u && (kept & 1u))",
+        "(dropped == 0x8000u)"),
+    "truncate_instead_of_round": (
+        "        kept += 1u;                /* may carry",
+        "        kept += 0u;                /* may carry"),
+    "unpack_skips_first_rank": (
+        "            for (int32_t d = 0; d < W; ++d) {\n                int32_t slot = token_slot[t * W + d];",
+        "            for (int32_t d = 1; d < W; ++d) {\n                int32_t slot = token_slot[t * W + d];"),
+    "reduce_row_of_first_pick": (
+        "                    int32_t row = recv_row[at];",
+        "                    int32_t row = recv_row[at - j];"),
+    "expert_rows_transposed_stride": (
+        "e * y_expert_stride + row * y_row_stride + h",
+        "row * y_expert_stride + e * y_row_stride + h"),
+}
+
+
+def _pin_battery():
+    """Fast subset of the pins, each a zero-argument callable."""
+    return [
+        pins.test_golden_pack,
+        pins.test_golden_batch,
+        lambda: pins.test_golden_reduce("bf16"),
+        lambda: pins.test_golden_reduce("f32"),
+        lambda: pins.test_golden_unpack("bf16"),
+        pins.test_golden_bf16_rounding,
+        lambda: pins.test_golden_products_rounded_before_add("bf16"),
+        lambda: pins.test_pack_exhaustive_micro(2, 2),
+        pins.test_combine_dense_brute_force_tiny,
+        lambda: pins.test_identity_round_trip_returns_a1(1),
+        lambda: pins.test_power_of_two_experts(1),
+        lambda: pins.test_invariants_full_size_metadata(1),
+    ]
+
+
+def _child(lib_path, q):
+    import faulthandler
+    faulthandler.disable()          # a crashing mutant is an expected outcome
+    failed = 0
+    with oracle.use_library(lib_path):
+        for fn in _pin_battery():
+            try:
+                fn()
+            except Exception:       # an assertion or a rejected call
+                failed += 1
+    q.put(failed)
+
+
+def _failing_pins(lib_path):
+    """Number of failing pins; a mutant that crashes its (forked, CPU-only)
+    process counts as caught."""
+    ctx = mp.get_context("fork")
+    q = ctx.Queue()
+    p = ctx.Process(target=_child, args=(lib_path, q))
+    p.start()
+    p.join(600)
+    if p.exitcode != 0:
+        return 1_000
+    return q.get(timeout=10)
+
+
+def test_unmutated_copy_passes_battery(tmp_path):
+    src = open(obuild.SRC).read()
+    c = tmp_path / "m.c"
+    c.write_text(src)
+    so = tmp_path / "m.so"
+    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c)], check=True)
+    assert _failing_pins(str(so)) == 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation site of {name} not unique"
+    c = tmp_path / f"{name}.c"
+    c.write_text(src.replace(old, new))
+    so = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c)], check=True)
+    assert _failing_pins(str(so)) > 0, f"no pin caught mutant {name}"
