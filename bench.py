@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE expert-parallel dispatch/combine layout transform on
+one MI355X.
+
+A step is one pass of the whole path over W logical ranks with synthetic,
+seeded inputs already resident in HBM: W dispatch packs, then for every
+destination the expert batch and the combine reduce, then W combine
+unpacks. `value` is tokens/s over all W*T tokens of a step; effective GB/s
+uses the algorithmic byte model (what the method must read and write, from
+the run's actual counts):
+
+  pack (source s)      8*T*K + T_routed*P + U*P + U*slots*8 + 4*W
+  batch (dest r)       4*W + S*slots*4 + S*P + R*P + 4*e_local
+  reduce (dest r)      R*Hb + S*slots*8 + S*Hb
+  unpack (source s)    U*Hb + T*Hb
+
+with P = payload bytes per token row, Hb = combine row bytes, U = slots a
+source sends, S = slots a destination receives, R = expert rows it batches.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
+PEAK_HBM_GBPS = 8000.0
+KERNEL_OF_CALL = {
+    "pack": "pack_copy_kernel",
+    "batch": "batch_copy_kernel",
+    "reduce": "combine_reduce_kernel",
+    "unpack": "combine_unpack_kernel",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources: a counter summary taken from an older
+    build of the kernels no longer describes them."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_topk_ids_dest_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>.<workload>.pmc.txt, or None when it is absent or was
+    taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def byte_model(w, row_bytes, slots, send_cnt, ent, routed):
+    """Algorithmic bytes per call kind (lists over ranks)."""
+    import numpy as np
+    P = int(sum(row_bytes))
+    Hb = w.H * 2
+    U = send_cnt.sum(axis=1)            # per source
+    S = send_cnt.sum(axis=0)            # per destination
+    R = ent.sum(axis=1)                 # per destination
+    pack = [8 * w.T * w.K + int(routed[s]) * P + int(U[s]) * P + int(U[s]) * slots * 8
+            + 4 * w.W for s in range(w.W)]
+    batch = [4 * w.W + int(S[r]) * slots * 4 + int(S[r]) * P + int(R[r]) * P
+             + 4 * w.e_local for r in range(w.W)]
+    reduce = [int(R[r]) * Hb + int(S[r]) * slots * 8 + int(S[r]) * Hb for r in range(w.W)]
+    unpack = [int(U[s]) * Hb + w.T * Hb for s in range(w.W)]
+    return {"pack": pack, "batch": batch, "reduce": reduce, "unpack": unpack,
+            "U": U, "S": S, "R": R}
+
+
+def cpu_baseline(w, srcs, pls, shares: int):
+    """The CPU oracle, as it stands, timed on this host: `shares` logical-rank
+    shares (pack of a source, batch and reduce of a destination, unpack of a
+    source), single-threaded."""
+    import numpy as np
+    import oracle
+    K = w.K
+    t_setup = time.perf_counter()
+    packs = [oracle.dispatch_pack(srcs[s][0], srcs[s][1], w.E, w.W, w.cap, pls[s])
+             for s in range(w.W)]
+    log(f"[cpu_baseline] oracle packs of {w.W} sources for the sample: "
+        f"{time.perf_counter() - t_setup:.1f} s")
+    times = []
+    nbytes = 0
+    for i in range(shares):
+        s = r = i % w.W
+        t0 = time.perf_counter()
+        p = oracle.dispatch_pack(srcs[s][0], srcs[s][1], w.E, w.W, w.cap, pls[s])
+        t1 = time.perf_counter()
+        cnt = np.ascontiguousarray(np.stack([q["send_cnt"][r] for q in packs]))
+        eloc = np.ascontiguousarray(np.stack([q["send_eloc"][r] for q in packs]))
+        wts = np.ascontiguousarray(np.stack([q["send_w"][r] for q in packs]))
+        recv = [oracle.stack_ranks([q["send"][j][r] for q in packs])
+                for j in range(len(pls[0]))]
+        t2 = time.perf_counter()
+        b = oracle.expert_batch(cnt, eloc, w.W, w.e_local, K, w.cap, recv)
+        t3 = time.perf_counter()
+        Y = b["b"][0].view(np.uint16).reshape(w.e_local, -1, w.H)    # identity experts
+        ret = oracle.combine_reduce(Y, cnt, eloc, wts, b["recv_row"], w.W,
+                                    w.e_local, K, w.cap)["ret"]
+        t4 = time.perf_counter()
+        rows = int(p["send_cnt"].max(initial=0))
+        a1 = pls[s][0].view(np.uint16).reshape(w.T, w.H)
+        back = np.empty((w.W, rows, w.H), np.uint16)
+        for d in range(w.W):
+            back[d] = a1[:rows] if rows <= w.T else 0
+        t5 = time.perf_counter()
+        oracle.combine_unpack(back, p["token_slot"])
+        t6 = time.perf_counter()
+        times.append((t1 - t0) + (t3 - t2) + (t4 - t3) + (t6 - t5))
+        P = sum(x.shape[1] for x in pls[s])
+        U = int(p["send_cnt"].sum())
+        S = int(cnt.sum())
+        R = int(b["expert_num_tokens"].sum())
+        routed = int((srcs[s][0] >= 0).any(axis=1).sum())
+        slots = p["slots"]
+        nbytes += (8 * w.T * K + routed * P + U * P + U * slots * 8 + S * slots * 4 + S * P
+                   + R * P + R * w.H * 2 + S * slots * 8 + S * w.H * 2 + U * w.H * 2
+                   + w.T * w.H * 2)
+        del b, ret, back
+    total = sum(times)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": shares * w.T / total,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{shares} logical-rank share(s) of {w.name}: pack of a source, batch and "
+                   f"reduce of a destination (identity experts), unpack of a source; "
+                   f"{total:.2f} s on 1 of {os.cpu_count()} host threads ({model})"),
+        "gbps": nbytes / total / 1e9,
+    }
+
+
+def probe_copy(steps: int):
+    """A plain device copy of known size, for scaling HBM counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"probe": "copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "ms": dt * 1e3,
+                      "gbps": 2 * n / dt / 1e9}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2,
+                    help="1 tiny, 2 dsv3_prefill, 3 mixtral_zipf, 4 decode, 5 multi_payload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-shares", type=int, default=2,
+                    help="logical-rank shares the CPU oracle is timed on")
+    ap.add_argument("--probe", choices=["copy"], default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the W expert-parallel ranks are logical "
+              "partitions on a single device, so --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from combine_topk_ids_dest_amd import binding
+    from combine_topk_ids_dest_amd.emulate import LogicalEP
+
+    binding.load()                      # the HIP library or nothing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.probe == "copy":
+        probe_copy(max(args.steps, 1))
+        return
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    srcs = [wl.routing(w, s) for s in range(w.W)]
+    pls = [wl.payloads(w, s, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
+    row_bytes = [p.shape[1] for p in pls[0]]
+    ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev)
+    for s in range(w.W):
+        ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
+    wl.expert_outputs_device(ep.Y, seed=1000 + w.wid)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: inputs generated and resident in "
+        f"{time.perf_counter() - t_gen:.1f} s")
+
+    for _ in range(args.warmup):
+        ep.step()
+    torch.cuda.synchronize()
+
+    kinds = ["pack"] * w.W + ["batch", "reduce"] * w.W + ["unpack"] * w.W
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in kinds] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        i = 0
+        for s in range(w.W):
+            ev[k][i][0].record(stream); ep.pack(s); ev[k][i][1].record(stream); i += 1
+        for r in range(w.W):
+            ev[k][i][0].record(stream); ep.batch(r); ev[k][i][1].record(stream); i += 1
+            ev[k][i][0].record(stream); ep.reduce(r); ev[k][i][1].record(stream); i += 1
+        for s in range(w.W):
+            ev[k][i][0].record(stream); ep.unpack(s); ev[k][i][1].record(stream); i += 1
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert int(ep.err.item()) == 0, "device reported data errors"
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kind = {k: [] for k in KERNEL_OF_CALL}
+    for k in range(args.steps):
+        for i, kind in enumerate(kinds):
+            per_kind[kind].append(ev[k][i][0].elapsed_time(ev[k][i][1]))
+
+    send_cnt = ep.send_cnt.cpu().numpy().astype(np.int64)
+    ent = ep.expert_num_tokens.cpu().numpy().astype(np.int64)
+    routed = [int((srcs[s][0] >= 0).any(axis=1).sum()) for s in range(w.W)]
+    bm = byte_model(w, row_bytes, ep.slots, send_cnt, ent, routed)
+    step_bytes = sum(sum(bm[k]) for k in KERNEL_OF_CALL)
+    gbps = step_bytes / (ms_per_step / 1e3) / 1e9
+    tokens = w.W * w.T
+    value = tokens / (ms_per_step / 1e3)
+
+    avg_us = {k: float(np.mean(v)) * 1e3 for k, v in per_kind.items()}
+    total_ms = {k: float(np.sum(v)) for k, v in per_kind.items()}
+    dom = max(total_ms, key=total_ms.get)
+    bytes_per_launch = float(np.mean(bm[dom]))
+    achieved = bytes_per_launch / (avg_us[dom] * 1e-6) / 1e9
+    traffic = read_traffic(KERNEL_OF_CALL[dom], w.name)
+    roofline = {
+        "bound": "hbm",
+        "kernel": KERNEL_OF_CALL[dom],
+        "call": f"moe_ep_{ {'pack': 'dispatch_pack', 'batch': 'expert_batch', 'reduce': 'combine_reduce', 'unpack': 'combine_unpack'}[dom] }",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_HBM_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBPS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": int(bytes_per_launch),
+        "avg_launch_us": round(avg_us[dom], 2),
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "T": w.T, "H": w.H, "E": w.E, "K": w.K,
+            "W": w.W, "cap": w.cap, "routing": w.routing
+            + (f" s={w.zipf_s}" if w.routing == "zipf" else ""),
+            "padding_rows": w.n_pad, "payload_bytes_per_row": int(sum(row_bytes)),
+            "combine_accumulation": "fp32",
+            "parallelism": f"1 GPU, {w.W} logical expert-parallel ranks",
+        },
+        "effective_gbps": round(gbps, 1),
+        "frac_of_peak_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "per_call_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
+        "per_call_gbps": {k: round(float(np.sum(bm[k])) / (total_ms[k] / args.steps / 1e3) / 1e9, 1)
+                          for k in KERNEL_OF_CALL},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    log(f"[bench] {w.name}: {ms_per_step:.3f} ms/step, {value / 1e6:.2f} M tokens/s, "
+        f"{gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f} % of peak); per call us "
+        f"{result['per_call_avg_us']}")
+
+    if not args.no_cpu_baseline:
+        del ep
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(w, srcs, pls, args.cpu_shares)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

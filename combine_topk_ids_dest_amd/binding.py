@@ -1,0 +1,260 @@
+"""Python binding of libmoe_ep.so: the same names as the C ABI
+(include/moe_ep.h), argument marshalling only.
+
+Tensors are torch device tensors; this module reads their data pointers,
+element strides and the current HIP stream, checks that the layouts are the
+ones the C ABI describes, and calls the library. Every step of the path runs
+in the library's HIP kernels. If the library is missing this module raises;
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
+
+OK, EINVAL, ECAP, EDTYPE, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
+BF16, F32 = 0, 1
+ERR_ID_RANGE, ERR_PICKS, ERR_ELOC, ERR_ROWCAP, ERR_CNT = 1, 2, 4, 8, 16
+MAX_PAYLOADS = 8
+
+EXPORTED = (
+    "moe_ep_capacities",
+    "moe_ep_workspace_bytes",
+    "moe_ep_status_string",
+    "moe_ep_dispatch_pack",
+    "moe_ep_expert_batch",
+    "moe_ep_combine_reduce",
+    "moe_ep_combine_unpack",
+)
+
+
+class MoeEpPayload(ctypes.Structure):
+    _fields_ = [
+        ("src", ctypes.c_void_p),
+        ("src_stride", ctypes.c_int64),
+        ("dst", ctypes.c_void_p),
+        ("dst_stride", ctypes.c_int64),
+        ("row_bytes", ctypes.c_int64),
+    ]
+
+
+class MoeEpError(RuntimeError):
+    def __init__(self, name: str, status: int, text: str):
+        super().__init__(f"{name}: {text} (status {status})")
+        self.status = status
+
+
+_lib = None
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads libmoe_ep.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -m combine_topk_ids_dest_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.moe_ep_capacities.argtypes = [_I32, _I32, _I32, _I64, _P, _P, _P]
+    lib.moe_ep_workspace_bytes.argtypes = [_I64, _I32, _I32, _I32, _I64, _P]
+    lib.moe_ep_status_string.argtypes = [ctypes.c_int]
+    lib.moe_ep_status_string.restype = ctypes.c_char_p
+    lib.moe_ep_dispatch_pack.argtypes = [
+        _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
+        _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_expert_batch.argtypes = [
+        _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
+        _P, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_combine_reduce.argtypes = [
+        _P, _I64, _I32, _I64, _P, _I64, _P, _P, _I64, _P,
+        _I32, _I32, _I32, _I64, _P, _I64, _P]
+    lib.moe_ep_combine_unpack.argtypes = [
+        _P, _I64, _I32, _I64, _P, _I64, _I32, _I64, _P, _P]
+    for name in EXPORTED:
+        if name != "moe_ep_status_string":
+            getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_ep_status_string(int(status)).decode()
+
+
+def _check(name: str, status: int):
+    if status != OK:
+        raise MoeEpError(name, status, status_string(status))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dense_from(t: torch.Tensor, first: int, name: str):
+    """Checks that dims >= first of t are dense (row-major, no gaps)."""
+    exp = 1
+    for ax in range(t.dim() - 1, first - 1, -1):
+        if t.size(ax) > 1 and t.stride(ax) != exp:
+            raise ValueError(f"{name}: dims from {first} on must be dense")
+        exp *= t.size(ax)
+
+
+def _row_bytes(t: torch.Tensor, first: int) -> int:
+    n = 1
+    for s in t.shape[first:]:
+        n *= s
+    return n * t.element_size()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"combine data must be bfloat16 or float32, not {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# Host-side queries
+# ---------------------------------------------------------------------------
+
+def moe_ep_capacities(K: int, E: int, W: int, max_num_tokens: int) -> Tuple[int, int, int]:
+    cap, slots, ecap = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64()
+    _check("moe_ep_capacities", load().moe_ep_capacities(
+        K, E, W, max_num_tokens, ctypes.byref(cap), ctypes.byref(slots),
+        ctypes.byref(ecap)))
+    return cap.value, slots.value, ecap.value
+
+
+def moe_ep_workspace_bytes(T: int, K: int, E: int, W: int, max_num_tokens: int) -> int:
+    b = ctypes.c_size_t()
+    _check("moe_ep_workspace_bytes", load().moe_ep_workspace_bytes(
+        T, K, E, W, max_num_tokens, ctypes.byref(b)))
+    return b.value
+
+
+# ---------------------------------------------------------------------------
+# The four calls of the path
+# ---------------------------------------------------------------------------
+
+def _payload_array(pairs, src_row_dim: int, dst_row_dim: int):
+    """Descriptors for (src, dst) pairs whose dim 0 is the strided leading
+    dim and whose dims from 1 on are dense; a row spans the dims from
+    src_row_dim (dst_row_dim) on."""
+    if len(pairs) > MAX_PAYLOADS:
+        raise ValueError("too many payloads")
+    arr = (MoeEpPayload * MAX_PAYLOADS)()
+    for i, (src, dst) in enumerate(pairs):
+        _dense_from(src, 1, "payload src")
+        _dense_from(dst, 1, "payload dst")
+        rb = _row_bytes(src, src_row_dim)
+        if _row_bytes(dst, dst_row_dim) != rb:
+            raise ValueError("payload src and dst rows differ in size")
+        arr[i].src = src.data_ptr()
+        arr[i].src_stride = src.stride(0) * src.element_size()
+        arr[i].dst = dst.data_ptr()
+        arr[i].dst_stride = dst.stride(0) * dst.element_size()
+        arr[i].row_bytes = rb
+    return arr
+
+
+def moe_ep_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                         E: int, W: int, max_num_tokens: int,
+                         payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                         send_cnt: torch.Tensor, send_eloc: torch.Tensor,
+                         send_w: torch.Tensor, token_slot: torch.Tensor,
+                         err_flags: Optional[torch.Tensor],
+                         workspace: torch.Tensor, stream=None) -> None:
+    """payloads: (src [T, ...], dst [W, cap, ...]) pairs; the rank stride of
+    dst is free, everything below it dense."""
+    T, K = topk_ids.shape
+    for t, n in ((topk_ids, "topk_ids"), (topk_weights, "topk_weights"),
+                 (send_eloc, "send_eloc"), (send_w, "send_w"),
+                 (token_slot, "token_slot"), (send_cnt, "send_cnt")):
+        _dense_from(t, 0, n)
+    arr = _payload_array(payloads, 1, 2)
+    _check("moe_ep_dispatch_pack", load().moe_ep_dispatch_pack(
+        _ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
+        ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
+        _ptr(send_w), _ptr(token_slot), _ptr(err_flags), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_ep_expert_batch(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
+                        W: int, e_local: int, K: int, max_num_tokens: int,
+                        payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                        expert_num_tokens: torch.Tensor, recv_row: torch.Tensor,
+                        err_flags: Optional[torch.Tensor],
+                        workspace: torch.Tensor, stream=None) -> None:
+    """recv_cnt: [W] view (any stride); recv_eloc: [W, cap, slots] view (rank
+    stride free); payloads: (src [W, cap, ...], dst [e_local, W*cap, ...])."""
+    _dense_from(recv_eloc, 1, "recv_eloc")
+    _dense_from(recv_row, 0, "recv_row")
+    _dense_from(expert_num_tokens, 0, "expert_num_tokens")
+    arr = _payload_array(payloads, 2, 2)
+    _check("moe_ep_expert_batch", load().moe_ep_expert_batch(
+        _ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
+        W, e_local, K, max_num_tokens, ctypes.addressof(arr), len(payloads),
+        _ptr(expert_num_tokens), _ptr(recv_row), _ptr(err_flags), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_ep_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,
+                          recv_eloc: torch.Tensor, recv_w: torch.Tensor,
+                          recv_row: torch.Tensor, W: int, e_local: int, K: int,
+                          max_num_tokens: int, ret: torch.Tensor,
+                          stream=None) -> None:
+    """expert_out: [e_local, W*cap, H] (expert stride free, rows dense);
+    recv_eloc / recv_w: [W, cap, slots] views with one rank stride;
+    ret: [W, cap, H] view (rank stride free)."""
+    dt = _dtype_code(expert_out)
+    if ret.dtype != expert_out.dtype:
+        raise ValueError("ret and expert_out differ in dtype")
+    _dense_from(expert_out, 1, "expert_out")
+    _dense_from(ret, 1, "ret")
+    _dense_from(recv_eloc, 1, "recv_eloc")
+    _dense_from(recv_w, 1, "recv_w")
+    _dense_from(recv_row, 0, "recv_row")
+    if recv_eloc.stride(0) != recv_w.stride(0):
+        raise ValueError("recv_eloc and recv_w must share a rank stride")
+    H = expert_out.size(2)
+    _check("moe_ep_combine_reduce", load().moe_ep_combine_reduce(
+        _ptr(expert_out), expert_out.stride(0), dt, H, _ptr(recv_cnt),
+        recv_cnt.stride(0), _ptr(recv_eloc), _ptr(recv_w), recv_eloc.stride(0),
+        _ptr(recv_row), W, e_local, K, max_num_tokens, _ptr(ret), ret.stride(0),
+        _stream(stream)))
+
+
+def moe_ep_combine_unpack(back: torch.Tensor, token_slot: torch.Tensor,
+                          max_num_tokens: int, out: torch.Tensor,
+                          stream=None) -> None:
+    """back: [W, cap, H] view (rank stride free); token_slot: [T, W];
+    out: [T, H] dense."""
+    dt = _dtype_code(back)
+    if out.dtype != back.dtype:
+        raise ValueError("out and back differ in dtype")
+    _dense_from(back, 1, "back")
+    _dense_from(token_slot, 0, "token_slot")
+    _dense_from(out, 0, "out")
+    T, W = token_slot.shape
+    H = back.size(2)
+    _check("moe_ep_combine_unpack", load().moe_ep_combine_unpack(
+        _ptr(back), back.stride(0), dt, H, _ptr(token_slot), T, W,
+        max_num_tokens, _ptr(out), _stream(stream)))

@@ -1,0 +1,279 @@
+// C ABI of the dispatch/combine layout transform: argument checks,
+// capacity and workspace queries, and the launch sequence of each call.
+// Every check runs before anything is enqueued; no HIP runtime call is made
+// unless all checks pass.
+#include <limits.h>
+
+#include "common.h"
+
+using namespace moe_ep;
+
+namespace {
+
+constexpr int64_t kI32Max = INT_MAX;
+
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Shapes common to every call; fills e_local, cap, slots, expert_cap.
+struct Shape {
+    int32_t W = 0, e_local = 0, slots = 0;
+    int64_t cap = 0, expert_cap = 0;
+};
+
+int check_shape(int32_t K, int32_t e_local, int32_t W, int64_t max_num_tokens,
+                Shape* sh) {
+    if (K <= 0 || W <= 0 || W > MOE_EP_MAX_WORLD || e_local <= 0 ||
+        e_local > MOE_EP_MAX_LOCAL_EXPERTS || max_num_tokens < 0)
+        return MOE_EP_EINVAL;
+    sh->W = W;
+    sh->e_local = e_local;
+    sh->slots = K < e_local ? K : e_local;
+    if (sh->slots > MOE_EP_MAX_SLOTS) return MOE_EP_EINVAL;
+    sh->cap = max_num_tokens;
+    sh->expert_cap = max_num_tokens * W;
+    if ((int64_t)W * sh->cap * sh->slots > kI32Max) return MOE_EP_EINVAL;
+    return MOE_EP_OK;
+}
+
+// Workspace regions, each padded to 128 bytes.
+struct PackWs { int64_t ntiles, cnt_off, off_off, bytes; };
+struct BatchWs { int64_t ntiles, cnt_off, off_off, bytes; };
+
+PackWs pack_ws(int64_t T, int32_t W) {
+    PackWs w;
+    w.ntiles = (T + kRouteTile - 1) / kRouteTile;
+    const int64_t region = round_up(w.ntiles * W * 4, 128);
+    w.cnt_off = 0;
+    w.off_off = region;
+    w.bytes = 2 * region;
+    return w;
+}
+
+BatchWs batch_ws(const Shape& sh) {
+    BatchWs w;
+    w.ntiles = ((int64_t)sh.W * sh.cap * sh.slots + kBatchTile - 1) / kBatchTile;
+    const int64_t region = round_up(w.ntiles * sh.e_local * 4, 128);
+    w.cnt_off = 0;
+    w.off_off = region;
+    w.bytes = 2 * region;
+    return w;
+}
+
+// Checks the payload descriptors and fills the kernel argument. min_src and
+// min_dst are the least leading-dim strides in units of row_bytes.
+int check_payloads(const moe_ep_payload* payloads, int32_t n_payloads,
+                   int64_t min_src_rows, int64_t min_dst_rows, bool need_ptrs,
+                   PayloadSet* P) {
+    if (n_payloads < 0 || n_payloads > MOE_EP_MAX_PAYLOADS) return MOE_EP_EINVAL;
+    if (n_payloads > 0 && payloads == nullptr) return MOE_EP_EINVAL;
+    P->n = n_payloads;
+    for (int p = 0; p < MOE_EP_MAX_PAYLOADS; ++p) {
+        P->src[p] = nullptr;
+        P->dst[p] = nullptr;
+        P->src_stride[p] = P->dst_stride[p] = P->row_bytes[p] = 0;
+    }
+    for (int p = 0; p < n_payloads; ++p) {
+        const moe_ep_payload& d = payloads[p];
+        if (d.row_bytes <= 0) return MOE_EP_EINVAL;
+        if (need_ptrs && (d.src == nullptr || d.dst == nullptr)) return MOE_EP_EINVAL;
+        if (d.row_bytes % 16 || d.src_stride % 16 || d.dst_stride % 16 ||
+            !aligned16(d.src) || !aligned16(d.dst))
+            return MOE_EP_EALIGN;
+        if (d.src_stride < min_src_rows * d.row_bytes ||
+            d.dst_stride < min_dst_rows * d.row_bytes)
+            return MOE_EP_EINVAL;
+        P->src[p] = static_cast<const uint8_t*>(d.src);
+        P->dst[p] = static_cast<uint8_t*>(d.dst);
+        P->src_stride[p] = d.src_stride;
+        P->dst_stride[p] = d.dst_stride;
+        P->row_bytes[p] = d.row_bytes;
+    }
+    return MOE_EP_OK;
+}
+
+int elem_bytes(int32_t dtype) {
+    if (dtype == MOE_EP_BF16) return 2;
+    if (dtype == MOE_EP_F32) return 4;
+    return 0;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_EP_OK : MOE_EP_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_ep_capacities(int32_t K, int32_t E, int32_t W, int64_t max_num_tokens,
+                      int64_t* cap, int32_t* slots, int64_t* expert_cap) {
+    if (!cap || !slots || !expert_cap) return MOE_EP_EINVAL;
+    if (K <= 0 || E <= 0 || W <= 0 || E % W != 0 || max_num_tokens < 0)
+        return MOE_EP_EINVAL;
+    const int32_t e_local = E / W;
+    *cap = max_num_tokens;
+    *slots = K < e_local ? K : e_local;
+    *expert_cap = max_num_tokens * W;
+    return MOE_EP_OK;
+}
+
+int moe_ep_workspace_bytes(int64_t T, int32_t K, int32_t E, int32_t W,
+                           int64_t max_num_tokens, size_t* bytes) {
+    if (!bytes || E <= 0 || W <= 0 || E % W != 0 || T < 0) return MOE_EP_EINVAL;
+    if (T > max_num_tokens) return MOE_EP_ECAP;
+    Shape sh;
+    const int rc = check_shape(K, E / W, W, max_num_tokens, &sh);
+    if (rc) return rc;
+    const int64_t a = pack_ws(max_num_tokens, W).bytes;
+    const int64_t b = batch_ws(sh).bytes;
+    *bytes = (size_t)(a > b ? a : b);
+    return MOE_EP_OK;
+}
+
+const char* moe_ep_status_string(int status) {
+    switch (status) {
+        case MOE_EP_OK: return "ok";
+        case MOE_EP_EINVAL: return "invalid argument";
+        case MOE_EP_ECAP: return "more tokens than max_num_tokens";
+        case MOE_EP_EDTYPE: return "unsupported combine data type";
+        case MOE_EP_EALIGN: return "pointer, stride or row not 16-byte aligned";
+        case MOE_EP_EWORKSPACE: return "workspace missing or too small";
+        case MOE_EP_EHIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
+                         int64_t T, int32_t K, int32_t E, int32_t W,
+                         int64_t max_num_tokens,
+                         const moe_ep_payload* payloads, int32_t n_payloads,
+                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
+                         int32_t* token_slot, uint32_t* err_flags,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (E <= 0 || W <= 0 || E % W != 0 || T < 0) return MOE_EP_EINVAL;
+    Shape sh;
+    int rc = check_shape(K, E / W, W, max_num_tokens, &sh);
+    if (rc) return rc;
+    if (T > max_num_tokens) return MOE_EP_ECAP;
+    if (T * K > kI32Max || T * W > kI32Max) return MOE_EP_EINVAL;
+    if (!send_cnt || !send_eloc || !send_w) return MOE_EP_EINVAL;
+    if (T > 0 && (!topk_ids || !topk_weights || !token_slot)) return MOE_EP_EINVAL;
+    PayloadSet P;
+    rc = check_payloads(payloads, n_payloads, 1, sh.cap, T > 0, &P);
+    if (rc) return rc;
+    const PackWs ws = pack_ws(T, W);
+    if (ws.bytes > 0 && (!workspace || workspace_bytes < (size_t)ws.bytes))
+        return MOE_EP_EWORKSPACE;
+    if (workspace && !aligned16(workspace)) return MOE_EP_EALIGN;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    int32_t* tile_cnt = reinterpret_cast<int32_t*>(wsb + ws.cnt_off);
+    int32_t* tile_off = reinterpret_cast<int32_t*>(wsb + ws.off_off);
+
+    rc = hip_status(launch_route_local(topk_ids, T, K, E, sh.e_local, W,
+                                       token_slot, tile_cnt, err_flags, st));
+    if (rc) return rc;
+    rc = hip_status(launch_column_scan(tile_cnt, (int)ws.ntiles, W, tile_off,
+                                       send_cnt, INT_MAX, st));
+    if (rc) return rc;
+    return hip_status(launch_pack_copy(topk_ids, topk_weights, T, K, E,
+                                       sh.e_local, W, sh.slots, sh.cap,
+                                       token_slot, tile_off, P, send_eloc,
+                                       send_w, err_flags, st));
+}
+
+int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                        const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                        int32_t W, int32_t e_local, int32_t K,
+                        int64_t max_num_tokens,
+                        const moe_ep_payload* payloads, int32_t n_payloads,
+                        int32_t* expert_num_tokens, int32_t* recv_row,
+                        uint32_t* err_flags, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    Shape sh;
+    int rc = check_shape(K, e_local, W, max_num_tokens, &sh);
+    if (rc) return rc;
+    if (!recv_cnt || !recv_eloc || !expert_num_tokens || !recv_row)
+        return MOE_EP_EINVAL;
+    if (cnt_rank_stride < 1 || eloc_rank_stride < sh.cap * sh.slots)
+        return MOE_EP_EINVAL;
+    PayloadSet P;
+    rc = check_payloads(payloads, n_payloads, sh.cap, sh.expert_cap, true, &P);
+    if (rc) return rc;
+    const BatchWs ws = batch_ws(sh);
+    if (ws.bytes > 0 && (!workspace || workspace_bytes < (size_t)ws.bytes))
+        return MOE_EP_EWORKSPACE;
+    if (workspace && !aligned16(workspace)) return MOE_EP_EALIGN;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    int32_t* tile_cnt = reinterpret_cast<int32_t*>(wsb + ws.cnt_off);
+    int32_t* tile_off = reinterpret_cast<int32_t*>(wsb + ws.off_off);
+    const int32_t clamp = sh.expert_cap < kI32Max ? (int32_t)sh.expert_cap : INT_MAX;
+
+    rc = hip_status(launch_batch_local(recv_cnt, cnt_rank_stride, recv_eloc,
+                                       eloc_rank_stride, W, e_local, sh.slots,
+                                       sh.cap, (int)ws.ntiles, recv_row,
+                                       tile_cnt, err_flags, st));
+    if (rc) return rc;
+    rc = hip_status(launch_column_scan(tile_cnt, (int)ws.ntiles, e_local,
+                                       tile_off, expert_num_tokens, clamp, st));
+    if (rc) return rc;
+    return hip_status(launch_batch_copy(recv_cnt, cnt_rank_stride, recv_eloc,
+                                        eloc_rank_stride, W, e_local, sh.slots,
+                                        sh.cap, tile_off, recv_row, P,
+                                        err_flags, st));
+}
+
+int moe_ep_combine_reduce(const void* expert_out, int64_t expert_stride,
+                          int32_t dtype, int64_t H,
+                          const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                          const int32_t* recv_eloc, const float* recv_w,
+                          int64_t meta_rank_stride, const int32_t* recv_row,
+                          int32_t W, int32_t e_local, int32_t K,
+                          int64_t max_num_tokens, void* ret,
+                          int64_t ret_rank_stride, void* stream) {
+    Shape sh;
+    int rc = check_shape(K, e_local, W, max_num_tokens, &sh);
+    if (rc) return rc;
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return MOE_EP_EDTYPE;
+    if (H <= 0) return MOE_EP_EINVAL;
+    if (!expert_out || !recv_cnt || !recv_eloc || !recv_w || !recv_row || !ret)
+        return MOE_EP_EINVAL;
+    if (cnt_rank_stride < 1 || meta_rank_stride < sh.cap * sh.slots ||
+        expert_stride < sh.expert_cap * H || ret_rank_stride < sh.cap * H)
+        return MOE_EP_EINVAL;
+    if ((H * eb) % 16 || (expert_stride * eb) % 16 || (ret_rank_stride * eb) % 16 ||
+        !aligned16(expert_out) || !aligned16(ret))
+        return MOE_EP_EALIGN;
+    return hip_status(launch_combine_reduce(
+        expert_out, expert_stride, dtype, H, recv_cnt, cnt_rank_stride,
+        recv_eloc, recv_w, meta_rank_stride, recv_row, W, e_local, sh.slots,
+        sh.cap, ret, ret_rank_stride, static_cast<hipStream_t>(stream)));
+}
+
+int moe_ep_combine_unpack(const void* back, int64_t back_rank_stride,
+                          int32_t dtype, int64_t H, const int32_t* token_slot,
+                          int64_t T, int32_t W, int64_t max_num_tokens,
+                          void* out, void* stream) {
+    if (W <= 0 || W > MOE_EP_MAX_WORLD || T < 0 || max_num_tokens < 0 || H <= 0)
+        return MOE_EP_EINVAL;
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return MOE_EP_EDTYPE;
+    if (T > max_num_tokens) return MOE_EP_ECAP;
+    if (T * W > kI32Max) return MOE_EP_EINVAL;
+    if (T > 0 && (!back || !token_slot || !out)) return MOE_EP_EINVAL;
+    if (back_rank_stride < max_num_tokens * H) return MOE_EP_EINVAL;
+    if ((H * eb) % 16 || (back_rank_stride * eb) % 16 || !aligned16(back) ||
+        !aligned16(out))
+        return MOE_EP_EALIGN;
+    return hip_status(launch_combine_unpack(back, back_rank_stride, dtype, H,
+                                            token_slot, T, W, max_num_tokens, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// Receive-side expert batching of one destination rank (prepare() on the
+// vLLM "alltoall_batched" documentation page after the exchange: a pick
+// (s, slot, j) is valid when slot < recv_cnt[s] and its local id is >= 0;
+// valid picks, taken in (s, slot, j) order, take the next row of their local
+// expert; rows are copied into [e_local, W*cap, row]; expert_num_tokens
+// counts them).
+//
+// The valid slots of all sources are numbered densely, v = pre[s] + slot
+// (pre = prefix of the received counts), and the picks q = v*slots + j are
+// cut into tiles of 1024. Rows come from a two-level scan with no atomics:
+//   batch_local: in each wave, a multi-split over the bits of the local id
+//     (log2(e_local) ballots) gives every pick its rank among the wave's
+//     picks of the same expert; a per-tile scan over the 16 wave chunks
+//     gives the in-tile rank, stored provisionally in recv_row, and the
+//     tile's count per expert goes to the workspace.
+//   column_scan: tile offsets per expert and expert_num_tokens.
+//   batch_copy: one slot row per block; final row = provisional + tile
+//     offset; the row is read once and stored to each of its experts' rows.
+#include "common.h"
+
+namespace moe_ep {
+
+__global__ __launch_bounds__(256) void batch_local_kernel(
+    const int32_t* __restrict__ recv_cnt, int64_t cnt_stride,
+    const int32_t* __restrict__ recv_eloc, int64_t eloc_stride, int W,
+    int e_local, int slots, int64_t cap, int nbits,
+    int32_t* __restrict__ recv_row, int32_t* __restrict__ tile_cnt,
+    uint32_t* __restrict__ err) {
+    // [kBatchChunks][e_local]; per-chunk counts and in-tile prefixes are
+    // at most kBatchTile, so 16 bits hold them.
+    extern __shared__ int16_t chunk_cnt[];
+    __shared__ int32_t pre[MOE_EP_MAX_WORLD + 1];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+
+    if (tid < 64) load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre, err);
+    for (int i = tid; i < kBatchChunks * e_local; i += 256) chunk_cnt[i] = 0;
+    __syncthreads();
+
+    const int64_t nq = (int64_t)pre[W] * slots;
+    const int64_t q0 = (int64_t)blockIdx.x * kBatchTile;
+    if (q0 >= nq) {
+        for (int e = tid; e < e_local; e += 256)
+            tile_cnt[(int64_t)blockIdx.x * e_local + e] = 0;
+        return;
+    }
+
+    int64_t at[kBatchRounds];    // recv_row index of this lane's pick
+    int32_t key[kBatchRounds];   // local expert, -1 if none
+    int32_t rnk[kBatchRounds];   // rank among the wave's picks of that key
+    uint32_t bad = 0;
+#pragma unroll
+    for (int c = 0; c < kBatchRounds; ++c) {
+        const int64_t q = q0 + c * 256 + tid;
+        int32_t e = -1;
+        at[c] = -1;
+        if (q < nq) {
+            const int32_t v = (int32_t)(q / slots);
+            const int j = (int)(q - (int64_t)v * slots);
+            const int s = find_source(pre, W, v);
+            const int32_t slot = v - pre[s];
+            e = recv_eloc[s * eloc_stride + (int64_t)slot * slots + j];
+            if (e >= e_local) { bad |= MOE_EP_ERR_ELOC; e = -1; }
+            at[c] = ((int64_t)s * cap + slot) * slots + j;
+        }
+        // Multi-split: lanes whose keys agree on every bit are peers.
+        uint64_t peers = __ballot(e >= 0);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t ones = __ballot(e >= 0 && ((e >> b) & 1));
+            peers &= ((e >> b) & 1) ? ones : ~ones;
+        }
+        key[c] = e;
+        rnk[c] = rank_below(peers);
+        if (e >= 0 && rnk[c] == 0)
+            chunk_cnt[(c * 4 + wave) * e_local + e] = (int16_t)__popcll(peers);
+    }
+    report(err, bad);
+    __syncthreads();
+
+    for (int e = tid; e < e_local; e += 256) {
+        int32_t run = 0;
+        for (int ch = 0; ch < kBatchChunks; ++ch) {
+            const int32_t v = chunk_cnt[ch * e_local + e];
+            chunk_cnt[ch * e_local + e] = (int16_t)run;
+            run += v;
+        }
+        tile_cnt[(int64_t)blockIdx.x * e_local + e] = run;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int c = 0; c < kBatchRounds; ++c) {
+        if (at[c] >= 0)
+            recv_row[at[c]] = key[c] >= 0
+                ? chunk_cnt[(c * 4 + wave) * e_local + key[c]] + rnk[c] : -1;
+    }
+}
+
+constexpr int kBatchThreads = 256;
+constexpr int kBatchUnroll = 4;
+
+__global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
+    const int32_t* __restrict__ recv_cnt, int64_t cnt_stride,
+    const int32_t* __restrict__ recv_eloc, int64_t eloc_stride, int W,
+    int e_local, int slots, int64_t cap, const int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ recv_row, const PayloadSet P,
+    uint32_t* __restrict__ err) {
+    __shared__ int32_t pre[MOE_EP_MAX_WORLD + 1];
+    __shared__ int32_t s_exp[MOE_EP_MAX_SLOTS];
+    __shared__ int32_t s_row[MOE_EP_MAX_SLOTS];
+    __shared__ int s_n;
+    const int tid = threadIdx.x;
+    const int64_t expert_cap = (int64_t)W * cap;
+
+    if (tid < 64) load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre, nullptr);
+    __syncthreads();
+    const int32_t S = pre[W];
+
+    for (int32_t v = blockIdx.x; v < S; v += gridDim.x) {
+        const int s = find_source(pre, W, v);
+        const int32_t slot = v - pre[s];
+        if (tid < 64) {
+            const int j = tid;
+            int32_t row = -1;
+            int32_t e = -1;
+            uint32_t bad = 0;
+            if (j < slots) {
+                const int64_t at = ((int64_t)s * cap + slot) * slots + j;
+                e = recv_eloc[s * eloc_stride + (int64_t)slot * slots + j];
+                if (e >= 0 && e < e_local) {
+                    const int64_t q = (int64_t)v * slots + j;
+                    const int64_t r = (int64_t)recv_row[at] +
+                                      tile_off[(q / kBatchTile) * e_local + e];
+                    if (r < expert_cap) row = (int32_t)r;
+                    else bad |= MOE_EP_ERR_ROWCAP;
+                }
+                recv_row[at] = row;
+            }
+            const uint64_t act = __ballot(row >= 0);
+            if (row >= 0) {
+                const int pos = rank_below(act);
+                s_exp[pos] = e;
+                s_row[pos] = row;
+            }
+            report(err, bad);
+            if (tid == 0) s_n = __popcll(act);
+        }
+        __syncthreads();
+        const int n = s_n;
+
+        for (int p = 0; p < P.n; ++p) {
+            const int64_t rb = P.row_bytes[p];
+            const uint8_t* src = P.src[p] + s * P.src_stride[p] + (int64_t)slot * rb;
+            const int64_t nvec = rb >> 4;
+            for (int64_t i0 = tid; i0 < nvec; i0 += kBatchThreads * kBatchUnroll) {
+                u32x4 x[kBatchUnroll];
+#pragma unroll
+                for (int u = 0; u < kBatchUnroll; ++u) {
+                    const int64_t i = i0 + u * kBatchThreads;
+                    if (i < nvec) x[u] = *reinterpret_cast<const u32x4*>(src + i * 16);
+                }
+                for (int a = 0; a < n; ++a) {
+                    uint8_t* dst = P.dst[p] + s_exp[a] * P.dst_stride[p] +
+                                   (int64_t)s_row[a] * rb;
+#pragma unroll
+                    for (int u = 0; u < kBatchUnroll; ++u) {
+                        const int64_t i = i0 + u * kBatchThreads;
+                        if (i < nvec) *reinterpret_cast<u32x4*>(dst + i * 16) = x[u];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
+                              const int32_t* recv_eloc, int64_t eloc_stride,
+                              int W, int e_local, int slots, int64_t cap,
+                              int ntiles, int32_t* recv_row, int32_t* tile_cnt,
+                              uint32_t* err, hipStream_t stream) {
+    if (ntiles == 0) return hipSuccess;
+    int nbits = 0;
+    while ((1 << nbits) < e_local) ++nbits;
+    const size_t lds = sizeof(int16_t) * kBatchChunks * (size_t)e_local;
+    batch_local_kernel<<<dim3(ntiles), dim3(256), lds, stream>>>(
+        recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
+        nbits, recv_row, tile_cnt, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
+                             const int32_t* recv_eloc, int64_t eloc_stride,
+                             int W, int e_local, int slots, int64_t cap,
+                             const int32_t* tile_off, int32_t* recv_row,
+                             const PayloadSet& P, uint32_t* err,
+                             hipStream_t stream) {
+    const int64_t max_rows = (int64_t)W * cap;
+    if (max_rows == 0) return hipSuccess;
+    const int64_t grid = max_rows < 8192 ? max_rows : 8192;
+    batch_copy_kernel<<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>(
+        recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
+        tile_off, recv_row, P, err);
+    return hipGetLastError();
+}
+
+}  // namespace moe_ep

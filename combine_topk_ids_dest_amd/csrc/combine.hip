@@ -1,0 +1,229 @@
+// Combine (finalize() on the vLLM "alltoall_batched" documentation page).
+//
+// combine_reduce, on the destination rank: for every valid received slot,
+// the fp32 sum over its picks, in ascending pick order, of
+// fp32(expert output row) * router weight, each product rounded to fp32
+// before the add (__fmul_rn / __fadd_rn: no contraction into an FMA); the
+// slot's sum is stored in the data type (bf16: round to nearest even), so
+// the return transfer is token-sized.
+//
+// combine_unpack, on the source rank: each token's partials from the ranks
+// it went to, summed in fp32 in ascending rank order from +0.0f and rounded
+// once; a token that went nowhere (padding) gets +0.0.
+//
+// Both are one row per block with 16-byte vector lanes. Wave 0 gathers the
+// row's sources (expert rows with weights, or returned partial slots) into
+// LDS in summation order; every lane then streams its columns.
+#include "common.h"
+
+namespace moe_ep {
+
+constexpr int kCombineThreads = 256;
+constexpr int kPickGroup = 8;   // expert rows loaded before they are summed
+
+struct Bf16Elems {
+    static constexpr int kPerVec = 8;
+    __device__ static void to_f32(const u32x4& v, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = bf16_lo(v[i]);
+            f[2 * i + 1] = bf16_hi(v[i]);
+        }
+    }
+    __device__ static u32x4 from_f32(const float* f) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = to_bf16_rne(f[2 * i]) | (to_bf16_rne(f[2 * i + 1]) << 16);
+        return v;
+    }
+};
+
+struct F32Elems {
+    static constexpr int kPerVec = 4;
+    __device__ static void to_f32(const u32x4& v, float* f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+    }
+    __device__ static u32x4 from_f32(const float* f) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+        return v;
+    }
+};
+
+template <class Elems, int ELEM_BYTES>
+__global__ __launch_bounds__(kCombineThreads) void combine_reduce_kernel(
+    const uint8_t* __restrict__ Y, int64_t y_expert_stride, int64_t H,
+    const int32_t* __restrict__ recv_cnt, int64_t cnt_stride,
+    const int32_t* __restrict__ recv_eloc, const float* __restrict__ recv_w,
+    int64_t meta_stride, const int32_t* __restrict__ recv_row, int W,
+    int e_local, int slots, int64_t cap, uint8_t* __restrict__ ret,
+    int64_t ret_stride) {
+    constexpr int V = Elems::kPerVec;
+    __shared__ int32_t pre[MOE_EP_MAX_WORLD + 1];
+    __shared__ int64_t s_base[MOE_EP_MAX_SLOTS];   // byte offset of the row
+    __shared__ float s_w[MOE_EP_MAX_SLOTS];
+    __shared__ int s_n;
+    const int tid = threadIdx.x;
+    const int64_t row_bytes = H * ELEM_BYTES;
+    const int64_t nvec = row_bytes >> 4;
+    const int64_t expert_cap = (int64_t)W * cap;
+
+    if (tid < 64) load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre, nullptr);
+    __syncthreads();
+    const int32_t S = pre[W];
+
+    for (int32_t v = blockIdx.x; v < S; v += gridDim.x) {
+        const int s = find_source(pre, W, v);
+        const int32_t slot = v - pre[s];
+        if (tid < 64) {
+            const int j = tid;
+            bool ok = false;
+            int64_t base = 0;
+            float w = 0.0f;
+            if (j < slots) {
+                const int64_t m = s * meta_stride + (int64_t)slot * slots + j;
+                const int32_t row = recv_row[((int64_t)s * cap + slot) * slots + j];
+                const int32_t e = recv_eloc[m];
+                if (row >= 0 && row < expert_cap && e >= 0 && e < e_local) {
+                    ok = true;
+                    base = (e * y_expert_stride + (int64_t)row * H) * ELEM_BYTES;
+                    w = recv_w[m];
+                }
+            }
+            const uint64_t act = __ballot(ok);
+            if (ok) {
+                const int pos = rank_below(act);
+                s_base[pos] = base;
+                s_w[pos] = w;
+            }
+            if (tid == 0) s_n = __popcll(act);
+        }
+        __syncthreads();
+        const int n = s_n;
+        uint8_t* out = ret + (s * ret_stride + (int64_t)slot * H) * ELEM_BYTES;
+
+        for (int64_t i = tid; i < nvec; i += kCombineThreads) {
+            float acc[V];
+#pragma unroll
+            for (int c = 0; c < V; ++c) acc[c] = 0.0f;
+            for (int a0 = 0; a0 < n; a0 += kPickGroup) {
+                u32x4 y[kPickGroup];
+#pragma unroll
+                for (int u = 0; u < kPickGroup; ++u)
+                    if (a0 + u < n)
+                        y[u] = *reinterpret_cast<const u32x4*>(Y + s_base[a0 + u] + i * 16);
+#pragma unroll
+                for (int u = 0; u < kPickGroup; ++u) {
+                    if (a0 + u < n) {
+                        const float w = s_w[a0 + u];
+                        float f[V];
+                        Elems::to_f32(y[u], f);
+#pragma unroll
+                        for (int c = 0; c < V; ++c)
+                            acc[c] = __fadd_rn(acc[c], __fmul_rn(f[c], w));
+                    }
+                }
+            }
+            *reinterpret_cast<u32x4*>(out + i * 16) = Elems::from_f32(acc);
+        }
+        __syncthreads();
+    }
+}
+
+template <class Elems, int ELEM_BYTES>
+__global__ __launch_bounds__(kCombineThreads) void combine_unpack_kernel(
+    const uint8_t* __restrict__ back, int64_t back_stride, int64_t H,
+    const int32_t* __restrict__ token_slot, int64_t T, int W, int64_t cap,
+    uint8_t* __restrict__ out) {
+    constexpr int V = Elems::kPerVec;
+    __shared__ int64_t s_base[MOE_EP_MAX_WORLD];
+    __shared__ int s_n;
+    const int tid = threadIdx.x;
+    const int64_t row_bytes = H * ELEM_BYTES;
+    const int64_t nvec = row_bytes >> 4;
+
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+        if (tid < 64) {
+            const int d = tid;
+            int32_t slot = -1;
+            if (d < W) slot = token_slot[t * W + d];
+            if (slot >= cap) slot = -1;          // not a slot of this layout
+            const uint64_t act = __ballot(slot >= 0);
+            if (slot >= 0)
+                s_base[rank_below(act)] = (d * back_stride + (int64_t)slot * H) * ELEM_BYTES;
+            if (tid == 0) s_n = __popcll(act);
+        }
+        __syncthreads();
+        const int n = s_n;
+        uint8_t* o = out + t * row_bytes;
+
+        for (int64_t i = tid; i < nvec; i += kCombineThreads) {
+            float acc[V];
+#pragma unroll
+            for (int c = 0; c < V; ++c) acc[c] = 0.0f;
+            for (int a0 = 0; a0 < n; a0 += kPickGroup) {
+                u32x4 y[kPickGroup];
+#pragma unroll
+                for (int u = 0; u < kPickGroup; ++u)
+                    if (a0 + u < n)
+                        y[u] = *reinterpret_cast<const u32x4*>(back + s_base[a0 + u] + i * 16);
+#pragma unroll
+                for (int u = 0; u < kPickGroup; ++u) {
+                    if (a0 + u < n) {
+                        float f[V];
+                        Elems::to_f32(y[u], f);
+#pragma unroll
+                        for (int c = 0; c < V; ++c) acc[c] = __fadd_rn(acc[c], f[c]);
+                    }
+                }
+            }
+            *reinterpret_cast<u32x4*>(o + i * 16) = Elems::from_f32(acc);
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_combine_reduce(const void* Y, int64_t y_expert_stride,
+                                 int dtype, int64_t H, const int32_t* recv_cnt,
+                                 int64_t cnt_stride, const int32_t* recv_eloc,
+                                 const float* recv_w, int64_t meta_stride,
+                                 const int32_t* recv_row, int W, int e_local,
+                                 int slots, int64_t cap, void* ret,
+                                 int64_t ret_stride, hipStream_t stream) {
+    const int64_t max_rows = (int64_t)W * cap;
+    if (max_rows == 0) return hipSuccess;
+    const int64_t grid = max_rows < 8192 ? max_rows : 8192;
+    const uint8_t* y = static_cast<const uint8_t*>(Y);
+    uint8_t* r = static_cast<uint8_t*>(ret);
+    if (dtype == MOE_EP_BF16)
+        combine_reduce_kernel<Bf16Elems, 2><<<dim3((unsigned)grid), dim3(kCombineThreads), 0, stream>>>(
+            y, y_expert_stride, H, recv_cnt, cnt_stride, recv_eloc, recv_w,
+            meta_stride, recv_row, W, e_local, slots, cap, r, ret_stride);
+    else
+        combine_reduce_kernel<F32Elems, 4><<<dim3((unsigned)grid), dim3(kCombineThreads), 0, stream>>>(
+            y, y_expert_stride, H, recv_cnt, cnt_stride, recv_eloc, recv_w,
+            meta_stride, recv_row, W, e_local, slots, cap, r, ret_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_unpack(const void* back, int64_t back_stride,
+                                 int dtype, int64_t H,
+                                 const int32_t* token_slot, int64_t T, int W,
+                                 int64_t cap, void* out, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int64_t grid = T < 65536 ? T : 65536;
+    const uint8_t* b = static_cast<const uint8_t*>(back);
+    uint8_t* o = static_cast<uint8_t*>(out);
+    if (dtype == MOE_EP_BF16)
+        combine_unpack_kernel<Bf16Elems, 2><<<dim3((unsigned)grid), dim3(kCombineThreads), 0, stream>>>(
+            b, back_stride, H, token_slot, T, W, cap, o);
+    else
+        combine_unpack_kernel<F32Elems, 4><<<dim3((unsigned)grid), dim3(kCombineThreads), 0, stream>>>(
+            b, back_stride, H, token_slot, T, W, cap, o);
+    return hipGetLastError();
+}
+
+}  // namespace moe_ep

@@ -1,0 +1,144 @@
+// Device helpers and launch declarations shared by the HIP kernels of the
+// MoE expert-parallel dispatch/combine layout transform (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_ep.h"
+
+namespace moe_ep {
+
+// Tokens per block of the routing kernel (4 waves, one token per lane).
+constexpr int kRouteTile = 256;
+// Pick entries per block of the receive-scan kernel (256 lanes x 4 rounds).
+constexpr int kBatchTile = 1024;
+constexpr int kBatchRounds = kBatchTile / 256;
+constexpr int kBatchChunks = kBatchTile / 64;   // wave-sized chunks per tile
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Payload descriptors passed by value as a kernel argument.
+struct PayloadSet {
+    const uint8_t* src[MOE_EP_MAX_PAYLOADS];
+    uint8_t* dst[MOE_EP_MAX_PAYLOADS];
+    int64_t src_stride[MOE_EP_MAX_PAYLOADS];
+    int64_t dst_stride[MOE_EP_MAX_PAYLOADS];
+    int64_t row_bytes[MOE_EP_MAX_PAYLOADS];
+    int n;
+};
+
+// Number of set bits of `mask` in lanes below the calling lane.
+__device__ __forceinline__ int rank_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi(
+        (uint32_t)(mask >> 32),
+        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
+    if (bits && err) atomicOr(err, bits);
+}
+
+// Largest s in [0, W) with pre[s] <= v, for an ascending prefix array
+// pre[0..W] (pre[0] = 0) and v < pre[W].
+__device__ __forceinline__ int find_source(const int32_t* pre, int W, int32_t v) {
+    int lo = 0, hi = W - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= v) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Counts received from each source, clamped to [0, cap], and their
+// exclusive prefix pre[0..W]. Run by wave 0 of a block; W <= 64.
+__device__ __forceinline__ void load_recv_prefix(const int32_t* recv_cnt,
+                                                 int64_t cnt_stride, int W,
+                                                 int64_t cap, int32_t* pre,
+                                                 uint32_t* err) {
+    const int lane = threadIdx.x & 63;
+    int32_t c = 0;
+    uint32_t bad = 0;
+    if (lane < W) {
+        int64_t v = recv_cnt[(int64_t)lane * cnt_stride];
+        if (v < 0 || v > cap) {
+            bad = MOE_EP_ERR_CNT;
+            v = v < 0 ? 0 : cap;
+        }
+        c = (int32_t)v;
+    }
+    report(err, bad);
+    const int32_t inc = wave_inclusive_scan(c);
+    if (lane == 0) pre[0] = 0;
+    if (lane < W) pre[lane + 1] = inc;
+}
+
+// bf16 <-> fp32. bf16 is the upper half of a binary32; rounding to bf16 is
+// to nearest, ties to even, NaNs stay quiet NaNs.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------
+// Launchers (defined next to their kernels). All return hipError_t of the
+// launch; grids are computed from host-known sizes only.
+// ---------------------------------------------------------------------
+hipError_t launch_route_local(const int32_t* ids, int64_t T, int K, int E,
+                              int e_local, int W, int32_t* token_slot,
+                              int32_t* tile_cnt, uint32_t* err,
+                              hipStream_t stream);
+
+hipError_t launch_column_scan(const int32_t* cnt, int ntiles, int nkeys,
+                              int32_t* off, int32_t* total, int32_t clamp_max,
+                              hipStream_t stream);
+
+hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
+                            int K, int E, int e_local, int W, int slots,
+                            int64_t cap, int32_t* token_slot,
+                            const int32_t* tile_off, const PayloadSet& P,
+                            int32_t* send_eloc, float* send_w, uint32_t* err,
+                            hipStream_t stream);
+
+hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
+                              const int32_t* recv_eloc, int64_t eloc_stride,
+                              int W, int e_local, int slots, int64_t cap,
+                              int ntiles, int32_t* recv_row, int32_t* tile_cnt,
+                              uint32_t* err, hipStream_t stream);
+
+hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
+                             const int32_t* recv_eloc, int64_t eloc_stride,
+                             int W, int e_local, int slots, int64_t cap,
+                             const int32_t* tile_off, int32_t* recv_row,
+                             const PayloadSet& P, uint32_t* err,
+                             hipStream_t stream);
+
+hipError_t launch_combine_reduce(const void* Y, int64_t y_expert_stride,
+                                 int dtype, int64_t H, const int32_t* recv_cnt,
+                                 int64_t cnt_stride, const int32_t* recv_eloc,
+                                 const float* recv_w, int64_t meta_stride,
+                                 const int32_t* recv_row, int W, int e_local,
+                                 int slots, int64_t cap, void* ret,
+                                 int64_t ret_stride, hipStream_t stream);
+
+hipError_t launch_combine_unpack(const void* back, int64_t back_stride,
+                                 int dtype, int64_t H,
+                                 const int32_t* token_slot, int64_t T, int W,
+                                 int64_t cap, void* out, hipStream_t stream);
+
+}  // namespace moe_ep

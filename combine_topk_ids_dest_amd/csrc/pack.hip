@@ -1,0 +1,106 @@
+// Payload and metadata pack of the send side (prepare() on the vLLM
+// "alltoall_batched" documentation page: send_x[dest, slot] = row of the
+// token; pick column j of the slot holds the j-th routed expert the token
+// wants on that rank, in router order, as a local id with its fp32 weight;
+// unused columns hold -1 and +0.0).
+//
+// Token-major: a block takes one token, reads each payload row from HBM
+// once into registers (16-byte vectors) and stores it to every destination
+// the token goes to (5.3 on average for 256 experts, top-8, 8 ranks). Wave 0
+// turns the in-tile ranks into final slots, writes the final token_slot
+// context and the pick metadata, and leaves the destination list in LDS.
+#include "common.h"
+
+namespace moe_ep {
+
+constexpr int kPackThreads = 256;
+constexpr int kPackUnroll = 4;
+
+__global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t T,
+    int K, int E, int e_local, int W, int slots, int64_t cap,
+    int32_t* __restrict__ token_slot, const int32_t* __restrict__ tile_off,
+    const PayloadSet P, int32_t* __restrict__ send_eloc,
+    float* __restrict__ send_w, uint32_t* __restrict__ err) {
+    __shared__ int32_t s_dest[MOE_EP_MAX_WORLD];
+    __shared__ int32_t s_slot[MOE_EP_MAX_WORLD];
+    __shared__ int s_n;
+    const int tid = threadIdx.x;
+
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+        if (tid < 64) {
+            const int d = tid;
+            int32_t slot = -1;
+            if (d < W) {
+                slot = token_slot[t * W + d];
+                if (slot >= 0) slot += tile_off[(t / kRouteTile) * W + d];
+            }
+            const uint64_t act = __ballot(slot >= 0);
+            uint32_t bad = 0;
+            if (slot >= 0) {
+                const int pos = rank_below(act);
+                s_dest[pos] = d;
+                s_slot[pos] = slot;
+                token_slot[t * W + d] = slot;
+                const int64_t meta = ((int64_t)d * cap + slot) * slots;
+                int j = 0;
+                for (int k = 0; k < K; ++k) {
+                    const int32_t id = ids[t * K + k];
+                    if (id < 0 || id >= E || id / e_local != d) continue;
+                    if (j >= slots) { bad |= MOE_EP_ERR_PICKS; continue; }
+                    send_eloc[meta + j] = id - d * e_local;
+                    send_w[meta + j] = wts[t * K + k];
+                    ++j;
+                }
+                for (; j < slots; ++j) {
+                    send_eloc[meta + j] = -1;
+                    send_w[meta + j] = 0.0f;
+                }
+            }
+            report(err, bad);
+            if (tid == 0) s_n = __popcll(act);
+        }
+        __syncthreads();
+        const int n = s_n;
+
+        for (int p = 0; p < P.n; ++p) {
+            const uint8_t* src = P.src[p] + t * P.src_stride[p];
+            const int64_t rb = P.row_bytes[p];
+            const int64_t nvec = rb >> 4;
+            for (int64_t i0 = tid; i0 < nvec; i0 += kPackThreads * kPackUnroll) {
+                u32x4 v[kPackUnroll];
+#pragma unroll
+                for (int u = 0; u < kPackUnroll; ++u) {
+                    const int64_t i = i0 + u * kPackThreads;
+                    if (i < nvec) v[u] = *reinterpret_cast<const u32x4*>(src + i * 16);
+                }
+                for (int a = 0; a < n; ++a) {
+                    uint8_t* dst = P.dst[p] + s_dest[a] * P.dst_stride[p] +
+                                   (int64_t)s_slot[a] * rb;
+#pragma unroll
+                    for (int u = 0; u < kPackUnroll; ++u) {
+                        const int64_t i = i0 + u * kPackThreads;
+                        if (i < nvec) *reinterpret_cast<u32x4*>(dst + i * 16) = v[u];
+                    }
+                }
+            }
+        }
+        __syncthreads();   // s_dest / s_slot are rewritten for the next token
+    }
+}
+
+hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
+                            int K, int E, int e_local, int W, int slots,
+                            int64_t cap, int32_t* token_slot,
+                            const int32_t* tile_off, const PayloadSet& P,
+                            int32_t* send_eloc, float* send_w, uint32_t* err,
+                            hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int64_t grid = T < 65536 ? T : 65536;
+    pack_copy_kernel<<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
+        ids, wts, T, K, E, e_local, W, slots, cap, token_slot, tile_off, P,
+        send_eloc, send_w, err);
+    return hipGetLastError();
+}
+
+}  // namespace moe_ep

@@ -1,0 +1,133 @@
+// Routing and slot assignment of the send side (prepare() on the vLLM
+// "alltoall_batched" documentation page: padding filter, destination =
+// floor(id / e_local), one slot per (destination, token) pair, slots in
+// ascending token order), plus the column scan shared by the send and
+// receive sides.
+//
+// Slot of (d, t) = number of tokens t' < t that also go to d. It is built in
+// two levels without atomics, so the result does not depend on scheduling:
+//   route_local: per tile of 256 tokens, a wave64 ballot per destination
+//     gives each token its rank among the tile's tokens for d; the tile's
+//     count per destination goes to the workspace.
+//   column_scan: exclusive prefix of the tile counts per destination (the
+//     tile offsets) and the per-destination totals (send_cnt).
+// pack_copy adds the tile offset to the in-tile rank.
+#include "common.h"
+
+namespace moe_ep {
+
+__global__ __launch_bounds__(kRouteTile) void route_local_kernel(
+    const int32_t* __restrict__ ids, int64_t T, int K, int E, int e_local,
+    int W, int32_t* __restrict__ token_slot, int32_t* __restrict__ tile_cnt,
+    uint32_t* __restrict__ err) {
+    __shared__ int32_t wave_cnt[kRouteTile / 64][MOE_EP_MAX_WORLD];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t t = (int64_t)blockIdx.x * kRouteTile + tid;
+
+    // Destination mask of the token: bit d set when some routed pick of the
+    // token lives on rank d. Negative ids are padding; ids >= E are dropped.
+    uint64_t mask = 0;
+    uint32_t bad = 0;
+    if (t < T) {
+        const int32_t* row = ids + t * K;
+        for (int k = 0; k < K; ++k) {
+            const int32_t id = row[k];
+            if (id < 0) continue;
+            if (id >= E) { bad |= MOE_EP_ERR_ID_RANGE; continue; }
+            mask |= 1ull << (id / e_local);
+        }
+    }
+    report(err, bad);
+
+    for (int d = 0; d < W; ++d) {
+        const uint64_t b = __ballot((mask >> d) & 1ull);
+        if (lane == 0) wave_cnt[wave][d] = __popcll(b);
+    }
+    __syncthreads();
+
+    for (int d = 0; d < W; ++d) {
+        const uint64_t b = __ballot((mask >> d) & 1ull);
+        int32_t before = 0;
+        for (int w = 0; w < wave; ++w) before += wave_cnt[w][d];
+        if (t < T)
+            token_slot[t * W + d] = ((mask >> d) & 1ull) ? before + rank_below(b) : -1;
+    }
+    if (tid < W) {
+        int32_t n = 0;
+        for (int w = 0; w < kRouteTile / 64; ++w) n += wave_cnt[w][tid];
+        tile_cnt[(int64_t)blockIdx.x * W + tid] = n;
+    }
+}
+
+// Exclusive prefix down the columns of cnt [ntiles][nkeys] into off, and the
+// column totals (clamped to clamp_max) into total. One block of 1024 lanes:
+// lane (g, key) first sums a contiguous run of tiles, the runs are then
+// scanned per key, and each lane finally writes its run's prefixes.
+__global__ __launch_bounds__(1024) void column_scan_kernel(
+    const int32_t* __restrict__ cnt, int ntiles, int nkeys,
+    int32_t* __restrict__ off, int32_t* __restrict__ total, int32_t clamp_max) {
+    extern __shared__ int32_t part[];   // [groups][nkeys]
+    int groups = 1024 / nkeys;
+    if (groups > 64) groups = 64;
+    if (groups > ntiles) groups = ntiles > 0 ? ntiles : 1;
+    const int chunk = (ntiles + groups - 1) / groups;
+
+    for (int i = threadIdx.x; i < groups * nkeys; i += blockDim.x) {
+        const int g = i / nkeys, key = i - g * nkeys;
+        const int lo = g * chunk;
+        const int hi = min(ntiles, lo + chunk);
+        int32_t s = 0;
+        for (int r = lo; r < hi; ++r) s += cnt[(int64_t)r * nkeys + key];
+        part[i] = s;
+    }
+    __syncthreads();
+    for (int key = threadIdx.x; key < nkeys; key += blockDim.x) {
+        int32_t run = 0;
+        for (int g = 0; g < groups; ++g) {
+            const int32_t v = part[g * nkeys + key];
+            part[g * nkeys + key] = run;
+            run += v;
+        }
+        total[key] = run < clamp_max ? run : clamp_max;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < groups * nkeys; i += blockDim.x) {
+        const int g = i / nkeys, key = i - g * nkeys;
+        const int lo = g * chunk;
+        const int hi = min(ntiles, lo + chunk);
+        int32_t run = part[i];
+        for (int r = lo; r < hi; ++r) {
+            const int64_t at = (int64_t)r * nkeys + key;
+            const int32_t v = cnt[at];
+            off[at] = run;
+            run += v;
+        }
+    }
+}
+
+hipError_t launch_route_local(const int32_t* ids, int64_t T, int K, int E,
+                              int e_local, int W, int32_t* token_slot,
+                              int32_t* tile_cnt, uint32_t* err,
+                              hipStream_t stream) {
+    const int64_t ntiles = (T + kRouteTile - 1) / kRouteTile;
+    if (ntiles == 0) return hipSuccess;
+    route_local_kernel<<<dim3((unsigned)ntiles), dim3(kRouteTile), 0, stream>>>(
+        ids, T, K, E, e_local, W, token_slot, tile_cnt, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_column_scan(const int32_t* cnt, int ntiles, int nkeys,
+                              int32_t* off, int32_t* total, int32_t clamp_max,
+                              hipStream_t stream) {
+    int groups = 1024 / nkeys;
+    if (groups > 64) groups = 64;
+    if (groups > ntiles) groups = ntiles > 0 ? ntiles : 1;
+    const size_t lds = sizeof(int32_t) * (size_t)groups * nkeys;
+    column_scan_kernel<<<dim3(1), dim3(1024), lds, stream>>>(
+        cnt, ntiles, nkeys, off, total, clamp_max);
+    return hipGetLastError();
+}
+
+}  // namespace moe_ep

@@ -1,0 +1,117 @@
+"""W logical expert-parallel ranks on one GPU.
+
+Every rank's buffers live on the one device. The exchange after the pack
+(recv_r[s] = send_s[r]) and after the reduce (back_s[d] = ret_d[s]) is not a
+kernel: the receive side reads the rank-stride view send[:, r] and the
+unpack reads ret[:, s], through the rank-stride arguments of the C ABI.
+
+Device layout (all dense, rank-major):
+  ids, wts        [W_src, T, K]           int32 / fp32
+  src[p]          [W_src, T, row_p]        payload p (uint8 rows)
+  send[p]         [W_src, W_dst, cap, row_p]
+  send_cnt        [W_src, W_dst]           int32
+  send_eloc/_w    [W_src, W_dst, cap, slots]
+  token_slot      [W_src, T, W_dst]        int32 (unpack context)
+  b[p]            [e_local, W*cap, row_p]  one buffer, reused per destination
+  expert_num_tokens [W_dst, e_local]
+  recv_row        [W_dst, W_src, cap, slots] (reduce context)
+  Y               [e_local, W*cap, H]      expert outputs, reused per destination
+  ret             [W_dst, W_src, cap, H]
+  out             [W_src, T, H]
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import binding as B
+
+
+class LogicalEP:
+    def __init__(self, T: int, H: int, E: int, K: int, W: int, cap: int,
+                 row_bytes: Sequence[int], combine_dtype=torch.bfloat16,
+                 device="cuda", fill: Optional[int] = None):
+        """row_bytes: bytes per row of each payload (payload 0 is the hidden
+        row that the combine returns). fill: byte to pre-fill every buffer
+        with (e.g. 0xFF, NaN in bf16/fp32) so unwritten tails stay visible;
+        None leaves buffers uninitialised."""
+        self.T, self.H, self.E, self.K, self.W, self.cap = T, H, E, K, W, cap
+        self.e_local = E // W
+        self.cap_, self.slots, self.expert_cap = B.moe_ep_capacities(K, E, W, cap)
+        self.dtype = combine_dtype
+        self.device = torch.device(device)
+        self.row_bytes = list(row_bytes)
+        W_, el, sl = W, self.e_local, self.slots
+
+        def alloc(shape, dtype):
+            t = torch.empty(shape, dtype=dtype, device=self.device)
+            if fill is not None:
+                t.view(torch.uint8).fill_(fill)
+            return t
+
+        self.ids = alloc((W_, T, K), torch.int32)
+        self.wts = alloc((W_, T, K), torch.float32)
+        self.src = [alloc((W_, T, rb), torch.uint8) for rb in self.row_bytes]
+        self.send = [alloc((W_, W_, cap, rb), torch.uint8) for rb in self.row_bytes]
+        self.send_cnt = alloc((W_, W_), torch.int32)
+        self.send_eloc = alloc((W_, W_, cap, sl), torch.int32)
+        self.send_w = alloc((W_, W_, cap, sl), torch.float32)
+        self.token_slot = alloc((W_, T, W_), torch.int32)
+        self.b = [alloc((el, self.expert_cap, rb), torch.uint8) for rb in self.row_bytes]
+        self.expert_num_tokens = alloc((W_, el), torch.int32)
+        self.recv_row = alloc((W_, W_, cap, sl), torch.int32)
+        self.Y = alloc((el, self.expert_cap, H), combine_dtype)
+        self.ret = alloc((W_, W_, cap, H), combine_dtype)
+        self.out = alloc((W_, T, H), combine_dtype)
+        self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
+        ws = B.moe_ep_workspace_bytes(cap, K, E, W, cap)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+
+    # -- inputs ---------------------------------------------------------
+    def set_source(self, s: int, ids, wts, payload_rows: Sequence):
+        """Copies one source rank's routing and payload rows (torch or numpy
+        arrays, payload rows as [T, row_bytes] bytes) to the device."""
+        self.ids[s].copy_(torch.as_tensor(ids))
+        self.wts[s].copy_(torch.as_tensor(wts))
+        for p, rows in enumerate(payload_rows):
+            t = torch.as_tensor(rows)
+            self.src[p][s].copy_(t.reshape(self.T, -1).view(torch.uint8))
+
+    # -- the four calls for one logical rank ----------------------------
+    def pack(self, s: int, stream=None):
+        B.moe_ep_dispatch_pack(
+            self.ids[s], self.wts[s], self.E, self.W, self.cap,
+            [(self.src[p][s], self.send[p][s]) for p in range(len(self.src))],
+            self.send_cnt[s], self.send_eloc[s], self.send_w[s],
+            self.token_slot[s], self.err, self.workspace, stream)
+
+    def batch(self, r: int, stream=None):
+        B.moe_ep_expert_batch(
+            self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
+            self.K, self.cap,
+            [(self.send[p][:, r], self.b[p]) for p in range(len(self.src))],
+            self.expert_num_tokens[r], self.recv_row[r], self.err,
+            self.workspace, stream)
+
+    def reduce(self, r: int, stream=None):
+        B.moe_ep_combine_reduce(
+            self.Y, self.send_cnt[:, r], self.send_eloc[:, r], self.send_w[:, r],
+            self.recv_row[r], self.W, self.e_local, self.K, self.cap,
+            self.ret[r], stream)
+
+    def unpack(self, s: int, stream=None):
+        B.moe_ep_combine_unpack(self.ret[:, s], self.token_slot[s], self.cap,
+                                self.out[s], stream)
+
+    def step(self, stream=None):
+        """One pass of the whole path over all W logical ranks: W packs,
+        then batch + reduce per destination (reusing b and Y), then W
+        unpacks."""
+        for s in range(self.W):
+            self.pack(s, stream)
+        for r in range(self.W):
+            self.batch(r, stream)
+            self.reduce(r, stream)
+        for s in range(self.W):
+            self.unpack(s, stream)

@@ -1,0 +1,226 @@
+/*
+ * moe_ep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel
+ * dispatch/combine layout transform.
+ *
+ * The operation is the one stated on the vLLM API documentation page
+ * "vllm.model_executor.layers.fused_moe.prepare_finalize.alltoall_batched"
+ * (class AllToAllBatchedPrepareAndFinalize): a token goes to each
+ * destination rank once however many of its experts live there, carrying
+ * its local expert ids and router weights as metadata (prepare(), send
+ * side); the receive side re-batches rows per local expert
+ * (prepare(), receive side); after the experts run, each destination
+ * weights and reduces a token's experts into one token-sized row
+ * (finalize(), first half) and each source sums its per-rank partials back
+ * into token rows (finalize(), second half). The list of opaque payloads
+ * that travel with a token follows the FlashInfer module
+ * "flashinfer/comm/trtllm_moe_alltoall.py" (moe_a2a_dispatch: several
+ * [T, *] payloads per call, each received as [ep_size, max_tokens, *]).
+ *
+ * Conventions shared by every call
+ *   - Pointers are device pointers unless a comment says host.
+ *   - The caller owns every buffer, including the workspace. The library
+ *     never allocates, frees, synchronises the host or keeps state between
+ *     calls. Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     default stream); outputs are ready when the stream reaches the call;
+ *     inputs must stay alive until then.
+ *   - Arguments are checked before anything is enqueued; a non-zero status
+ *     means nothing was enqueued (except MOE_EP_EHIP, a launch failure).
+ *   - Notation: T tokens of this source rank, K picks per token, E experts,
+ *     W ranks, e_local = E / W local experts per rank,
+ *     cap = max_num_tokens token slots per (source, destination),
+ *     slots = min(K, e_local) pick columns per slot,
+ *     expert_cap = W * cap rows per local expert
+ *     (capacities() on the vLLM page).
+ *   - Only valid prefixes are written: send slots [0, send_cnt[d]), expert
+ *     rows [0, expert_num_tokens[e]), returned slots [0, recv_cnt[s]).
+ *     Tails keep whatever the caller left there. combine_unpack writes
+ *     every token row.
+ *   - Data errors that the host cannot see without a sync are reported by
+ *     OR-ing MOE_EP_ERR_* bits into *err_flags (if non-NULL; the caller
+ *     clears it) and have the defined behaviour given with each bit.
+ *   - Limits: 1 <= W <= 64, e_local <= 1024, slots <= 64,
+ *     n_payloads <= 8, and W * cap * slots, T * K, T * W < 2^31.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_EP_API __attribute__((visibility("default")))
+#else
+#define MOE_EP_API
+#endif
+
+/* Status codes. */
+#define MOE_EP_OK          0
+#define MOE_EP_EINVAL     -1   /* bad pointer, size, stride or limit      */
+#define MOE_EP_ECAP       -2   /* T > max_num_tokens                       */
+#define MOE_EP_EDTYPE     -3   /* combine data type not supported          */
+#define MOE_EP_EALIGN     -4   /* pointer, stride or row not 16-B aligned  */
+#define MOE_EP_EWORKSPACE -5   /* workspace missing or too small           */
+#define MOE_EP_EHIP       -6   /* a kernel launch failed                    */
+
+/* Combine data types (expert outputs, partials and token outputs). */
+#define MOE_EP_BF16 0
+#define MOE_EP_F32  1
+
+/* err_flags bits. */
+#define MOE_EP_ERR_ID_RANGE 1u  /* topk id >= E: the entry is dropped       */
+#define MOE_EP_ERR_PICKS    2u  /* more picks for one (token, dest) than
+                                   slots (duplicate ids): extras dropped   */
+#define MOE_EP_ERR_ELOC     4u  /* received local id >= e_local: dropped    */
+#define MOE_EP_ERR_ROWCAP   8u  /* expert row >= expert_cap: dropped        */
+#define MOE_EP_ERR_CNT     16u  /* received count outside [0, cap]: clamped */
+
+#define MOE_EP_MAX_PAYLOADS      8
+#define MOE_EP_MAX_WORLD        64
+#define MOE_EP_MAX_LOCAL_EXPERTS 1024
+#define MOE_EP_MAX_SLOTS        64
+
+/*
+ * One payload: every byte of a row is moved as is (bf16, fp8, fp32 scales,
+ * int32 ids ...). The leading dimension of src and dst may be strided;
+ * rows inside it are dense (row pitch = row_bytes). src, dst, both strides
+ * and row_bytes must be multiples of 16 bytes.
+ */
+typedef struct moe_ep_payload {
+    const void* src;       /* device */
+    int64_t src_stride;    /* bytes between leading-dim items of src */
+    void* dst;             /* device */
+    int64_t dst_stride;    /* bytes between leading-dim items of dst */
+    int64_t row_bytes;     /* bytes per row, > 0 */
+} moe_ep_payload;
+
+/*
+ * capacities() of the vLLM page: cap = max_num_tokens,
+ * slots = min(K, E / W), expert_cap = max_num_tokens * W. Host only.
+ * EINVAL if K <= 0, E <= 0, W <= 0, E % W != 0 or max_num_tokens < 0.
+ */
+MOE_EP_API int moe_ep_capacities(int32_t K, int32_t E, int32_t W, int64_t max_num_tokens,
+                      int64_t* cap, int32_t* slots, int64_t* expert_cap);
+
+/*
+ * Bytes of workspace that moe_ep_dispatch_pack (any T <= max_num_tokens)
+ * and moe_ep_expert_batch need for these sizes; one buffer of this size
+ * serves both calls when they are ordered on one stream. Each region is
+ * padded to 128 bytes, as the FlashInfer module pads its workspace regions
+ * (moe_a2a_get_workspace_size_per_rank). Host only.
+ */
+MOE_EP_API int moe_ep_workspace_bytes(int64_t T, int32_t K, int32_t E, int32_t W,
+                           int64_t max_num_tokens, size_t* bytes);
+
+/* Static text for a status code. Host only. */
+MOE_EP_API const char* moe_ep_status_string(int status);
+
+/*
+ * Dispatch, send side of one source rank (prepare() on the vLLM page:
+ * padding filter, destination = floor(id / e_local), one slot per
+ * (destination, token) pair in ascending token order, payload scatter,
+ * local ids and weights in router order).
+ *
+ *   topk_ids      int32 [T, K]; a negative id is padding (takes no part).
+ *   topk_weights  fp32  [T, K].
+ *   payloads      host array of n_payloads descriptors: src [T, row]
+ *                 (src_stride = bytes between tokens), dst [W, cap, row]
+ *                 (dst_stride = bytes between destination blocks,
+ *                 >= cap * row_bytes).
+ *   send_cnt      int32 [W] out: slots used per destination.
+ *   send_eloc     int32 [W, cap, slots] out: local expert id of pick j of
+ *                 slot (d, s), -1 for an unused column.
+ *   send_w        fp32  [W, cap, slots] out: its weight, +0.0 unused.
+ *   token_slot    int32 [T, W] out: slot of token t at destination d, -1
+ *                 if none. Context for moe_ep_combine_unpack; keep it.
+ *   err_flags     nullable; bits MOE_EP_ERR_ID_RANGE, MOE_EP_ERR_PICKS.
+ *   workspace     >= moe_ep_workspace_bytes(...), 16-B aligned.
+ */
+MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
+                         int64_t T, int32_t K, int32_t E, int32_t W,
+                         int64_t max_num_tokens,
+                         const moe_ep_payload* payloads, int32_t n_payloads,
+                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
+                         int32_t* token_slot, uint32_t* err_flags,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dispatch, receive side of one destination rank (prepare() on the vLLM
+ * page after the exchange: a pick (s, slot, j) is valid when
+ * slot < recv_cnt[s] and its local id is >= 0; valid picks, taken in
+ * (s, slot, j) order, take the next row of their local expert).
+ *
+ *   recv_cnt      int32, element s at recv_cnt[s * cnt_rank_stride].
+ *   recv_eloc     int32, source s block [cap, slots] at
+ *                 recv_eloc + s * eloc_rank_stride (elements,
+ *                 >= cap * slots).
+ *   payloads      src [W, cap, row] (src_stride = bytes between source
+ *                 blocks, >= cap * row_bytes), dst [e_local, W*cap, row]
+ *                 (dst_stride = bytes between experts,
+ *                 >= expert_cap * row_bytes).
+ *   expert_num_tokens int32 [e_local] out: rows per local expert.
+ *   recv_row      int32 [W, cap, slots] out: expert row of each valid pick,
+ *                 -1 for an unused column. Context for combine_reduce.
+ *   err_flags     nullable; bits MOE_EP_ERR_ELOC, MOE_EP_ERR_ROWCAP,
+ *                 MOE_EP_ERR_CNT.
+ */
+MOE_EP_API int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                        const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                        int32_t W, int32_t e_local, int32_t K,
+                        int64_t max_num_tokens,
+                        const moe_ep_payload* payloads, int32_t n_payloads,
+                        int32_t* expert_num_tokens, int32_t* recv_row,
+                        uint32_t* err_flags, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Combine, on the destination rank (finalize() on the vLLM page: weight
+ * and reduce a token's experts so the return is token-sized). For every
+ * valid received slot (s, slot) and column h:
+ *   acc = +0.0f; for j ascending with recv_row >= 0:
+ *     acc = acc + (fp32(Y[e_j, row_j, h]) * w_j)   (product rounded to
+ *                                                    fp32, no fused FMA)
+ *   ret[s, slot, h] = acc, rounded to bf16 to nearest-even for MOE_EP_BF16.
+ *
+ *   expert_out    [e_local, W*cap, H] of dtype; expert e starts at
+ *                 expert_out + e * expert_stride (elements), rows dense.
+ *   recv_w        fp32, same layout and stride as recv_eloc
+ *                 (meta_rank_stride elements between sources).
+ *   recv_row      the context written by moe_ep_expert_batch.
+ *   ret           [W, cap, H] of dtype; source s block at
+ *                 ret + s * ret_rank_stride (elements, >= cap * H).
+ */
+MOE_EP_API int moe_ep_combine_reduce(const void* expert_out, int64_t expert_stride,
+                          int32_t dtype, int64_t H,
+                          const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                          const int32_t* recv_eloc, const float* recv_w,
+                          int64_t meta_rank_stride, const int32_t* recv_row,
+                          int32_t W, int32_t e_local, int32_t K,
+                          int64_t max_num_tokens, void* ret,
+                          int64_t ret_rank_stride, void* stream);
+
+/*
+ * Combine, on the source rank (finalize() on the vLLM page: sum each
+ * token's per-rank partials). out[t, h] = sum over d ascending with
+ * token_slot[t, d] >= 0 of fp32(back[d, token_slot[t, d], h]), from +0.0f,
+ * rounded once (bf16 to nearest-even). A token with no slot (padding)
+ * gets +0.0. Every row of out is written.
+ *
+ *   back          [W, cap, H] of dtype; destination d block at
+ *                 back + d * back_rank_stride (elements, >= cap * H).
+ *   token_slot    the context written by moe_ep_dispatch_pack.
+ *   out           [T, H] of dtype, dense.
+ */
+MOE_EP_API int moe_ep_combine_unpack(const void* back, int64_t back_rank_stride,
+                          int32_t dtype, int64_t H, const int32_t* token_slot,
+                          int64_t T, int32_t W, int64_t max_num_tokens,
+                          void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

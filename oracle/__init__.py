@@ -145,8 +145,9 @@ def dispatch_pack(topk_ids: np.ndarray, topk_weights: np.ndarray, E: int,
 
     payloads: 2-D arrays [T, row] of any dtype with dense rows (row stride
     may exceed the row). Returns send_cnt [W], send_eloc / send_w
-    [W, cap, slots], token_slot [T, W], send (one uint8 [W, cap, row_bytes]
-    array per payload, tails filled with `fill`) and err.
+    [W, cap, slots], token_slot [T, W], send (one uint8 [W, rows, row_bytes]
+    array per payload with rows = max(send_cnt), the valid prefix of the
+    [W, cap, row] layout; tails filled with `fill`) and err.
     """
     ids = np.ascontiguousarray(topk_ids, dtype=np.int32)
     wts = np.ascontiguousarray(topk_weights, dtype=np.float32)
@@ -156,6 +157,10 @@ def dispatch_pack(topk_ids: np.ndarray, topk_weights: np.ndarray, E: int,
     send_eloc = np.full((W, cap, slots), -7, np.int32)
     send_w = np.full((W, cap, slots), np.nan, np.float32)
     token_slot = np.full((T, W), -7, np.int32)
+    rows = 0
+    if len(payloads):
+        # the counts alone first, to size the send rows to the valid prefix
+        rows = int(dispatch_pack(ids, wts, E, W, max_num_tokens)["send_cnt"].max(initial=0))
     srcs, rbytes, sstr, dsts = [], [], [], []
     for p in payloads:
         if p.ndim != 2 or p.shape[0] != T:
@@ -166,11 +171,11 @@ def dispatch_pack(topk_ids: np.ndarray, topk_weights: np.ndarray, E: int,
         srcs.append(p)
         sstr.append(p.strides[0])
         rbytes.append(rb)
-        dsts.append(np.full((W, cap, rb), fill, np.uint8))
+        dsts.append(np.full((W, rows, rb), fill, np.uint8))
     err = load().oracle_dispatch_pack(
         _ptr(ids), _ptr(wts), T, K, E, W, max_num_tokens, len(srcs),
         _ptr_array(srcs), _i64_array(sstr), _i64_array(rbytes),
-        _ptr_array(dsts), _i64_array([cap * rb for rb in rbytes]),
+        _ptr_array(dsts), _i64_array([rows * rb for rb in rbytes]),
         _i64_array(rbytes),
         _ptr(send_cnt), _ptr(send_eloc), _ptr(send_w), _ptr(token_slot))
     if err == 0xFFFFFFFF:
@@ -187,10 +192,11 @@ def expert_batch(recv_cnt: np.ndarray, recv_eloc: np.ndarray, W: int,
     """Receive side of one destination rank.
 
     recv_cnt: int32 [W] (any stride). recv_eloc: int32 [W, cap, slots]
-    (rank stride free, inner dense). recv_payloads: uint8 [W, cap, row]
-    (rank stride free, inner dense). Returns expert_num_tokens [e_local],
-    recv_row [W, cap, slots], b (uint8 [e_local, W*cap, row] per payload)
-    and err.
+    (rank stride free, inner dense). recv_payloads: uint8 [W, rows, row]
+    (rank stride free, inner dense, rows >= every received count). Returns expert_num_tokens [e_local],
+    recv_row [W, cap, slots], b (uint8 [e_local, rows, row] per payload,
+    rows = the largest expert_num_tokens, i.e. the valid prefix of the
+    [e_local, W*cap, row] layout) and err.
     """
     cap, slots, ecap = capacities(K, e_local * W, W, max_num_tokens)
     if recv_cnt.dtype != np.int32 or recv_eloc.dtype != np.int32:
@@ -202,24 +208,29 @@ def expert_batch(recv_cnt: np.ndarray, recv_eloc: np.ndarray, W: int,
         raise ValueError(f"recv_eloc must be {(W, cap, slots)}")
     ent = np.zeros(e_local, np.int32)
     recv_row = np.full((W, cap, slots), -7, np.int32)
+    nrows = 0
+    if len(recv_payloads):
+        # the counts alone first, to size the batched rows to the valid prefix
+        nrows = int(expert_batch(recv_cnt, recv_eloc, W, e_local, K,
+                                 max_num_tokens)["expert_num_tokens"].max(initial=0))
     srcs, rstr, rowstr, rbytes, dsts = [], [], [], [], []
     for p in recv_payloads:
         _inner_contiguous(p, "recv payload", 3)
-        if p.shape[:2] != (W, cap):
-            raise ValueError("recv payloads must be [W, cap, row]")
+        if p.shape[0] != W or p.shape[1] < int(np.clip(recv_cnt, 0, cap).max(initial=0)):
+            raise ValueError("recv payloads must be [W, rows >= counts, row]")
         rb = p.shape[2] * p.itemsize
         srcs.append(p)
         rstr.append(p.strides[0])
         rowstr.append(rb)
         rbytes.append(rb)
-        dsts.append(np.full((e_local, ecap, rb), fill, np.uint8))
+        dsts.append(np.full((e_local, nrows, rb), fill, np.uint8))
     err = load().oracle_expert_batch(
         _ptr(recv_cnt), recv_cnt.strides[0] // 4,
         _ptr(recv_eloc), recv_eloc.strides[0] // 4,
         W, e_local, K, max_num_tokens, len(srcs),
         _ptr_array(srcs), _i64_array(rstr), _i64_array(rowstr),
         _i64_array(rbytes), _ptr_array(dsts),
-        _i64_array([ecap * rb for rb in rbytes]), _i64_array(rbytes),
+        _i64_array([nrows * rb for rb in rbytes]), _i64_array(rbytes),
         _ptr(ent), _ptr(recv_row))
     if err == 0xFFFFFFFF:
         raise ValueError("oracle_expert_batch rejected its arguments")
@@ -243,26 +254,30 @@ def combine_reduce(Y: np.ndarray, recv_cnt: np.ndarray, recv_eloc: np.ndarray,
 
     Y: [e_local, rows, H] (bf16 bits as uint16, or float32), strides free
     on the two outer axes, last axis dense. recv_eloc / recv_w share one
-    rank stride. Returns ret [W, cap, H] (same dtype as Y; rows of invalid
-    slots hold `fill`) and err.
+    rank stride. Returns ret [W, rows, H] (same dtype as Y; rows = the
+    largest received count, the valid prefix of the [W, cap, H] layout;
+    rows past a source's count hold `fill`) and err.
     """
     dt = _dtype_code(Y)
     cap, slots, _ = capacities(K, e_local * W, W, max_num_tokens)
-    if Y.ndim != 3 or Y.shape[0] != e_local or Y.strides[2] != Y.itemsize:
+    if Y.ndim != 3 or Y.shape[0] != e_local or (Y.size and Y.strides[2] != Y.itemsize):
         raise ValueError("Y must be [e_local, rows, H] with dense rows")
+    if Y.size == 0:                      # nothing can be read from it
+        Y = np.zeros((e_local, 1, Y.shape[2]), Y.dtype)
     if recv_eloc.strides != recv_w.strides:
         raise ValueError("recv_eloc and recv_w must share strides")
     _inner_contiguous(recv_eloc, "recv_eloc", 3)
     H = Y.shape[2]
     if fill is None:
         fill = 0xFFFF if dt == BF16 else np.nan
-    ret = np.full((W, cap, H), fill, Y.dtype)
+    rows = int(np.clip(recv_cnt, 0, cap).max(initial=0))
+    ret = np.full((W, rows, H), fill, Y.dtype)
     rr = np.ascontiguousarray(recv_row, dtype=np.int32)
     err = load().oracle_combine_reduce(
         _ptr(Y), Y.strides[0] // Y.itemsize, Y.strides[1] // Y.itemsize, dt, H,
         _ptr(recv_cnt), recv_cnt.strides[0] // 4,
         _ptr(recv_eloc), _ptr(recv_w), recv_eloc.strides[0] // 4, _ptr(rr),
-        W, e_local, K, max_num_tokens, _ptr(ret), cap * H, H)
+        W, e_local, K, max_num_tokens, _ptr(ret), rows * H, H)
     if err == 0xFFFFFFFF:
         raise ValueError("oracle_combine_reduce rejected its arguments")
     return dict(ret=ret, err=int(err))
@@ -271,12 +286,14 @@ def combine_reduce(Y: np.ndarray, recv_cnt: np.ndarray, recv_eloc: np.ndarray,
 def combine_unpack(back: np.ndarray, token_slot: np.ndarray) -> np.ndarray:
     """Per-token sum of the returned partials of one source rank.
 
-    back: [W, cap, H] (bf16 bits uint16 or float32), rank stride free, rows
-    dense. token_slot: int32 [T, W]. Returns out [T, H], every row written.
+    back: [W, rows, H] (bf16 bits uint16 or float32), rank stride free, rows
+    dense, rows past every slot in token_slot. token_slot: int32 [T, W]. Returns out [T, H], every row written.
     """
     dt = _dtype_code(back)
-    if back.ndim != 3 or back.strides[2] != back.itemsize:
-        raise ValueError("back must be [W, cap, H] with dense rows")
+    if back.ndim != 3 or (back.size and back.strides[2] != back.itemsize):
+        raise ValueError("back must be [W, rows, H] with dense rows")
+    if back.size == 0:                   # no slot can be read from it
+        back = np.zeros((back.shape[0], 1, back.shape[2]), back.dtype)
     ts = np.ascontiguousarray(token_slot, dtype=np.int32)
     T, W = ts.shape
     if back.shape[0] != W:
@@ -292,6 +309,15 @@ def combine_unpack(back: np.ndarray, token_slot: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Whole-path helpers over W logical ranks (the exchange is an index swap).
 # --------------------------------------------------------------------------
+
+def stack_ranks(blocks: Sequence[np.ndarray], fill=0) -> np.ndarray:
+    """[n_i, ...] blocks of W ranks -> [W, max n_i, ...], padded with fill."""
+    rows = max((b.shape[0] for b in blocks), default=0)
+    out = np.full((len(blocks), rows) + blocks[0].shape[1:], fill, blocks[0].dtype)
+    for i, b in enumerate(blocks):
+        out[i, :b.shape[0]] = b
+    return out
+
 
 def run_path(srcs_ids: List[np.ndarray], srcs_wts: List[np.ndarray],
              srcs_payloads: List[List[np.ndarray]], E: int, W: int,
@@ -315,7 +341,7 @@ def run_path(srcs_ids: List[np.ndarray], srcs_wts: List[np.ndarray],
     send_w = np.stack([p["send_w"] for p in packs])
     batches = []
     for r in range(W):
-        recv_pl = [np.stack([packs[s]["send"][p][r] for s in range(W)])
+        recv_pl = [stack_ranks([packs[s]["send"][p][r] for s in range(W)])
                    for p in range(n_pl)]
         batches.append(expert_batch(
             np.ascontiguousarray(send_cnt[:, r]),
@@ -335,7 +361,7 @@ def run_path(srcs_ids: List[np.ndarray], srcs_wts: List[np.ndarray],
             W, e_local, K, max_num_tokens)["ret"])
     outs = []
     for s in range(W):
-        back = np.stack([rets[d][s] for d in range(W)])
+        back = stack_ranks([rets[d][s] for d in range(W)])
         outs.append(combine_unpack(back, packs[s]["token_slot"]))
     res.update(rets=rets, outs=outs)
     return res

@@ -1,0 +1,193 @@
+"""The C-ABI library loads without a GPU, exports every symbol that
+include/moe_ep.h declares, and rejects bad arguments with the documented
+status codes before anything reaches the GPU (no valid compute call is made
+here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from combine_topk_ids_dest_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+
+# An address the checks accept as a 16-byte aligned device pointer; no call
+# below passes every check, so it is never dereferenced.
+FAKE = 0x7F0000000000
+
+
+def _header():
+    return open(HEADER).read()
+
+
+def _declared():
+    return re.findall(r"MOE_EP_API\s+[\w\s\*]*?\b(moe_ep_\w+)\s*\(", _header())
+
+
+def _defines():
+    return {m.group(1): int(m.group(2).rstrip("u"))
+            for m in re.finditer(r"#define\s+(MOE_EP_\w+)\s+(-?\d+u?)", _header())}
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = B.load()
+    declared = _declared()
+    assert sorted(declared) == sorted(B.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared)
+
+
+def test_python_constants_match_header():
+    d = _defines()
+    assert (d["MOE_EP_OK"], d["MOE_EP_EINVAL"], d["MOE_EP_ECAP"],
+            d["MOE_EP_EDTYPE"], d["MOE_EP_EALIGN"], d["MOE_EP_EWORKSPACE"],
+            d["MOE_EP_EHIP"]) == (B.OK, B.EINVAL, B.ECAP, B.EDTYPE, B.EALIGN,
+                                  B.EWORKSPACE, B.EHIP)
+    assert (d["MOE_EP_BF16"], d["MOE_EP_F32"]) == (B.BF16, B.F32)
+    assert (d["MOE_EP_ERR_ID_RANGE"], d["MOE_EP_ERR_PICKS"], d["MOE_EP_ERR_ELOC"],
+            d["MOE_EP_ERR_ROWCAP"], d["MOE_EP_ERR_CNT"]) == \
+        (B.ERR_ID_RANGE, B.ERR_PICKS, B.ERR_ELOC, B.ERR_ROWCAP, B.ERR_CNT)
+    assert d["MOE_EP_MAX_PAYLOADS"] == B.MAX_PAYLOADS
+    assert ctypes.sizeof(B.MoeEpPayload) == 40
+
+
+def test_capacities_and_workspace():
+    assert B.moe_ep_capacities(8, 256, 8, 4096) == (4096, 8, 32768)
+    assert B.moe_ep_capacities(2, 8, 8, 8192) == (8192, 1, 65536)
+    assert B.moe_ep_capacities(8, 256, 32, 128) == (128, 8, 4096)
+    for bad in [(0, 8, 2, 4), (2, 0, 2, 4), (2, 8, 0, 4), (2, 9, 2, 4), (2, 8, 2, -1)]:
+        with pytest.raises(B.MoeEpError) as e:
+            B.moe_ep_capacities(*bad)
+        assert e.value.status == B.EINVAL
+    ws = B.moe_ep_workspace_bytes(4096, 8, 256, 8, 4096)
+    assert ws > 0 and ws % 128 == 0
+    # receive-scan tiles dominate: 8*4096*8/1024 tiles x 32 experts x 4 B x 2
+    assert ws == 256 * 32 * 4 * 2
+    with pytest.raises(B.MoeEpError) as e:
+        B.moe_ep_workspace_bytes(5000, 8, 256, 8, 4096)
+    assert e.value.status == B.ECAP
+    with pytest.raises(B.MoeEpError) as e:
+        B.moe_ep_workspace_bytes(10, 8, 256, 128, 4096)    # W > 64
+    assert e.value.status == B.EINVAL
+
+
+def test_status_strings():
+    for code in (B.OK, B.EINVAL, B.ECAP, B.EDTYPE, B.EALIGN, B.EWORKSPACE, B.EHIP):
+        s = B.status_string(code)
+        assert s and s != "unknown status"
+    assert B.status_string(12345) == "unknown status"
+
+
+def _payloads(*descs):
+    arr = (B.MoeEpPayload * 8)()
+    for i, (src, ss, dst, ds, rb) in enumerate(descs):
+        arr[i].src, arr[i].src_stride = src, ss
+        arr[i].dst, arr[i].dst_stride = dst, ds
+        arr[i].row_bytes = rb
+    return arr
+
+
+def _pack(T=16, K=2, E=8, W=4, cap=16, pl=None, npl=1, ws_bytes=1 << 20,
+          ws=FAKE, ids=FAKE):
+    lib = B.load()
+    if pl is None:
+        pl = _payloads((FAKE, 512, FAKE, cap * 512, 512))
+    return lib.moe_ep_dispatch_pack(ids, FAKE, T, K, E, W, cap,
+                                    ctypes.addressof(pl), npl, FAKE, FAKE,
+                                    FAKE, FAKE, None, ws, ws_bytes, None)
+
+
+def test_dispatch_pack_argument_checks():
+    assert _pack(W=0) == B.EINVAL
+    assert _pack(W=65, E=65 * 2) == B.EINVAL
+    assert _pack(E=9) == B.EINVAL                       # E % W != 0
+    assert _pack(K=0) == B.EINVAL
+    assert _pack(T=17) == B.ECAP                        # T > max_num_tokens
+    assert _pack(T=-1) == B.EINVAL
+    assert _pack(npl=9) == B.EINVAL
+    assert _pack(ids=None) == B.EINVAL
+    assert _pack(pl=_payloads((FAKE, 520, FAKE, 16 * 520, 520))) == B.EALIGN
+    assert _pack(pl=_payloads((FAKE + 8, 512, FAKE, 16 * 512, 512))) == B.EALIGN
+    assert _pack(pl=_payloads((FAKE, 256, FAKE, 16 * 512, 512))) == B.EINVAL
+    assert _pack(pl=_payloads((FAKE, 512, FAKE, 15 * 512, 512))) == B.EINVAL
+    assert _pack(pl=_payloads((FAKE, 512, FAKE, 16 * 512, 0))) == B.EINVAL
+    assert _pack(ws_bytes=8) == B.EWORKSPACE
+    assert _pack(ws=None) == B.EWORKSPACE
+    assert _pack(ws=FAKE + 4) == B.EALIGN
+    assert _pack(K=65, E=65 * 4) == B.EINVAL           # slots > 64
+    # size limit W * cap * slots < 2^31
+    assert _pack(T=0, cap=1 << 28, K=8, E=64, W=8) == B.EINVAL
+
+
+def test_expert_batch_argument_checks():
+    lib = B.load()
+
+    def call(W=4, el=2, K=2, cap=16, eloc_stride=None, ws=FAKE, ws_bytes=1 << 20,
+             pl=None, npl=1, cnt=FAKE):
+        slots = min(K, el)
+        if eloc_stride is None:
+            eloc_stride = cap * slots
+        if pl is None:
+            pl = _payloads((FAKE, cap * 512, FAKE, W * cap * 512, 512))
+        return lib.moe_ep_expert_batch(cnt, 1, FAKE, eloc_stride, W, el, K, cap,
+                                       ctypes.addressof(pl), npl, FAKE, FAKE,
+                                       None, ws, ws_bytes, None)
+
+    assert call(el=0) == B.EINVAL
+    assert call(el=1025) == B.EINVAL
+    assert call(W=0) == B.EINVAL
+    assert call(cnt=None) == B.EINVAL
+    assert call(eloc_stride=16 * 2 - 1) == B.EINVAL
+    assert call(pl=_payloads((FAKE, 15 * 512, FAKE, 64 * 512, 512))) == B.EINVAL
+    assert call(pl=_payloads((FAKE, 16 * 512, FAKE, 63 * 512, 512))) == B.EINVAL
+    assert call(pl=_payloads((FAKE, 16 * 520, FAKE, 64 * 520, 520))) == B.EALIGN
+    assert call(ws=None) == B.EWORKSPACE
+    assert call(ws_bytes=4) == B.EWORKSPACE
+
+
+def test_combine_argument_checks():
+    lib = B.load()
+
+    def reduce(dtype=B.BF16, H=256, W=4, el=2, K=2, cap=16, estride=None,
+               rstride=None, y=FAKE):
+        if estride is None:
+            estride = W * cap * H
+        if rstride is None:
+            rstride = cap * H
+        return lib.moe_ep_combine_reduce(y, estride, dtype, H, FAKE, 1, FAKE,
+                                         FAKE, cap * min(K, el), FAKE, W, el,
+                                         K, cap, FAKE, rstride, None)
+
+    assert reduce(dtype=7) == B.EDTYPE
+    assert reduce(H=0) == B.EINVAL
+    assert reduce(H=260) == B.EALIGN                   # 520 B rows
+    assert reduce(dtype=B.F32, H=258) == B.EALIGN
+    assert reduce(estride=4 * 16 * 256 - 1) == B.EINVAL
+    assert reduce(rstride=16 * 256 - 8) == B.EINVAL
+    assert reduce(y=None) == B.EINVAL
+    assert reduce(y=FAKE + 2) == B.EALIGN
+
+    def unpack(dtype=B.BF16, H=256, T=8, W=4, cap=16, bstride=None, out=FAKE):
+        if bstride is None:
+            bstride = cap * H
+        return lib.moe_ep_combine_unpack(FAKE, bstride, dtype, H, FAKE, T, W,
+                                         cap, out, None)
+
+    assert unpack(dtype=3) == B.EDTYPE
+    assert unpack(T=17) == B.ECAP
+    assert unpack(W=65) == B.EINVAL
+    assert unpack(bstride=16 * 256 - 8) == B.EINVAL
+    assert unpack(out=None) == B.EINVAL
+    assert unpack(H=12) == B.EALIGN
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        B.load(str(tmp_path / "absent.so"))

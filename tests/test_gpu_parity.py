@@ -1,0 +1,96 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle,
+element by element, on seeded inputs at sizes the oracle finishes in
+seconds. Sizes span several routing tiles (256 tokens), several receive-scan
+tiles (1024 picks), ragged vector tails and the degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from parity import run_full_parity, say
+
+pytestmark = pytest.mark.gpu
+
+W1, W2, W3, W4, W5 = (wl.WORKLOADS[i] for i in range(1, 6))
+
+CASES = {
+    # the tiny workload at its real size
+    "tiny": W1,
+    # DeepSeek-V3 shape, fewer tokens; ragged vs the 256-token tile, rows of
+    # 129 vectors (ragged vs 256 lanes), cap > T
+    "dsv3_small": W2.scaled(T=300, cap=320, H=1032),
+    # Mixtral shape: e_local = 1, Zipf 1.1, 3 % padding, several scan tiles
+    "mixtral_small": W3.scaled(T=700, cap=700, H=512),
+    # decode at its real size: W = 32, T = 128, H = 7168
+    "decode": W4,
+    # five payloads (bf16, fp8, scales, ids, weights), Zipf 1.2, 10 % padding
+    "multi_small": W5.scaled(T=300, cap=300, H=1024),
+    # one rank: pack is a compaction, batch a counting sort
+    "w1": W1.scaled(W=1, E=8, K=2, T=200, cap=200, H=64),
+    # the largest world, 2 experts per rank, slots = e_local < K
+    "w64": W1.scaled(W=64, E=128, K=4, T=90, cap=96, H=128),
+    # many local experts (e_local = 512): 9-bit multi-split
+    "e_local_512": W1.scaled(W=2, E=1024, K=8, T=260, cap=260, H=64),
+    # top-1
+    "k1": W1.scaled(W=4, E=16, K=1, T=129, cap=129, H=32),
+    # every row padding
+    "all_padding": W1.scaled(T=40, cap=40, pad_frac=1.0),
+    # no tokens at all
+    "empty": W1.scaled(T=0, cap=16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_parity(name):
+    w = CASES[name]
+    say(f"[parity] {name}: T={w.T} H={w.H} E={w.E} K={w.K} W={w.W} cap={w.cap}")
+    run_full_parity(w, salt=3)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv3_small", "mixtral_small"])
+def test_parity_fp32_combine(name):
+    w = CASES[name]
+    say(f"[parity fp32] {name}")
+    run_full_parity(w, salt=5, f32=True)
+
+
+def test_parity_second_seed():
+    say("[parity] dsv3_small seed 2")
+    run_full_parity(CASES["dsv3_small"], salt=11)
+
+
+def test_bad_ids_and_duplicates_follow_defined_behaviour():
+    """ids >= E are dropped (bit 0), duplicate ids past the slots are dropped
+    (bit 1), both exactly as the oracle does."""
+    w = W1.scaled(W=4, E=8, K=3, T=70, cap=70, H=64, pad_frac=0.0)
+    srcs, pls = [], []
+    for s in range(w.W):
+        ids, wts = wl.routing(w, s, 7)
+        ids = ids.copy()
+        ids[3, 1] = 8 + s            # out of range
+        ids[5] = [2, 2, 2]           # duplicates: e_local 2 -> slots 2
+        ids[9, 0] = -5               # any negative id is padding
+        srcs.append((ids, wts))
+        pls.append(wl.payloads(w, s, 7))
+    say("[parity] bad ids")
+    run_full_parity(w, srcs=srcs, pls=pls)
+
+
+def test_received_count_out_of_range_is_clamped():
+    w = W1.scaled(W=4, E=8, K=2, T=50, cap=50, H=64)
+    say("[parity] corrupt count")
+    run_full_parity(w, salt=9, corrupt_cnt=(1, 2, 77))
+
+
+def test_runs_are_bit_identical():
+    """Same inputs twice: every output byte equal (no order dependence)."""
+    w = CASES["mixtral_small"]
+    say("[determinism] mixtral_small x2")
+    ep1, _ = run_full_parity(w, salt=13)
+    outs1 = [ep1.out.clone(), ep1.ret.clone(), ep1.recv_row.clone(),
+             ep1.token_slot.clone()]
+    del ep1
+    ep2, _ = run_full_parity(w, salt=13)
+    outs2 = [ep2.out, ep2.ret, ep2.recv_row, ep2.token_slot]
+    for a, b in zip(outs1, outs2):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))

@@ -161,6 +161,9 @@ def quantize_fp8_e4m3(hidden_bits: np.ndarray, group: int = 128):
     T, H = hidden_bits.shape
     if H % group:
         raise ValueError("H must be a multiple of the quantisation group")
+    if T == 0:
+        return (np.zeros((0, H), np.uint8),
+                np.zeros((0, H // group), np.float32))
     x = torch.from_numpy(bf16_bits_to_f32(hidden_bits)).view(T, H // group, group)
     amax = x.abs().amax(dim=2)
     scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
@@ -177,16 +180,17 @@ def payloads(w: Workload, rank: int, salt: int = 0,
     Payload 0 is always the bf16 hidden a1. The multi-payload workload adds
     the fp8 copy, its scales, the int32 ids and the fp32 weights.
     """
+    def rows(a):
+        a = np.ascontiguousarray(a)
+        return a.view(np.uint8).reshape(w.T, a.itemsize * int(np.prod(a.shape[1:])))
+
     a1 = hidden_bf16(w, rank, salt)
-    out = [a1.view(np.uint8).reshape(w.T, -1)]
+    out = [rows(a1)]
     if w.multi_payload:
         if ids is None or wts is None:
             ids, wts = routing(w, rank, salt)
         q, s = quantize_fp8_e4m3(a1)
-        out.append(np.ascontiguousarray(q))
-        out.append(np.ascontiguousarray(s).view(np.uint8).reshape(w.T, -1))
-        out.append(np.ascontiguousarray(ids).view(np.uint8).reshape(w.T, -1))
-        out.append(np.ascontiguousarray(wts).view(np.uint8).reshape(w.T, -1))
+        out += [rows(q), rows(s), rows(ids), rows(wts)]
     return out
 
 
@@ -217,12 +221,12 @@ def expert_outputs_f32(w: Workload, dest: int, counts: Sequence[int],
     return out
 
 
-def expert_outputs_device(shape, seed: int, device, dtype=None):
-    """Large expert-output buffers drawn on the device with torch's seeded
-    Philox generator (N(0,1)), for full-size runs where a host draw of
+def expert_outputs_device(out, seed: int):
+    """Fills a large device buffer of expert outputs with N(0,1) draws of
+    torch's seeded Philox generator, for full-size runs where a host draw of
     gigabytes would dominate. Every value is a plain seeded draw."""
     import torch
-    dtype = dtype or torch.bfloat16
-    g = torch.Generator(device=device)
+    g = torch.Generator(device=out.device)
     g.manual_seed(int(seed))
-    return torch.randn(shape, generator=g, device=device, dtype=dtype)
+    torch.randn(out.shape, generator=g, device=out.device, dtype=out.dtype, out=out)
+    return out
