@@ -75,8 +75,8 @@ class LogicalEP:
         self.ids[s].copy_(torch.as_tensor(ids))
         self.wts[s].copy_(torch.as_tensor(wts))
         for p, rows in enumerate(payload_rows):
-            t = torch.as_tensor(rows)
-            self.src[p][s].copy_(t.reshape(self.T, -1).view(torch.uint8))
+            t = torch.as_tensor(rows).view(torch.uint8)
+            self.src[p][s].copy_(t.reshape(self.T, self.row_bytes[p]))
 
     # -- the four calls for one logical rank ----------------------------
     def pack(self, s: int, stream=None):

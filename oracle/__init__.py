@@ -310,9 +310,10 @@ def combine_unpack(back: np.ndarray, token_slot: np.ndarray) -> np.ndarray:
 # Whole-path helpers over W logical ranks (the exchange is an index swap).
 # --------------------------------------------------------------------------
 
-def stack_ranks(blocks: Sequence[np.ndarray], fill=0) -> np.ndarray:
-    """[n_i, ...] blocks of W ranks -> [W, max n_i, ...], padded with fill."""
-    rows = max((b.shape[0] for b in blocks), default=0)
+def stack_ranks(blocks: Sequence[np.ndarray], fill=0, min_rows: int = 0) -> np.ndarray:
+    """[n_i, ...] blocks of W ranks -> [W, max(n_i, min_rows), ...], padded
+    with fill."""
+    rows = max([b.shape[0] for b in blocks] + [min_rows])
     out = np.full((len(blocks), rows) + blocks[0].shape[1:], fill, blocks[0].dtype)
     for i, b in enumerate(blocks):
         out[i, :b.shape[0]] = b

@@ -100,7 +100,8 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
     n_pl = len(pls[0])
     batches, rets = [], []
     for r in range(w.W):
-        recv_pl = [oracle.stack_ranks([packs[s]["send"][p][r] for s in range(w.W)])
+        recv_pl = [oracle.stack_ranks([packs[s]["send"][p][r] for s in range(w.W)],
+                                      min_rows=w.cap if corrupt_cnt else 0)
                    for p in range(n_pl)]
         b = oracle.expert_batch(np.ascontiguousarray(send_cnt[:, r]),
                                 np.ascontiguousarray(send_eloc[:, r]), w.W,
