@@ -192,7 +192,7 @@ def main():
     ap.add_argument("--workload", type=int, default=2,
                     help="1 tiny, 2 dsv3_prefill, 3 mixtral_zipf, 4 decode, 5 multi_payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-shares", type=int, default=2,
+    ap.add_argument("--cpu-shares", type=int, default=8,
                     help="logical-rank shares the CPU oracle is timed on")
     ap.add_argument("--probe", choices=["copy"], default=None)
     args = ap.parse_args()

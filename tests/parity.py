@@ -195,3 +195,149 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
         assert_combine_close(gout[s], outs[s], f"out src {s}")
     assert int(ep.err.item()) == exp_err, f"err flags {ep.err.item()} vs {exp_err}"
     return ep, dict(packs=packs, batches=batches, rets=rets, outs=outs)
+
+
+# ---------------------------------------------------------------------------
+# Full workload sizes (the launch configuration bench.py times)
+# ---------------------------------------------------------------------------
+
+def column_windows(nbytes: int, width: int = 64):
+    """Byte windows of a row: the start, the 4 KiB boundary of one pass of
+    256 lanes x 16 B, the middle and the end (16-byte aligned)."""
+    starts = {0, 4096 - width // 2, (nbytes // 2) // 16 * 16, nbytes - width}
+    out = []
+    for s in sorted(starts):
+        s = max(0, min(s, nbytes - width)) // 16 * 16
+        out.extend(range(s, min(nbytes, s + width)))
+    return np.array(sorted(set(out)), dtype=np.int64)
+
+
+def run_fullsize(w: wl.Workload, seed: int = 0):
+    """Whole path at full size. Every integer output and every valid payload
+    byte is compared; the combine is compared on column windows that the
+    oracle computes exactly (the reduction is independent per column)."""
+    dev = torch.device("cuda")
+    say(f"[fullsize] {w.name}: generating inputs")
+    srcs = [wl.routing(w, s, seed) for s in range(w.W)]
+    pls = [wl.payloads(w, s, seed, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
+    row_bytes = [p.shape[1] for p in pls[0]]
+    n_pl = len(row_bytes)
+    ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
+                   fill=SENTINEL)
+    for s in range(w.W):
+        ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
+    wl.expert_outputs_device(ep.Y, seed=2000 + w.wid)
+    # the expert outputs are an input of the combine; the oracle gets a host
+    # copy of the column windows it checks
+    hcols = column_windows(w.H * 2) // 2
+    hcols = np.unique(hcols)
+    say(f"[fullsize] {w.name}: oracle metadata")
+    packs = [oracle.dispatch_pack(srcs[s][0], srcs[s][1], w.E, w.W, w.cap)
+             for s in range(w.W)]
+    send_cnt = np.stack([p["send_cnt"] for p in packs])
+    send_eloc = np.stack([p["send_eloc"] for p in packs])
+    send_w = np.stack([p["send_w"] for p in packs])
+    batches = [oracle.expert_batch(np.ascontiguousarray(send_cnt[:, r]),
+                                   np.ascontiguousarray(send_eloc[:, r]), w.W,
+                                   w.e_local, w.K, w.cap) for r in range(w.W)]
+    maxn = max(int(b["expert_num_tokens"].max(initial=0)) for b in batches)
+    Ysub = ep.Y[:, :max(maxn, 1)][:, :, torch.from_numpy(hcols).to(dev)].contiguous()
+    Ysub = Ysub.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    say(f"[fullsize] {w.name}: pack on the GPU")
+    for s in range(w.W):
+        ep.pack(s)
+    torch.cuda.synchronize()
+    assert np.array_equal(ep.send_cnt.cpu().numpy(), send_cnt), "send_cnt"
+    assert np.array_equal(ep.token_slot.cpu().numpy(),
+                          np.stack([p["token_slot"] for p in packs])), "token_slot"
+    g_eloc = ep.send_eloc.cpu().numpy()
+    g_w = ep.send_w.cpu().numpy()
+    for s in range(w.W):
+        for d in range(w.W):
+            c = int(send_cnt[s, d])
+            assert np.array_equal(g_eloc[s, d, :c], send_eloc[s, d, :c]), f"eloc {s}->{d}"
+            assert np.array_equal(g_w[s, d, :c].view(np.uint32),
+                                  send_w[s, d, :c].view(np.uint32)), f"w {s}->{d}"
+    # every valid payload byte: send[s, d, slot] is the source row of the
+    # token the oracle put in that slot
+    tok_of = {}
+    for s in range(w.W):
+        ts = packs[s]["token_slot"]
+        for d in range(w.W):
+            toks = np.nonzero(ts[:, d] >= 0)[0]
+            order = np.argsort(ts[toks, d], kind="stable")
+            tok_of[(s, d)] = toks[order]
+            idx = torch.from_numpy(tok_of[(s, d)]).to(dev)
+            c = len(idx)
+            for p in range(n_pl):
+                exp = ep.src[p][s].index_select(0, idx)
+                assert torch.equal(ep.send[p][s, d, :c], exp), f"payload {p} {s}->{d}"
+                assert bool((ep.send[p][s, d, c:] == SENTINEL).all()), f"payload {p} tail {s}->{d}"
+
+    say(f"[fullsize] {w.name}: batch + reduce on the GPU")
+    rets_sub = []
+    src_flat = [x.view(w.W * w.T, -1) for x in ep.src]
+    for r in range(w.W):
+        for p in range(n_pl):
+            ep.b[p].fill_(SENTINEL)
+        ep.batch(r)
+        ep.reduce(r)
+        torch.cuda.synchronize()
+        b = batches[r]
+        ent = ep.expert_num_tokens[r].cpu().numpy()
+        assert np.array_equal(ent, b["expert_num_tokens"]), f"expert_num_tokens {r}"
+        rr = ep.recv_row[r].cpu().numpy()
+        e_all, row_all, src_all = [], [], []
+        for s in range(w.W):
+            c = int(send_cnt[s, r])
+            assert np.array_equal(rr[s, :c], b["recv_row"][s, :c]), f"recv_row {s}->{r}"
+            rows = b["recv_row"][s, :c]                       # [c, slots]
+            m = rows >= 0
+            e_all.append(send_eloc[s, r, :c][m])
+            row_all.append(rows[m])
+            src_all.append(np.broadcast_to((s * w.T + tok_of[(s, r)])[:, None], rows.shape)[m])
+        e_all = np.concatenate(e_all) if e_all else np.zeros(0, np.int32)
+        row_all = np.concatenate(row_all) if row_all else np.zeros(0, np.int32)
+        src_all = np.concatenate(src_all) if src_all else np.zeros(0, np.int64)
+        for e in range(w.e_local):
+            n = int(ent[e])
+            sel = e_all == e
+            order = np.argsort(row_all[sel], kind="stable")
+            assert np.array_equal(row_all[sel][order], np.arange(n))
+            idx = torch.from_numpy(src_all[sel][order].astype(np.int64)).to(dev)
+            for p in range(n_pl):
+                assert torch.equal(ep.b[p][e, :n], src_flat[p].index_select(0, idx)), \
+                    f"batched payload {p} e{e} dst {r}"
+                assert bool((ep.b[p][e, n:] == SENTINEL).all()), f"batched tail e{e} dst {r}"
+        # combine reduce on the column windows
+        exp_ret = oracle.combine_reduce(
+            Ysub, np.ascontiguousarray(send_cnt[:, r]),
+            np.ascontiguousarray(send_eloc[:, r]), np.ascontiguousarray(send_w[:, r]),
+            b["recv_row"], w.W, w.e_local, w.K, w.cap)["ret"]
+        rets_sub.append(exp_ret)
+        gret = ep.ret[r][:, :, torch.from_numpy(hcols).to(dev)].cpu()
+        gret = gret.view(torch.int16).numpy().view(np.uint16)
+        for s in range(w.W):
+            c = int(send_cnt[s, r])
+            assert_combine_close(gret[s, :c], exp_ret[s, :c], f"ret {s}->{r}")
+            assert bool((ep.ret[r][s, c:].view(torch.uint8) == SENTINEL).all()), "ret tail"
+
+    say(f"[fullsize] {w.name}: unpack on the GPU")
+    for s in range(w.W):
+        ep.unpack(s)
+    torch.cuda.synchronize()
+    gout = ep.out[:, :, torch.from_numpy(hcols).to(dev)].cpu()
+    gout = gout.view(torch.int16).numpy().view(np.uint16)
+    for s in range(w.W):
+        back = oracle.stack_ranks([rets_sub[d][s] for d in range(w.W)])
+        exp_out = oracle.combine_unpack(back, packs[s]["token_slot"])
+        assert_combine_close(gout[s], exp_out, f"out src {s}")
+        pad = (srcs[s][0] < 0).all(axis=1)
+        if pad.any():
+            pidx = torch.from_numpy(np.nonzero(pad)[0]).to(dev)
+            assert bool((ep.out[s].index_select(0, pidx).view(torch.int16) == 0).all()), \
+                "padding rows must be +0.0"
+    assert int(ep.err.item()) == 0
+    say(f"[fullsize] {w.name}: ok")
+    return ep
