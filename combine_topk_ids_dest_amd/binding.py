@@ -175,13 +175,28 @@ def _payload_array(pairs, src_row_dim: int, dst_row_dim: int):
     return arr
 
 
-def moe_ep_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
-                         E: int, W: int, max_num_tokens: int,
-                         payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
-                         send_cnt: torch.Tensor, send_eloc: torch.Tensor,
-                         send_w: torch.Tensor, token_slot: torch.Tensor,
-                         err_flags: Optional[torch.Tensor],
-                         workspace: torch.Tensor, stream=None) -> None:
+class PreparedCall:
+    """One call of the library with its arguments marshalled once; calling
+    it passes them unchanged with the stream of the moment. It keeps the
+    tensors (and the payload descriptor array) it points into alive."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self.name = name
+        self.fn = getattr(load(), name)
+        self.args = args
+        self.keep = keep
+
+    def __call__(self, stream=None) -> None:
+        _check(self.name, self.fn(*self.args, _stream(stream)))
+
+
+def prepare_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                          E: int, W: int, max_num_tokens: int,
+                          payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                          send_cnt: torch.Tensor, send_eloc: torch.Tensor,
+                          send_w: torch.Tensor, token_slot: torch.Tensor,
+                          err_flags: Optional[torch.Tensor],
+                          workspace: torch.Tensor) -> PreparedCall:
     """payloads: (src [T, ...], dst [W, cap, ...]) pairs; the rank stride of
     dst is free, everything below it dense."""
     T, K = topk_ids.shape
@@ -190,37 +205,56 @@ def moe_ep_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                  (token_slot, "token_slot"), (send_cnt, "send_cnt")):
         _dense_from(t, 0, n)
     arr = _payload_array(payloads, 1, 2)
-    _check("moe_ep_dispatch_pack", load().moe_ep_dispatch_pack(
-        _ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
-        ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
-        _ptr(send_w), _ptr(token_slot), _ptr(err_flags), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
+            ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
+            _ptr(send_w), _ptr(token_slot), _ptr(err_flags), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    return PreparedCall("moe_ep_dispatch_pack", args,
+                        (arr, topk_ids, topk_weights, payloads, send_cnt, send_eloc,
+                         send_w, token_slot, err_flags, workspace))
 
 
-def moe_ep_expert_batch(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
-                        W: int, e_local: int, K: int, max_num_tokens: int,
-                        payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
-                        expert_num_tokens: torch.Tensor, recv_row: torch.Tensor,
-                        err_flags: Optional[torch.Tensor],
-                        workspace: torch.Tensor, stream=None) -> None:
+def moe_ep_dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens, payloads,
+                         send_cnt, send_eloc, send_w, token_slot, err_flags,
+                         workspace, stream=None) -> None:
+    prepare_dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens, payloads,
+                          send_cnt, send_eloc, send_w, token_slot, err_flags,
+                          workspace)(stream)
+
+
+def prepare_expert_batch(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
+                         W: int, e_local: int, K: int, max_num_tokens: int,
+                         payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                         expert_num_tokens: torch.Tensor, recv_row: torch.Tensor,
+                         err_flags: Optional[torch.Tensor],
+                         workspace: torch.Tensor) -> PreparedCall:
     """recv_cnt: [W] view (any stride); recv_eloc: [W, cap, slots] view (rank
     stride free); payloads: (src [W, cap, ...], dst [e_local, W*cap, ...])."""
     _dense_from(recv_eloc, 1, "recv_eloc")
     _dense_from(recv_row, 0, "recv_row")
     _dense_from(expert_num_tokens, 0, "expert_num_tokens")
     arr = _payload_array(payloads, 2, 2)
-    _check("moe_ep_expert_batch", load().moe_ep_expert_batch(
-        _ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
-        W, e_local, K, max_num_tokens, ctypes.addressof(arr), len(payloads),
-        _ptr(expert_num_tokens), _ptr(recv_row), _ptr(err_flags), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
+            W, e_local, K, max_num_tokens, ctypes.addressof(arr), len(payloads),
+            _ptr(expert_num_tokens), _ptr(recv_row), _ptr(err_flags), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    return PreparedCall("moe_ep_expert_batch", args,
+                        (arr, recv_cnt, recv_eloc, payloads, expert_num_tokens,
+                         recv_row, err_flags, workspace))
 
 
-def moe_ep_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,
-                          recv_eloc: torch.Tensor, recv_w: torch.Tensor,
-                          recv_row: torch.Tensor, W: int, e_local: int, K: int,
-                          max_num_tokens: int, ret: torch.Tensor,
-                          stream=None) -> None:
+def moe_ep_expert_batch(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
+                        payloads, expert_num_tokens, recv_row, err_flags,
+                        workspace, stream=None) -> None:
+    prepare_expert_batch(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
+                         payloads, expert_num_tokens, recv_row, err_flags,
+                         workspace)(stream)
+
+
+def prepare_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,
+                           recv_eloc: torch.Tensor, recv_w: torch.Tensor,
+                           recv_row: torch.Tensor, W: int, e_local: int, K: int,
+                           max_num_tokens: int, ret: torch.Tensor) -> PreparedCall:
     """expert_out: [e_local, W*cap, H] (expert stride free, rows dense);
     recv_eloc / recv_w: [W, cap, slots] views with one rank stride;
     ret: [W, cap, H] view (rank stride free)."""
@@ -235,16 +269,21 @@ def moe_ep_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,
     if recv_eloc.stride(0) != recv_w.stride(0):
         raise ValueError("recv_eloc and recv_w must share a rank stride")
     H = expert_out.size(2)
-    _check("moe_ep_combine_reduce", load().moe_ep_combine_reduce(
-        _ptr(expert_out), expert_out.stride(0), dt, H, _ptr(recv_cnt),
-        recv_cnt.stride(0), _ptr(recv_eloc), _ptr(recv_w), recv_eloc.stride(0),
-        _ptr(recv_row), W, e_local, K, max_num_tokens, _ptr(ret), ret.stride(0),
-        _stream(stream)))
+    args = (_ptr(expert_out), expert_out.stride(0), dt, H, _ptr(recv_cnt),
+            recv_cnt.stride(0), _ptr(recv_eloc), _ptr(recv_w), recv_eloc.stride(0),
+            _ptr(recv_row), W, e_local, K, max_num_tokens, _ptr(ret), ret.stride(0))
+    return PreparedCall("moe_ep_combine_reduce", args,
+                        (expert_out, recv_cnt, recv_eloc, recv_w, recv_row, ret))
 
 
-def moe_ep_combine_unpack(back: torch.Tensor, token_slot: torch.Tensor,
-                          max_num_tokens: int, out: torch.Tensor,
-                          stream=None) -> None:
+def moe_ep_combine_reduce(expert_out, recv_cnt, recv_eloc, recv_w, recv_row, W,
+                          e_local, K, max_num_tokens, ret, stream=None) -> None:
+    prepare_combine_reduce(expert_out, recv_cnt, recv_eloc, recv_w, recv_row, W,
+                           e_local, K, max_num_tokens, ret)(stream)
+
+
+def prepare_combine_unpack(back: torch.Tensor, token_slot: torch.Tensor,
+                           max_num_tokens: int, out: torch.Tensor) -> PreparedCall:
     """back: [W, cap, H] view (rank stride free); token_slot: [T, W];
     out: [T, H] dense."""
     dt = _dtype_code(back)
@@ -255,6 +294,10 @@ def moe_ep_combine_unpack(back: torch.Tensor, token_slot: torch.Tensor,
     _dense_from(out, 0, "out")
     T, W = token_slot.shape
     H = back.size(2)
-    _check("moe_ep_combine_unpack", load().moe_ep_combine_unpack(
-        _ptr(back), back.stride(0), dt, H, _ptr(token_slot), T, W,
-        max_num_tokens, _ptr(out), _stream(stream)))
+    args = (_ptr(back), back.stride(0), dt, H, _ptr(token_slot), T, W,
+            max_num_tokens, _ptr(out))
+    return PreparedCall("moe_ep_combine_unpack", args, (back, token_slot, out))
+
+
+def moe_ep_combine_unpack(back, token_slot, max_num_tokens, out, stream=None) -> None:
+    prepare_combine_unpack(back, token_slot, max_num_tokens, out)(stream)

@@ -176,12 +176,18 @@ int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
     rc = hip_status(launch_route_local(topk_ids, T, K, E, sh.e_local, W,
                                        token_slot, tile_cnt, err_flags, st));
     if (rc) return rc;
-    rc = hip_status(launch_column_scan(tile_cnt, (int)ws.ntiles, W, tile_off,
-                                       send_cnt, INT_MAX, st));
-    if (rc) return rc;
+    // Few tiles (or none): pack_copy sums the tile counts itself; the scan
+    // kernel still runs for T = 0 so that send_cnt is written.
+    const bool fused = ws.ntiles > 0 && ws.ntiles <= kPackFuseTiles;
+    if (!fused) {
+        rc = hip_status(launch_column_scan(tile_cnt, (int)ws.ntiles, W, tile_off,
+                                           send_cnt, INT_MAX, st));
+        if (rc) return rc;
+    }
     return hip_status(launch_pack_copy(topk_ids, topk_weights, T, K, E,
                                        sh.e_local, W, sh.slots, sh.cap,
-                                       token_slot, tile_off, P, send_eloc,
+                                       token_slot, fused ? tile_cnt : nullptr,
+                                       tile_off, send_cnt, P, send_eloc,
                                        send_w, err_flags, st));
 }
 

@@ -37,8 +37,10 @@ __global__ __launch_bounds__(256) void batch_local_kernel(
     for (int i = tid; i < kBatchChunks * e_local; i += 256) chunk_cnt[i] = 0;
     __syncthreads();
 
-    const int64_t nq = (int64_t)pre[W] * slots;
-    const int64_t q0 = (int64_t)blockIdx.x * kBatchTile;
+    // Pick indices fit in 32 bits (W * cap * slots < 2^31 is checked on the
+    // host), which keeps the divisions below 32-bit.
+    const int32_t nq = pre[W] * slots;
+    const int32_t q0 = (int32_t)blockIdx.x * kBatchTile;
     if (q0 >= nq) {
         for (int e = tid; e < e_local; e += 256)
             tile_cnt[(int64_t)blockIdx.x * e_local + e] = 0;
@@ -49,20 +51,25 @@ __global__ __launch_bounds__(256) void batch_local_kernel(
     int32_t key[kBatchRounds];   // local expert, -1 if none
     int32_t rnk[kBatchRounds];   // rank among the wave's picks of that key
     uint32_t bad = 0;
+    // All rounds' loads first, so their latencies overlap.
 #pragma unroll
     for (int c = 0; c < kBatchRounds; ++c) {
-        const int64_t q = q0 + c * 256 + tid;
-        int32_t e = -1;
+        const int32_t q = q0 + c * 256 + tid;
+        key[c] = -1;
         at[c] = -1;
         if (q < nq) {
-            const int32_t v = (int32_t)(q / slots);
-            const int j = (int)(q - (int64_t)v * slots);
+            const int32_t v = q / slots;
+            const int j = q - v * slots;
             const int s = find_source(pre, W, v);
             const int32_t slot = v - pre[s];
-            e = recv_eloc[s * eloc_stride + (int64_t)slot * slots + j];
-            if (e >= e_local) { bad |= MOE_EP_ERR_ELOC; e = -1; }
+            key[c] = recv_eloc[s * eloc_stride + (int64_t)slot * slots + j];
             at[c] = ((int64_t)s * cap + slot) * slots + j;
         }
+    }
+#pragma unroll
+    for (int c = 0; c < kBatchRounds; ++c) {
+        int32_t e = key[c];
+        if (e >= e_local) { bad |= MOE_EP_ERR_ELOC; e = -1; }
         // Multi-split: lanes whose keys agree on every bit are peers.
         uint64_t peers = __ballot(e >= 0);
         for (int b = 0; b < nbits; ++b) {
@@ -128,9 +135,9 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
                 const int64_t at = ((int64_t)s * cap + slot) * slots + j;
                 e = recv_eloc[s * eloc_stride + (int64_t)slot * slots + j];
                 if (e >= 0 && e < e_local) {
-                    const int64_t q = (int64_t)v * slots + j;
+                    const int32_t q = v * slots + j;
                     const int64_t r = (int64_t)recv_row[at] +
-                                      tile_off[(q / kBatchTile) * e_local + e];
+                                      tile_off[(int64_t)(q / kBatchTile) * e_local + e];
                     if (r < expert_cap) row = (int32_t)r;
                     else bad |= MOE_EP_ERR_ROWCAP;
                 }
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
 #pragma unroll
                 for (int u = 0; u < kBatchUnroll; ++u) {
                     const int64_t i = i0 + u * kBatchThreads;
-                    if (i < nvec) x[u] = *reinterpret_cast<const u32x4*>(src + i * 16);
+                    if (i < nvec) x[u] = ld_row<MOE_EP_COPY_NT>(src + i * 16);
                 }
                 for (int a = 0; a < n; ++a) {
                     uint8_t* dst = P.dst[p] + s_exp[a] * P.dst_stride[p] +
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
 #pragma unroll
                     for (int u = 0; u < kBatchUnroll; ++u) {
                         const int64_t i = i0 + u * kBatchThreads;
-                        if (i < nvec) *reinterpret_cast<u32x4*>(dst + i * 16) = x[u];
+                        if (i < nvec) st_row<MOE_EP_COPY_NT>(dst + i * 16, x[u]);
                     }
                 }
             }
@@ -197,7 +204,7 @@ hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
                              hipStream_t stream) {
     const int64_t max_rows = (int64_t)W * cap;
     if (max_rows == 0) return hipSuccess;
-    const int64_t grid = max_rows < 8192 ? max_rows : 8192;
+    const int64_t grid = max_rows < MOE_EP_ROW_GRID ? max_rows : MOE_EP_ROW_GRID;
     batch_copy_kernel<<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>(
         recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
         tile_off, recv_row, P, err);

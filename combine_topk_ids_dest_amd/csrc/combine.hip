@@ -19,7 +19,19 @@
 namespace moe_ep {
 
 constexpr int kCombineThreads = 256;
-constexpr int kPickGroup = 8;   // expert rows loaded before they are summed
+// Vectors each lane keeps in flight per pick, and picks loaded per group:
+// a received slot averages 1.5 picks at 256 experts, top-8, 8 ranks, so the
+// loads of several vectors are issued before any is summed.
+#ifndef MOE_EP_COMBINE_VU
+#define MOE_EP_COMBINE_VU 4
+#endif
+#ifndef MOE_EP_REDUCE_PG
+#define MOE_EP_REDUCE_PG 2
+#endif
+#ifndef MOE_EP_UNPACK_PG
+#define MOE_EP_UNPACK_PG 4
+#endif
+constexpr int kVU = MOE_EP_COMBINE_VU;
 
 struct Bf16Elems {
     static constexpr int kPerVec = 8;
@@ -53,6 +65,60 @@ struct F32Elems {
     }
 };
 
+// out[i] = sum over a < n, in order, of (w_a *) fp32(row_a[i]) for every
+// 16-byte vector i of a row, accumulated from +0.0f with each product
+// rounded to fp32 before the add. Row a starts at base + off[a] (bytes).
+template <class Elems, bool WEIGHTED, int PG>
+__device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ base,
+                                         const int64_t* off, const float* w,
+                                         int n, int64_t nvec,
+                                         uint8_t* __restrict__ out) {
+    constexpr int V = Elems::kPerVec;
+    for (int64_t i0 = threadIdx.x; i0 < nvec; i0 += kCombineThreads * kVU) {
+        float acc[kVU][V];
+#pragma unroll
+        for (int v = 0; v < kVU; ++v)
+#pragma unroll
+            for (int c = 0; c < V; ++c) acc[v][c] = 0.0f;
+        for (int a0 = 0; a0 < n; a0 += PG) {
+            u32x4 y[PG][kVU];
+#pragma unroll
+            for (int u = 0; u < PG; ++u) {
+                if (a0 + u < n) {
+                    const uint8_t* row = base + off[a0 + u];
+#pragma unroll
+                    for (int v = 0; v < kVU; ++v) {
+                        const int64_t i = i0 + v * kCombineThreads;
+                        if (i < nvec) y[u][v] = ld_row<MOE_EP_COMBINE_NT>(row + i * 16);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < PG; ++u) {
+                if (a0 + u < n) {
+                    const float wa = WEIGHTED ? w[a0 + u] : 1.0f;
+#pragma unroll
+                    for (int v = 0; v < kVU; ++v) {
+                        if (i0 + v * kCombineThreads < nvec) {
+                            float f[V];
+                            Elems::to_f32(y[u][v], f);
+#pragma unroll
+                            for (int c = 0; c < V; ++c)
+                                acc[v][c] = WEIGHTED ? __fadd_rn(acc[v][c], __fmul_rn(f[c], wa))
+                                                     : __fadd_rn(acc[v][c], f[c]);
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < kVU; ++v) {
+            const int64_t i = i0 + v * kCombineThreads;
+            if (i < nvec) st_row<MOE_EP_COMBINE_NT>(out + i * 16, Elems::from_f32(acc[v]));
+        }
+    }
+}
+
 template <class Elems, int ELEM_BYTES>
 __global__ __launch_bounds__(kCombineThreads) void combine_reduce_kernel(
     const uint8_t* __restrict__ Y, int64_t y_expert_stride, int64_t H,
@@ -61,14 +127,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_reduce_kernel(
     int64_t meta_stride, const int32_t* __restrict__ recv_row, int W,
     int e_local, int slots, int64_t cap, uint8_t* __restrict__ ret,
     int64_t ret_stride) {
-    constexpr int V = Elems::kPerVec;
     __shared__ int32_t pre[MOE_EP_MAX_WORLD + 1];
     __shared__ int64_t s_base[MOE_EP_MAX_SLOTS];   // byte offset of the row
     __shared__ float s_w[MOE_EP_MAX_SLOTS];
     __shared__ int s_n;
     const int tid = threadIdx.x;
-    const int64_t row_bytes = H * ELEM_BYTES;
-    const int64_t nvec = row_bytes >> 4;
+    const int64_t nvec = (H * ELEM_BYTES) >> 4;
     const int64_t expert_cap = (int64_t)W * cap;
 
     if (tid < 64) load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre, nullptr);
@@ -102,33 +166,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_reduce_kernel(
             if (tid == 0) s_n = __popcll(act);
         }
         __syncthreads();
-        const int n = s_n;
-        uint8_t* out = ret + (s * ret_stride + (int64_t)slot * H) * ELEM_BYTES;
-
-        for (int64_t i = tid; i < nvec; i += kCombineThreads) {
-            float acc[V];
-#pragma unroll
-            for (int c = 0; c < V; ++c) acc[c] = 0.0f;
-            for (int a0 = 0; a0 < n; a0 += kPickGroup) {
-                u32x4 y[kPickGroup];
-#pragma unroll
-                for (int u = 0; u < kPickGroup; ++u)
-                    if (a0 + u < n)
-                        y[u] = *reinterpret_cast<const u32x4*>(Y + s_base[a0 + u] + i * 16);
-#pragma unroll
-                for (int u = 0; u < kPickGroup; ++u) {
-                    if (a0 + u < n) {
-                        const float w = s_w[a0 + u];
-                        float f[V];
-                        Elems::to_f32(y[u], f);
-#pragma unroll
-                        for (int c = 0; c < V; ++c)
-                            acc[c] = __fadd_rn(acc[c], __fmul_rn(f[c], w));
-                    }
-                }
-            }
-            *reinterpret_cast<u32x4*>(out + i * 16) = Elems::from_f32(acc);
-        }
+        sum_rows<Elems, true, MOE_EP_REDUCE_PG>(
+            Y, s_base, s_w, s_n, nvec,
+            ret + (s * ret_stride + (int64_t)slot * H) * ELEM_BYTES);
         __syncthreads();
     }
 }
@@ -138,7 +178,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_unpack_kernel(
     const uint8_t* __restrict__ back, int64_t back_stride, int64_t H,
     const int32_t* __restrict__ token_slot, int64_t T, int W, int64_t cap,
     uint8_t* __restrict__ out) {
-    constexpr int V = Elems::kPerVec;
     __shared__ int64_t s_base[MOE_EP_MAX_WORLD];
     __shared__ int s_n;
     const int tid = threadIdx.x;
@@ -157,31 +196,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_unpack_kernel(
             if (tid == 0) s_n = __popcll(act);
         }
         __syncthreads();
-        const int n = s_n;
-        uint8_t* o = out + t * row_bytes;
-
-        for (int64_t i = tid; i < nvec; i += kCombineThreads) {
-            float acc[V];
-#pragma unroll
-            for (int c = 0; c < V; ++c) acc[c] = 0.0f;
-            for (int a0 = 0; a0 < n; a0 += kPickGroup) {
-                u32x4 y[kPickGroup];
-#pragma unroll
-                for (int u = 0; u < kPickGroup; ++u)
-                    if (a0 + u < n)
-                        y[u] = *reinterpret_cast<const u32x4*>(back + s_base[a0 + u] + i * 16);
-#pragma unroll
-                for (int u = 0; u < kPickGroup; ++u) {
-                    if (a0 + u < n) {
-                        float f[V];
-                        Elems::to_f32(y[u], f);
-#pragma unroll
-                        for (int c = 0; c < V; ++c) acc[c] = __fadd_rn(acc[c], f[c]);
-                    }
-                }
-            }
-            *reinterpret_cast<u32x4*>(o + i * 16) = Elems::from_f32(acc);
-        }
+        sum_rows<Elems, false, MOE_EP_UNPACK_PG>(back, s_base, nullptr, s_n, nvec,
+                                                 out + t * row_bytes);
         __syncthreads();
     }
 }
@@ -195,7 +211,7 @@ hipError_t launch_combine_reduce(const void* Y, int64_t y_expert_stride,
                                  int64_t ret_stride, hipStream_t stream) {
     const int64_t max_rows = (int64_t)W * cap;
     if (max_rows == 0) return hipSuccess;
-    const int64_t grid = max_rows < 8192 ? max_rows : 8192;
+    const int64_t grid = max_rows < MOE_EP_ROW_GRID ? max_rows : MOE_EP_ROW_GRID;
     const uint8_t* y = static_cast<const uint8_t*>(Y);
     uint8_t* r = static_cast<uint8_t*>(ret);
     if (dtype == MOE_EP_BF16)

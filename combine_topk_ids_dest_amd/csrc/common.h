@@ -11,12 +11,42 @@ namespace moe_ep {
 
 // Tokens per block of the routing kernel (4 waves, one token per lane).
 constexpr int kRouteTile = 256;
+// Up to this many token tiles, pack_copy derives tile offsets itself.
+constexpr int kPackFuseTiles = 64;
 // Pick entries per block of the receive-scan kernel (256 lanes x 4 rounds).
 constexpr int kBatchTile = 1024;
 constexpr int kBatchRounds = kBatchTile / 256;
 constexpr int kBatchChunks = kBatchTile / 64;   // wave-sized chunks per tile
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Row data is touched once per call. The combine kernels (many scattered
+// reads per written row) load and store it with the nontemporal hint, which
+// measured faster on gfx950; the copy kernels (one read, several writes) use
+// plain loads and stores, which measured faster for them. Knobs for tuning
+// builds; the defaults are the product settings.
+#ifndef MOE_EP_COPY_NT
+#define MOE_EP_COPY_NT 0
+#endif
+#ifndef MOE_EP_COMBINE_NT
+#define MOE_EP_COMBINE_NT 1
+#endif
+// Grid cap of the kernels that walk received slot rows (grid-stride).
+#ifndef MOE_EP_ROW_GRID
+#define MOE_EP_ROW_GRID 32768
+#endif
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_row(const uint8_t* p) {
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st_row(uint8_t* p, const u32x4& v) {
+    if (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+}
 
 // Payload descriptors passed by value as a kernel argument.
 struct PayloadSet {
@@ -108,10 +138,14 @@ hipError_t launch_column_scan(const int32_t* cnt, int ntiles, int nkeys,
                               int32_t* off, int32_t* total, int32_t clamp_max,
                               hipStream_t stream);
 
+// tile_cnt != nullptr selects the fused tile offsets (ntiles <=
+// kPackFuseTiles): offsets are summed from tile_cnt and block 0 writes
+// send_cnt; otherwise tile_off holds the offsets from column_scan.
 hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             int K, int E, int e_local, int W, int slots,
                             int64_t cap, int32_t* token_slot,
-                            const int32_t* tile_off, const PayloadSet& P,
+                            const int32_t* tile_cnt, const int32_t* tile_off,
+                            int32_t* send_cnt, const PayloadSet& P,
                             int32_t* send_eloc, float* send_w, uint32_t* err,
                             hipStream_t stream);
 

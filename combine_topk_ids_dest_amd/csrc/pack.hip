@@ -7,8 +7,10 @@
 // Token-major: a block takes one token, reads each payload row from HBM
 // once into registers (16-byte vectors) and stores it to every destination
 // the token goes to (5.3 on average for 256 experts, top-8, 8 ranks). Wave 0
-// turns the in-tile ranks into final slots, writes the final token_slot
-// context and the pick metadata, and leaves the destination list in LDS.
+// turns the in-tile ranks into final slots (adding the offset of the token's
+// tile, summed here from the tile counts when there are few tiles), writes
+// the final token_slot context and the pick metadata, and leaves the
+// destination list in LDS.
 #include "common.h"
 
 namespace moe_ep {
@@ -16,10 +18,25 @@ namespace moe_ep {
 constexpr int kPackThreads = 256;
 constexpr int kPackUnroll = 4;
 
+// Sum of tile_cnt[j][d] over tiles j < tiles (loads issued 8 at a time).
+__device__ __forceinline__ int32_t sum_tiles(const int32_t* __restrict__ tile_cnt,
+                                             int64_t tiles, int W, int d) {
+    int32_t s = 0;
+    for (int64_t j0 = 0; j0 < tiles; j0 += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = j0 + u < tiles ? tile_cnt[(j0 + u) * W + d] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    return s;
+}
+
 __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t T,
     int K, int E, int e_local, int W, int slots, int64_t cap,
-    int32_t* __restrict__ token_slot, const int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ token_slot, const int32_t* __restrict__ tile_cnt,
+    const int32_t* __restrict__ tile_off, int32_t* __restrict__ send_cnt,
     const PayloadSet P, int32_t* __restrict__ send_eloc,
     float* __restrict__ send_w, uint32_t* __restrict__ err) {
     __shared__ int32_t s_dest[MOE_EP_MAX_WORLD];
@@ -27,13 +44,18 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     __shared__ int s_n;
     const int tid = threadIdx.x;
 
+    if (tile_cnt && blockIdx.x == 0 && tid < W)
+        send_cnt[tid] = sum_tiles(tile_cnt, (T + kRouteTile - 1) / kRouteTile, W, tid);
+
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
         if (tid < 64) {
             const int d = tid;
             int32_t slot = -1;
             if (d < W) {
                 slot = token_slot[t * W + d];
-                if (slot >= 0) slot += tile_off[(t / kRouteTile) * W + d];
+                if (slot >= 0)
+                    slot += tile_cnt ? sum_tiles(tile_cnt, t / kRouteTile, W, d)
+                                     : tile_off[(t / kRouteTile) * W + d];
             }
             const uint64_t act = __ballot(slot >= 0);
             uint32_t bad = 0;
@@ -44,6 +66,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
                 token_slot[t * W + d] = slot;
                 const int64_t meta = ((int64_t)d * cap + slot) * slots;
                 int j = 0;
+#pragma unroll 8
                 for (int k = 0; k < K; ++k) {
                     const int32_t id = ids[t * K + k];
                     if (id < 0 || id >= E || id / e_local != d) continue;
@@ -72,7 +95,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                 for (int u = 0; u < kPackUnroll; ++u) {
                     const int64_t i = i0 + u * kPackThreads;
-                    if (i < nvec) v[u] = *reinterpret_cast<const u32x4*>(src + i * 16);
+                    if (i < nvec) v[u] = ld_row<MOE_EP_COPY_NT>(src + i * 16);
                 }
                 for (int a = 0; a < n; ++a) {
                     uint8_t* dst = P.dst[p] + s_dest[a] * P.dst_stride[p] +
@@ -80,7 +103,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                     for (int u = 0; u < kPackUnroll; ++u) {
                         const int64_t i = i0 + u * kPackThreads;
-                        if (i < nvec) *reinterpret_cast<u32x4*>(dst + i * 16) = v[u];
+                        if (i < nvec) st_row<MOE_EP_COPY_NT>(dst + i * 16, v[u]);
                     }
                 }
             }
@@ -92,14 +115,15 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             int K, int E, int e_local, int W, int slots,
                             int64_t cap, int32_t* token_slot,
-                            const int32_t* tile_off, const PayloadSet& P,
+                            const int32_t* tile_cnt, const int32_t* tile_off,
+                            int32_t* send_cnt, const PayloadSet& P,
                             int32_t* send_eloc, float* send_w, uint32_t* err,
                             hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int64_t grid = T < 65536 ? T : 65536;
     pack_copy_kernel<<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
-        ids, wts, T, K, E, e_local, W, slots, cap, token_slot, tile_off, P,
-        send_eloc, send_w, err);
+        ids, wts, T, K, E, e_local, W, slots, cap, token_slot, tile_cnt, tile_off,
+        send_cnt, P, send_eloc, send_w, err);
     return hipGetLastError();
 }
 

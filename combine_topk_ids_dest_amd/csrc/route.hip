@@ -9,8 +9,10 @@
 //   route_local: per tile of 256 tokens, a wave64 ballot per destination
 //     gives each token its rank among the tile's tokens for d; the tile's
 //     count per destination goes to the workspace.
-//   column_scan: exclusive prefix of the tile counts per destination (the
-//     tile offsets) and the per-destination totals (send_cnt).
+//   tile offsets: the exclusive prefix of the tile counts per destination.
+//     With at most kPackFuseTiles tiles, pack_copy sums the counts of the
+//     earlier tiles itself (and block 0 writes send_cnt); otherwise
+//     column_scan computes them and send_cnt.
 // pack_copy adds the tile offset to the in-tile rank.
 #include "common.h"
 
@@ -32,6 +34,7 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
     uint32_t bad = 0;
     if (t < T) {
         const int32_t* row = ids + t * K;
+#pragma unroll 8
         for (int k = 0; k < K; ++k) {
             const int32_t id = row[k];
             if (id < 0) continue;
@@ -63,46 +66,58 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
 
 // Exclusive prefix down the columns of cnt [ntiles][nkeys] into off, and the
 // column totals (clamped to clamp_max) into total. One block of 1024 lanes:
-// lane (g, key) first sums a contiguous run of tiles, the runs are then
-// scanned per key, and each lane finally writes its run's prefixes.
+// lane (g, key) sums a contiguous run of tiles (loads issued kScanBatch at a
+// time so their latencies overlap), each lane then adds the runs of the
+// groups before it from LDS, and finally writes its run's prefixes.
+constexpr int kScanBatch = 16;
+
+__host__ __device__ inline int scan_groups(int ntiles, int nkeys) {
+    int groups = 1024 / nkeys;
+    if (groups > 64) groups = 64;
+    if (groups > ntiles) groups = ntiles > 0 ? ntiles : 1;
+    return groups;
+}
+
 __global__ __launch_bounds__(1024) void column_scan_kernel(
     const int32_t* __restrict__ cnt, int ntiles, int nkeys,
     int32_t* __restrict__ off, int32_t* __restrict__ total, int32_t clamp_max) {
     extern __shared__ int32_t part[];   // [groups][nkeys]
-    int groups = 1024 / nkeys;
-    if (groups > 64) groups = 64;
-    if (groups > ntiles) groups = ntiles > 0 ? ntiles : 1;
+    const int groups = scan_groups(ntiles, nkeys);
     const int chunk = (ntiles + groups - 1) / groups;
+    const int i = threadIdx.x;
+    const bool active = i < groups * nkeys;
+    const int g = active ? i / nkeys : 0;
+    const int key = active ? i - g * nkeys : 0;
+    const int lo = g * chunk;
+    const int hi = active ? min(ntiles, lo + chunk) : lo;
 
-    for (int i = threadIdx.x; i < groups * nkeys; i += blockDim.x) {
-        const int g = i / nkeys, key = i - g * nkeys;
-        const int lo = g * chunk;
-        const int hi = min(ntiles, lo + chunk);
-        int32_t s = 0;
-        for (int r = lo; r < hi; ++r) s += cnt[(int64_t)r * nkeys + key];
-        part[i] = s;
+    int32_t run = 0;
+    for (int r0 = lo; r0 < hi; r0 += kScanBatch) {
+        int32_t v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+            v[u] = r0 + u < hi ? cnt[(int64_t)(r0 + u) * nkeys + key] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) run += v[u];
     }
+    if (active) part[i] = run;
     __syncthreads();
-    for (int key = threadIdx.x; key < nkeys; key += blockDim.x) {
-        int32_t run = 0;
-        for (int g = 0; g < groups; ++g) {
-            const int32_t v = part[g * nkeys + key];
-            part[g * nkeys + key] = run;
-            run += v;
-        }
-        total[key] = run < clamp_max ? run : clamp_max;
+    if (!active) return;
+    int32_t before = 0;
+    for (int g2 = 0; g2 < g; ++g2) before += part[g2 * nkeys + key];
+    if (g == groups - 1) {
+        const int32_t tot = before + run;
+        total[key] = tot < clamp_max ? tot : clamp_max;
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < groups * nkeys; i += blockDim.x) {
-        const int g = i / nkeys, key = i - g * nkeys;
-        const int lo = g * chunk;
-        const int hi = min(ntiles, lo + chunk);
-        int32_t run = part[i];
-        for (int r = lo; r < hi; ++r) {
-            const int64_t at = (int64_t)r * nkeys + key;
-            const int32_t v = cnt[at];
-            off[at] = run;
-            run += v;
+    for (int r0 = lo; r0 < hi; r0 += kScanBatch) {
+        int32_t v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+            v[u] = r0 + u < hi ? cnt[(int64_t)(r0 + u) * nkeys + key] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+            if (r0 + u < hi) off[(int64_t)(r0 + u) * nkeys + key] = before;
+            before += v[u];
         }
     }
 }
@@ -121,10 +136,7 @@ hipError_t launch_route_local(const int32_t* ids, int64_t T, int K, int E,
 hipError_t launch_column_scan(const int32_t* cnt, int ntiles, int nkeys,
                               int32_t* off, int32_t* total, int32_t clamp_max,
                               hipStream_t stream) {
-    int groups = 1024 / nkeys;
-    if (groups > 64) groups = 64;
-    if (groups > ntiles) groups = ntiles > 0 ? ntiles : 1;
-    const size_t lds = sizeof(int32_t) * (size_t)groups * nkeys;
+    const size_t lds = sizeof(int32_t) * (size_t)scan_groups(ntiles, nkeys) * nkeys + 16;
     column_scan_kernel<<<dim3(1), dim3(1024), lds, stream>>>(
         cnt, ntiles, nkeys, off, total, clamp_max);
     return hipGetLastError();

@@ -67,6 +67,7 @@ class LogicalEP:
         self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
         ws = B.moe_ep_workspace_bytes(cap, K, E, W, cap)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+        self._calls = {}
 
     # -- inputs ---------------------------------------------------------
     def set_source(self, s: int, ids, wts, payload_rows: Sequence):
@@ -79,30 +80,51 @@ class LogicalEP:
             self.src[p][s].copy_(t.reshape(self.T, self.row_bytes[p]))
 
     # -- the four calls for one logical rank ----------------------------
-    def pack(self, s: int, stream=None):
-        B.moe_ep_dispatch_pack(
+    # Each call is marshalled once (binding.prepare_*) and replayed; the
+    # buffers never move, so the prepared arguments stay valid.
+    def _prepared(self, kind: str, i: int):
+        key = (kind, i)
+        call = self._calls.get(key)
+        if call is None:
+            call = self._calls[key] = getattr(self, "_prep_" + kind)(i)
+        return call
+
+    def _prep_pack(self, s: int):
+        return B.prepare_dispatch_pack(
             self.ids[s], self.wts[s], self.E, self.W, self.cap,
             [(self.src[p][s], self.send[p][s]) for p in range(len(self.src))],
             self.send_cnt[s], self.send_eloc[s], self.send_w[s],
-            self.token_slot[s], self.err, self.workspace, stream)
+            self.token_slot[s], self.err, self.workspace)
 
-    def batch(self, r: int, stream=None):
-        B.moe_ep_expert_batch(
+    def _prep_batch(self, r: int):
+        return B.prepare_expert_batch(
             self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
             self.K, self.cap,
             [(self.send[p][:, r], self.b[p]) for p in range(len(self.src))],
             self.expert_num_tokens[r], self.recv_row[r], self.err,
-            self.workspace, stream)
+            self.workspace)
 
-    def reduce(self, r: int, stream=None):
-        B.moe_ep_combine_reduce(
+    def _prep_reduce(self, r: int):
+        return B.prepare_combine_reduce(
             self.Y, self.send_cnt[:, r], self.send_eloc[:, r], self.send_w[:, r],
             self.recv_row[r], self.W, self.e_local, self.K, self.cap,
-            self.ret[r], stream)
+            self.ret[r])
+
+    def _prep_unpack(self, s: int):
+        return B.prepare_combine_unpack(self.ret[:, s], self.token_slot[s],
+                                        self.cap, self.out[s])
+
+    def pack(self, s: int, stream=None):
+        self._prepared("pack", s)(stream)
+
+    def batch(self, r: int, stream=None):
+        self._prepared("batch", r)(stream)
+
+    def reduce(self, r: int, stream=None):
+        self._prepared("reduce", r)(stream)
 
     def unpack(self, s: int, stream=None):
-        B.moe_ep_combine_unpack(self.ret[:, s], self.token_slot[s], self.cap,
-                                self.out[s], stream)
+        self._prepared("unpack", s)(stream)
 
     def step(self, stream=None):
         """One pass of the whole path over all W logical ranks: W packs,
