@@ -34,11 +34,21 @@ if ROOT not in sys.path:
 
 METRIC = "dispatch+combine tokens/s and effective HBM GB/s (% of peak), 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
+# Calls timed one by one in the per-call pass, with the kernel that moves
+# the rows in each (moe_ep_expert_batch is timed as its two halves).
 KERNEL_OF_CALL = {
     "pack": "pack_copy_kernel",
-    "batch": "batch_copy_kernel",
+    "batch_plan": "batch_local_kernel",
+    "batch_copy": "batch_copy_kernel",
     "reduce": "combine_reduce_kernel",
     "unpack": "combine_unpack_kernel",
+}
+ABI_OF_CALL = {
+    "pack": "moe_ep_dispatch_pack",
+    "batch_plan": "moe_ep_expert_batch_plan",
+    "batch_copy": "moe_ep_expert_batch_copy",
+    "reduce": "moe_ep_combine_reduce",
+    "unpack": "moe_ep_combine_unpack",
 }
 
 
@@ -87,12 +97,12 @@ def byte_model(w, row_bytes, slots, send_cnt, ent, routed):
     R = ent.sum(axis=1)                 # per destination
     pack = [8 * w.T * w.K + int(routed[s]) * P + int(U[s]) * P + int(U[s]) * slots * 8
             + 4 * w.W for s in range(w.W)]
-    batch = [4 * w.W + int(S[r]) * slots * 4 + int(S[r]) * P + int(R[r]) * P
-             + 4 * w.e_local for r in range(w.W)]
+    batch_plan = [4 * w.W + int(S[r]) * slots * 4 + 4 * w.e_local for r in range(w.W)]
+    batch_copy = [int(S[r]) * P + int(R[r]) * P for r in range(w.W)]
     reduce = [int(R[r]) * Hb + int(S[r]) * slots * 8 + int(S[r]) * Hb for r in range(w.W)]
     unpack = [int(U[s]) * Hb + w.T * Hb for s in range(w.W)]
-    return {"pack": pack, "batch": batch, "reduce": reduce, "unpack": unpack,
-            "U": U, "S": S, "R": R}
+    return {"pack": pack, "batch_plan": batch_plan, "batch_copy": batch_copy,
+            "reduce": reduce, "unpack": unpack, "U": U, "S": S, "R": R}
 
 
 def cpu_baseline(w, srcs, pls, shares: int):
@@ -195,6 +205,8 @@ def main():
     ap.add_argument("--cpu-shares", type=int, default=8,
                     help="logical-rank shares the CPU oracle is timed on")
     ap.add_argument("--probe", choices=["copy"], default=None)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -238,10 +250,24 @@ def main():
 
     # Timed region: K whole steps, nothing else enqueued between them.
     stream = torch.cuda.current_stream()
+    run_step = ep.step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            ep.step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            ep.step()
+        torch.cuda.synchronize()
+        graph.replay()
+        run_step = graph.replay
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        ep.step()
+        run_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert int(ep.err.item()) == 0, "device reported data errors"
@@ -251,7 +277,8 @@ def main():
     # call, on the stream the library launches on (torch's current stream).
     # The events add a few microseconds between calls, so these steps are
     # timed separately from the region above.
-    kinds = ["pack"] * w.W + ["batch", "reduce"] * w.W + ["unpack"] * w.W
+    kinds = (["pack"] * w.W + ["batch_plan", "batch_copy", "reduce"] * w.W
+             + ["unpack"] * w.W)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in kinds] for _ in range(args.steps)]
     for k in range(args.steps):
@@ -259,7 +286,8 @@ def main():
         for s in range(w.W):
             ev[k][i][0].record(stream); ep.pack(s); ev[k][i][1].record(stream); i += 1
         for r in range(w.W):
-            ev[k][i][0].record(stream); ep.batch(r); ev[k][i][1].record(stream); i += 1
+            ev[k][i][0].record(stream); ep.batch_plan(r); ev[k][i][1].record(stream); i += 1
+            ev[k][i][0].record(stream); ep.batch_copy(r); ev[k][i][1].record(stream); i += 1
             ev[k][i][0].record(stream); ep.reduce(r); ev[k][i][1].record(stream); i += 1
         for s in range(w.W):
             ev[k][i][0].record(stream); ep.unpack(s); ev[k][i][1].record(stream); i += 1
@@ -288,7 +316,7 @@ def main():
     roofline = {
         "bound": "hbm",
         "kernel": KERNEL_OF_CALL[dom],
-        "call": f"moe_ep_{ {'pack': 'dispatch_pack', 'batch': 'expert_batch', 'reduce': 'combine_reduce', 'unpack': 'combine_unpack'}[dom] }",
+        "call": ABI_OF_CALL[dom],
         "achieved": round(achieved, 1),
         "peak": PEAK_HBM_GBPS,
         "unit": "GB/s",
@@ -317,6 +345,7 @@ def main():
             + (f" s={w.zipf_s}" if w.routing == "zipf" else ""),
             "padding_rows": w.n_pad, "payload_bytes_per_row": int(sum(row_bytes)),
             "combine_accumulation": "fp32",
+            "launch": "hip_graph" if args.graph else "eager",
             "parallelism": f"1 GPU, {w.W} logical expert-parallel ranks",
         },
         "effective_gbps": round(gbps, 1),

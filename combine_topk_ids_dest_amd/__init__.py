@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     moe_ep_combine_unpack,
     moe_ep_dispatch_pack,
     moe_ep_expert_batch,
+    moe_ep_expert_batch_copy,
+    moe_ep_expert_batch_plan,
     moe_ep_workspace_bytes,
     status_string,
 )

@@ -28,6 +28,8 @@ EXPORTED = (
     "moe_ep_status_string",
     "moe_ep_dispatch_pack",
     "moe_ep_expert_batch",
+    "moe_ep_expert_batch_plan",
+    "moe_ep_expert_batch_copy",
     "moe_ep_combine_reduce",
     "moe_ep_combine_unpack",
 )
@@ -73,6 +75,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_ep_expert_batch.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
         _P, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_expert_batch_plan.argtypes = [
+        _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_expert_batch_copy.argtypes = [
+        _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32, _P, _P, _P, _SZ, _P]
     lib.moe_ep_combine_reduce.argtypes = [
         _P, _I64, _I32, _I64, _P, _I64, _P, _P, _I64, _P,
         _I32, _I32, _I32, _I64, _P, _I64, _P]
@@ -249,6 +255,57 @@ def moe_ep_expert_batch(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
     prepare_expert_batch(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
                          payloads, expert_num_tokens, recv_row, err_flags,
                          workspace)(stream)
+
+
+def prepare_expert_batch_plan(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
+                              W: int, e_local: int, K: int, max_num_tokens: int,
+                              expert_num_tokens: torch.Tensor, recv_row: torch.Tensor,
+                              err_flags: Optional[torch.Tensor],
+                              workspace: torch.Tensor) -> PreparedCall:
+    """The receive scan half of moe_ep_expert_batch."""
+    _dense_from(recv_eloc, 1, "recv_eloc")
+    _dense_from(recv_row, 0, "recv_row")
+    _dense_from(expert_num_tokens, 0, "expert_num_tokens")
+    args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
+            W, e_local, K, max_num_tokens, _ptr(expert_num_tokens), _ptr(recv_row),
+            _ptr(err_flags), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    return PreparedCall("moe_ep_expert_batch_plan", args,
+                        (recv_cnt, recv_eloc, expert_num_tokens, recv_row,
+                         err_flags, workspace))
+
+
+def prepare_expert_batch_copy(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
+                              W: int, e_local: int, K: int, max_num_tokens: int,
+                              payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                              recv_row: torch.Tensor,
+                              err_flags: Optional[torch.Tensor],
+                              workspace: torch.Tensor) -> PreparedCall:
+    """The row copy half of moe_ep_expert_batch (after the plan)."""
+    _dense_from(recv_eloc, 1, "recv_eloc")
+    _dense_from(recv_row, 0, "recv_row")
+    arr = _payload_array(payloads, 2, 2)
+    args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
+            W, e_local, K, max_num_tokens, ctypes.addressof(arr), len(payloads),
+            _ptr(recv_row), _ptr(err_flags), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    return PreparedCall("moe_ep_expert_batch_copy", args,
+                        (arr, recv_cnt, recv_eloc, payloads, recv_row, err_flags,
+                         workspace))
+
+
+def moe_ep_expert_batch_plan(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
+                             expert_num_tokens, recv_row, err_flags, workspace,
+                             stream=None) -> None:
+    prepare_expert_batch_plan(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
+                              expert_num_tokens, recv_row, err_flags, workspace)(stream)
+
+
+def moe_ep_expert_batch_copy(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
+                             payloads, recv_row, err_flags, workspace,
+                             stream=None) -> None:
+    prepare_expert_batch_copy(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
+                              payloads, recv_row, err_flags, workspace)(stream)
 
 
 def prepare_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,

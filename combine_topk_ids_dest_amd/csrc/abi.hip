@@ -40,7 +40,7 @@ int check_shape(int32_t K, int32_t e_local, int32_t W, int64_t max_num_tokens,
 }
 
 // Workspace regions, each padded to 128 bytes.
-struct PackWs { int64_t ntiles, cnt_off, off_off, bytes; };
+struct PackWs { int64_t ntiles, cnt_off, off_off, rank_off, bytes; };
 struct BatchWs { int64_t ntiles, cnt_off, off_off, bytes; };
 
 PackWs pack_ws(int64_t T, int32_t W) {
@@ -49,7 +49,8 @@ PackWs pack_ws(int64_t T, int32_t W) {
     const int64_t region = round_up(w.ntiles * W * 4, 128);
     w.cnt_off = 0;
     w.off_off = region;
-    w.bytes = 2 * region;
+    w.rank_off = 2 * region;
+    w.bytes = w.rank_off + round_up(T * W * 4, 128);
     return w;
 }
 
@@ -102,6 +103,56 @@ int elem_bytes(int32_t dtype) {
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_EP_OK : MOE_EP_EHIP; }
+
+// Checks shared by the receive-side calls; fills sh and the workspace
+// layout.
+int check_batch(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                const int32_t* recv_eloc, int64_t eloc_rank_stride, int32_t W,
+                int32_t e_local, int32_t K, int64_t max_num_tokens,
+                const int32_t* recv_row, void* workspace, size_t workspace_bytes,
+                Shape* sh, BatchWs* ws) {
+    int rc = check_shape(K, e_local, W, max_num_tokens, sh);
+    if (rc) return rc;
+    if (!recv_cnt || !recv_eloc || !recv_row) return MOE_EP_EINVAL;
+    if (cnt_rank_stride < 1 || eloc_rank_stride < sh->cap * sh->slots)
+        return MOE_EP_EINVAL;
+    *ws = batch_ws(*sh);
+    if (ws->bytes > 0 && (!workspace || workspace_bytes < (size_t)ws->bytes))
+        return MOE_EP_EWORKSPACE;
+    if (workspace && !aligned16(workspace)) return MOE_EP_EALIGN;
+    return MOE_EP_OK;
+}
+
+int launch_plan(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                const Shape& sh, const BatchWs& ws, int32_t* expert_num_tokens,
+                int32_t* recv_row, uint32_t* err_flags, void* workspace,
+                hipStream_t st) {
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    int32_t* tile_cnt = reinterpret_cast<int32_t*>(wsb + ws.cnt_off);
+    int32_t* tile_off = reinterpret_cast<int32_t*>(wsb + ws.off_off);
+    const int32_t clamp = sh.expert_cap < kI32Max ? (int32_t)sh.expert_cap : INT_MAX;
+    int rc = hip_status(launch_batch_local(recv_cnt, cnt_rank_stride, recv_eloc,
+                                           eloc_rank_stride, sh.W, sh.e_local,
+                                           sh.slots, sh.cap, (int)ws.ntiles,
+                                           recv_row, tile_cnt, err_flags, st));
+    if (rc) return rc;
+    return hip_status(launch_column_scan(tile_cnt, (int)ws.ntiles, sh.e_local,
+                                         tile_off, expert_num_tokens, clamp, st));
+}
+
+int launch_copy(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                const Shape& sh, const BatchWs& ws, const PayloadSet& P,
+                int32_t* recv_row, uint32_t* err_flags, void* workspace,
+                hipStream_t st) {
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    const int32_t* tile_off = reinterpret_cast<const int32_t*>(wsb + ws.off_off);
+    return hip_status(launch_batch_copy(recv_cnt, cnt_rank_stride, recv_eloc,
+                                        eloc_rank_stride, sh.W, sh.e_local,
+                                        sh.slots, sh.cap, tile_off, recv_row, P,
+                                        err_flags, st));
+}
 
 }  // namespace
 
@@ -172,9 +223,10 @@ int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
     uint8_t* wsb = static_cast<uint8_t*>(workspace);
     int32_t* tile_cnt = reinterpret_cast<int32_t*>(wsb + ws.cnt_off);
     int32_t* tile_off = reinterpret_cast<int32_t*>(wsb + ws.off_off);
+    int32_t* rank = reinterpret_cast<int32_t*>(wsb + ws.rank_off);
 
     rc = hip_status(launch_route_local(topk_ids, T, K, E, sh.e_local, W,
-                                       token_slot, tile_cnt, err_flags, st));
+                                       rank, tile_cnt, err_flags, st));
     if (rc) return rc;
     // Few tiles (or none): pack_copy sums the tile counts itself; the scan
     // kernel still runs for T = 0 so that send_cnt is written.
@@ -185,10 +237,51 @@ int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
         if (rc) return rc;
     }
     return hip_status(launch_pack_copy(topk_ids, topk_weights, T, K, E,
-                                       sh.e_local, W, sh.slots, sh.cap,
+                                       sh.e_local, W, sh.slots, sh.cap, rank,
                                        token_slot, fused ? tile_cnt : nullptr,
                                        tile_off, send_cnt, P, send_eloc,
                                        send_w, err_flags, st));
+}
+
+int moe_ep_expert_batch_plan(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                             const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                             int32_t W, int32_t e_local, int32_t K,
+                             int64_t max_num_tokens, int32_t* expert_num_tokens,
+                             int32_t* recv_row, uint32_t* err_flags,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    Shape sh;
+    BatchWs ws;
+    int rc = check_batch(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride,
+                         W, e_local, K, max_num_tokens, recv_row, workspace,
+                         workspace_bytes, &sh, &ws);
+    if (rc) return rc;
+    if (!expert_num_tokens) return MOE_EP_EINVAL;
+    return launch_plan(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride, sh,
+                       ws, expert_num_tokens, recv_row, err_flags, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+int moe_ep_expert_batch_copy(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                             const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                             int32_t W, int32_t e_local, int32_t K,
+                             int64_t max_num_tokens,
+                             const moe_ep_payload* payloads, int32_t n_payloads,
+                             int32_t* recv_row, uint32_t* err_flags,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    Shape sh;
+    BatchWs ws;
+    int rc = check_batch(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride,
+                         W, e_local, K, max_num_tokens, recv_row, workspace,
+                         workspace_bytes, &sh, &ws);
+    if (rc) return rc;
+    PayloadSet P;
+    rc = check_payloads(payloads, n_payloads, sh.cap, sh.expert_cap, true, &P);
+    if (rc) return rc;
+    return launch_copy(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride, sh,
+                       ws, P, recv_row, err_flags, workspace,
+                       static_cast<hipStream_t>(stream));
 }
 
 int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_stride,
@@ -200,38 +293,21 @@ int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_stride,
                         uint32_t* err_flags, void* workspace,
                         size_t workspace_bytes, void* stream) {
     Shape sh;
-    int rc = check_shape(K, e_local, W, max_num_tokens, &sh);
+    BatchWs ws;
+    int rc = check_batch(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride,
+                         W, e_local, K, max_num_tokens, recv_row, workspace,
+                         workspace_bytes, &sh, &ws);
     if (rc) return rc;
-    if (!recv_cnt || !recv_eloc || !expert_num_tokens || !recv_row)
-        return MOE_EP_EINVAL;
-    if (cnt_rank_stride < 1 || eloc_rank_stride < sh.cap * sh.slots)
-        return MOE_EP_EINVAL;
+    if (!expert_num_tokens) return MOE_EP_EINVAL;
     PayloadSet P;
     rc = check_payloads(payloads, n_payloads, sh.cap, sh.expert_cap, true, &P);
     if (rc) return rc;
-    const BatchWs ws = batch_ws(sh);
-    if (ws.bytes > 0 && (!workspace || workspace_bytes < (size_t)ws.bytes))
-        return MOE_EP_EWORKSPACE;
-    if (workspace && !aligned16(workspace)) return MOE_EP_EALIGN;
-
     hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t* wsb = static_cast<uint8_t*>(workspace);
-    int32_t* tile_cnt = reinterpret_cast<int32_t*>(wsb + ws.cnt_off);
-    int32_t* tile_off = reinterpret_cast<int32_t*>(wsb + ws.off_off);
-    const int32_t clamp = sh.expert_cap < kI32Max ? (int32_t)sh.expert_cap : INT_MAX;
-
-    rc = hip_status(launch_batch_local(recv_cnt, cnt_rank_stride, recv_eloc,
-                                       eloc_rank_stride, W, e_local, sh.slots,
-                                       sh.cap, (int)ws.ntiles, recv_row,
-                                       tile_cnt, err_flags, st));
+    rc = launch_plan(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride, sh, ws,
+                     expert_num_tokens, recv_row, err_flags, workspace, st);
     if (rc) return rc;
-    rc = hip_status(launch_column_scan(tile_cnt, (int)ws.ntiles, e_local,
-                                       tile_off, expert_num_tokens, clamp, st));
-    if (rc) return rc;
-    return hip_status(launch_batch_copy(recv_cnt, cnt_rank_stride, recv_eloc,
-                                        eloc_rank_stride, W, e_local, sh.slots,
-                                        sh.cap, tile_off, recv_row, P,
-                                        err_flags, st));
+    return launch_copy(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride, sh, ws,
+                       P, recv_row, err_flags, workspace, st);
 }
 
 int moe_ep_combine_reduce(const void* expert_out, int64_t expert_stride,

@@ -11,9 +11,10 @@
 // it went to, summed in fp32 in ascending rank order from +0.0f and rounded
 // once; a token that went nowhere (padding) gets +0.0.
 //
-// Both are one row per block with 16-byte vector lanes. Wave 0 gathers the
-// row's sources (expert rows with weights, or returned partial slots) into
-// LDS in summation order; every lane then streams its columns.
+// Both are one row (the unpack: one column part of a row when there are few
+// tokens) per block with 16-byte vector lanes. Wave 0 gathers the row's
+// sources (expert rows with weights, or returned partial slots) into LDS in
+// summation order; every lane then streams its columns.
 #include "common.h"
 
 namespace moe_ep {
@@ -65,16 +66,17 @@ struct F32Elems {
     }
 };
 
-// out[i] = sum over a < n, in order, of (w_a *) fp32(row_a[i]) for every
-// 16-byte vector i of a row, accumulated from +0.0f with each product
-// rounded to fp32 before the add. Row a starts at base + off[a] (bytes).
+// out[i] = sum over a < n, in order, of (w_a *) fp32(row_a[i]) for the
+// 16-byte vectors v_lo <= i < nvec of a row, accumulated from +0.0f with
+// each product rounded to fp32 before the add. Row a starts at
+// base + off[a] (bytes).
 template <class Elems, bool WEIGHTED, int PG>
 __device__ __forceinline__ void sum_rows(const uint8_t* __restrict__ base,
                                          const int64_t* off, const float* w,
-                                         int n, int64_t nvec,
+                                         int n, int64_t v_lo, int64_t nvec,
                                          uint8_t* __restrict__ out) {
     constexpr int V = Elems::kPerVec;
-    for (int64_t i0 = threadIdx.x; i0 < nvec; i0 += kCombineThreads * kVU) {
+    for (int64_t i0 = v_lo + threadIdx.x; i0 < nvec; i0 += kCombineThreads * kVU) {
         float acc[kVU][V];
 #pragma unroll
         for (int v = 0; v < kVU; ++v)
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_reduce_kernel(
         }
         __syncthreads();
         sum_rows<Elems, true, MOE_EP_REDUCE_PG>(
-            Y, s_base, s_w, s_n, nvec,
+            Y, s_base, s_w, s_n, 0, nvec,
             ret + (s * ret_stride + (int64_t)slot * H) * ELEM_BYTES);
         __syncthreads();
     }
@@ -177,14 +179,18 @@ template <class Elems, int ELEM_BYTES>
 __global__ __launch_bounds__(kCombineThreads) void combine_unpack_kernel(
     const uint8_t* __restrict__ back, int64_t back_stride, int64_t H,
     const int32_t* __restrict__ token_slot, int64_t T, int W, int64_t cap,
-    uint8_t* __restrict__ out) {
+    int nsplit, uint8_t* __restrict__ out) {
     __shared__ int64_t s_base[MOE_EP_MAX_WORLD];
     __shared__ int s_n;
     const int tid = threadIdx.x;
     const int64_t row_bytes = H * ELEM_BYTES;
     const int64_t nvec = row_bytes >> 4;
+    const int64_t per = (nvec + nsplit - 1) / nsplit;
 
-    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    for (int64_t b = blockIdx.x; b < T * nsplit; b += gridDim.x) {
+        const int64_t t = b / nsplit;
+        const int64_t v_lo = (b - t * nsplit) * per;
+        const int64_t v_hi = v_lo + per < nvec ? v_lo + per : nvec;
         if (tid < 64) {
             const int d = tid;
             int32_t slot = -1;
@@ -196,8 +202,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_unpack_kernel(
             if (tid == 0) s_n = __popcll(act);
         }
         __syncthreads();
-        sum_rows<Elems, false, MOE_EP_UNPACK_PG>(back, s_base, nullptr, s_n, nvec,
-                                                 out + t * row_bytes);
+        sum_rows<Elems, false, MOE_EP_UNPACK_PG>(back, s_base, nullptr, s_n, v_lo,
+                                                 v_hi, out + t * row_bytes);
         __syncthreads();
     }
 }
@@ -230,15 +236,18 @@ hipError_t launch_combine_unpack(const void* back, int64_t back_stride,
                                  const int32_t* token_slot, int64_t T, int W,
                                  int64_t cap, void* out, hipStream_t stream) {
     if (T == 0) return hipSuccess;
-    const int64_t grid = T < 65536 ? T : 65536;
+    const int eb = dtype == MOE_EP_BF16 ? 2 : 4;
+    const int nsplit = row_split(T, H * eb / 16);
+    const int64_t blocks = T * nsplit;
+    const int64_t grid = blocks < 65536 ? blocks : 65536;
     const uint8_t* b = static_cast<const uint8_t*>(back);
     uint8_t* o = static_cast<uint8_t*>(out);
     if (dtype == MOE_EP_BF16)
         combine_unpack_kernel<Bf16Elems, 2><<<dim3((unsigned)grid), dim3(kCombineThreads), 0, stream>>>(
-            b, back_stride, H, token_slot, T, W, cap, o);
+            b, back_stride, H, token_slot, T, W, cap, nsplit, o);
     else
         combine_unpack_kernel<F32Elems, 4><<<dim3((unsigned)grid), dim3(kCombineThreads), 0, stream>>>(
-            b, back_stride, H, token_slot, T, W, cap, o);
+            b, back_stride, H, token_slot, T, W, cap, nsplit, o);
     return hipGetLastError();
 }
 

@@ -129,8 +129,18 @@ __device__ __forceinline__ uint32_t to_bf16_rne(float f) {
 // Launchers (defined next to their kernels). All return hipError_t of the
 // launch; grids are computed from host-known sizes only.
 // ---------------------------------------------------------------------
+// Column parts a row is cut into so that `rows` rows still give enough
+// blocks to fill the chip; no part is narrower than one pass of 256 lanes.
+inline int row_split(int64_t rows, int64_t max_vecs) {
+    int64_t s = rows > 0 ? (2048 + rows - 1) / rows : 1;
+    const int64_t by_width = max_vecs / 256 > 0 ? max_vecs / 256 : 1;
+    if (s > by_width) s = by_width;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
 hipError_t launch_route_local(const int32_t* ids, int64_t T, int K, int E,
-                              int e_local, int W, int32_t* token_slot,
+                              int e_local, int W, int32_t* rank,
                               int32_t* tile_cnt, uint32_t* err,
                               hipStream_t stream);
 
@@ -138,16 +148,17 @@ hipError_t launch_column_scan(const int32_t* cnt, int ntiles, int nkeys,
                               int32_t* off, int32_t* total, int32_t clamp_max,
                               hipStream_t stream);
 
+// rank: the in-tile ranks of route_local ([T, W], -1 = no pair).
 // tile_cnt != nullptr selects the fused tile offsets (ntiles <=
 // kPackFuseTiles): offsets are summed from tile_cnt and block 0 writes
 // send_cnt; otherwise tile_off holds the offsets from column_scan.
 hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             int K, int E, int e_local, int W, int slots,
-                            int64_t cap, int32_t* token_slot,
-                            const int32_t* tile_cnt, const int32_t* tile_off,
-                            int32_t* send_cnt, const PayloadSet& P,
-                            int32_t* send_eloc, float* send_w, uint32_t* err,
-                            hipStream_t stream);
+                            int64_t cap, const int32_t* rank,
+                            int32_t* token_slot, const int32_t* tile_cnt,
+                            const int32_t* tile_off, int32_t* send_cnt,
+                            const PayloadSet& P, int32_t* send_eloc,
+                            float* send_w, uint32_t* err, hipStream_t stream);
 
 hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
                               const int32_t* recv_eloc, int64_t eloc_stride,

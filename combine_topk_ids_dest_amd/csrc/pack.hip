@@ -4,13 +4,15 @@
 // wants on that rank, in router order, as a local id with its fp32 weight;
 // unused columns hold -1 and +0.0).
 //
-// Token-major: a block takes one token, reads each payload row from HBM
-// once into registers (16-byte vectors) and stores it to every destination
-// the token goes to (5.3 on average for 256 experts, top-8, 8 ranks). Wave 0
-// turns the in-tile ranks into final slots (adding the offset of the token's
-// tile, summed here from the tile counts when there are few tiles), writes
-// the final token_slot context and the pick metadata, and leaves the
-// destination list in LDS.
+// Token-major: a token's row is read from HBM once into registers (16-byte
+// vectors) and stored to every destination the token goes to (5.3 on average
+// for 256 experts, top-8, 8 ranks). When there are few tokens (decode), each
+// row is cut into `nsplit` column parts handled by different blocks, so the
+// grid still fills the chip. In every block wave 0 turns the token's in-tile
+// ranks into final slots (adding the offset of its tile, summed here from
+// the tile counts when there are few tiles) and leaves the destination list
+// in LDS; the block of part 0 also writes the final token_slot context and
+// the pick metadata.
 #include "common.h"
 
 namespace moe_ep {
@@ -34,11 +36,12 @@ __device__ __forceinline__ int32_t sum_tiles(const int32_t* __restrict__ tile_cn
 
 __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t T,
-    int K, int E, int e_local, int W, int slots, int64_t cap,
-    int32_t* __restrict__ token_slot, const int32_t* __restrict__ tile_cnt,
-    const int32_t* __restrict__ tile_off, int32_t* __restrict__ send_cnt,
-    const PayloadSet P, int32_t* __restrict__ send_eloc,
-    float* __restrict__ send_w, uint32_t* __restrict__ err) {
+    int K, int E, int e_local, int W, int slots, int64_t cap, int nsplit,
+    const int32_t* __restrict__ rank, int32_t* __restrict__ token_slot,
+    const int32_t* __restrict__ tile_cnt, const int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ send_cnt, const PayloadSet P,
+    int32_t* __restrict__ send_eloc, float* __restrict__ send_w,
+    uint32_t* __restrict__ err) {
     __shared__ int32_t s_dest[MOE_EP_MAX_WORLD];
     __shared__ int32_t s_slot[MOE_EP_MAX_WORLD];
     __shared__ int s_n;
@@ -47,55 +50,64 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     if (tile_cnt && blockIdx.x == 0 && tid < W)
         send_cnt[tid] = sum_tiles(tile_cnt, (T + kRouteTile - 1) / kRouteTile, W, tid);
 
-    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    for (int64_t b = blockIdx.x; b < T * nsplit; b += gridDim.x) {
+        const int64_t t = b / nsplit;
+        const int part = (int)(b - t * nsplit);
         if (tid < 64) {
             const int d = tid;
             int32_t slot = -1;
             if (d < W) {
-                slot = token_slot[t * W + d];
+                slot = rank[t * W + d];
                 if (slot >= 0)
                     slot += tile_cnt ? sum_tiles(tile_cnt, t / kRouteTile, W, d)
                                      : tile_off[(t / kRouteTile) * W + d];
             }
             const uint64_t act = __ballot(slot >= 0);
-            uint32_t bad = 0;
             if (slot >= 0) {
                 const int pos = rank_below(act);
                 s_dest[pos] = d;
                 s_slot[pos] = slot;
-                token_slot[t * W + d] = slot;
-                const int64_t meta = ((int64_t)d * cap + slot) * slots;
-                int j = 0;
-#pragma unroll 8
-                for (int k = 0; k < K; ++k) {
-                    const int32_t id = ids[t * K + k];
-                    if (id < 0 || id >= E || id / e_local != d) continue;
-                    if (j >= slots) { bad |= MOE_EP_ERR_PICKS; continue; }
-                    send_eloc[meta + j] = id - d * e_local;
-                    send_w[meta + j] = wts[t * K + k];
-                    ++j;
-                }
-                for (; j < slots; ++j) {
-                    send_eloc[meta + j] = -1;
-                    send_w[meta + j] = 0.0f;
-                }
             }
-            report(err, bad);
+            if (part == 0 && d < W) {
+                token_slot[t * W + d] = slot;
+                uint32_t bad = 0;
+                if (slot >= 0) {
+                    const int64_t meta = ((int64_t)d * cap + slot) * slots;
+                    int j = 0;
+#pragma unroll 8
+                    for (int k = 0; k < K; ++k) {
+                        const int32_t id = ids[t * K + k];
+                        if (id < 0 || id >= E || id / e_local != d) continue;
+                        if (j >= slots) { bad |= MOE_EP_ERR_PICKS; continue; }
+                        send_eloc[meta + j] = id - d * e_local;
+                        send_w[meta + j] = wts[t * K + k];
+                        ++j;
+                    }
+                    for (; j < slots; ++j) {
+                        send_eloc[meta + j] = -1;
+                        send_w[meta + j] = 0.0f;
+                    }
+                }
+                report(err, bad);
+            }
             if (tid == 0) s_n = __popcll(act);
         }
         __syncthreads();
         const int n = s_n;
 
         for (int p = 0; p < P.n; ++p) {
-            const uint8_t* src = P.src[p] + t * P.src_stride[p];
             const int64_t rb = P.row_bytes[p];
             const int64_t nvec = rb >> 4;
-            for (int64_t i0 = tid; i0 < nvec; i0 += kPackThreads * kPackUnroll) {
+            const int64_t per = (nvec + nsplit - 1) / nsplit;
+            const int64_t v_lo = part * per;
+            const int64_t v_hi = v_lo + per < nvec ? v_lo + per : nvec;
+            const uint8_t* src = P.src[p] + t * P.src_stride[p];
+            for (int64_t i0 = v_lo + tid; i0 < v_hi; i0 += kPackThreads * kPackUnroll) {
                 u32x4 v[kPackUnroll];
 #pragma unroll
                 for (int u = 0; u < kPackUnroll; ++u) {
                     const int64_t i = i0 + u * kPackThreads;
-                    if (i < nvec) v[u] = ld_row<MOE_EP_COPY_NT>(src + i * 16);
+                    if (i < v_hi) v[u] = ld_row<MOE_EP_COPY_NT>(src + i * 16);
                 }
                 for (int a = 0; a < n; ++a) {
                     uint8_t* dst = P.dst[p] + s_dest[a] * P.dst_stride[p] +
@@ -103,7 +115,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                     for (int u = 0; u < kPackUnroll; ++u) {
                         const int64_t i = i0 + u * kPackThreads;
-                        if (i < nvec) st_row<MOE_EP_COPY_NT>(dst + i * 16, v[u]);
+                        if (i < v_hi) st_row<MOE_EP_COPY_NT>(dst + i * 16, v[u]);
                     }
                 }
             }
@@ -114,16 +126,21 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 
 hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             int K, int E, int e_local, int W, int slots,
-                            int64_t cap, int32_t* token_slot,
-                            const int32_t* tile_cnt, const int32_t* tile_off,
-                            int32_t* send_cnt, const PayloadSet& P,
-                            int32_t* send_eloc, float* send_w, uint32_t* err,
-                            hipStream_t stream) {
+                            int64_t cap, const int32_t* rank,
+                            int32_t* token_slot, const int32_t* tile_cnt,
+                            const int32_t* tile_off, int32_t* send_cnt,
+                            const PayloadSet& P, int32_t* send_eloc,
+                            float* send_w, uint32_t* err, hipStream_t stream) {
     if (T == 0) return hipSuccess;
-    const int64_t grid = T < 65536 ? T : 65536;
+    int64_t max_vecs = 0;
+    for (int p = 0; p < P.n; ++p)
+        if (P.row_bytes[p] / 16 > max_vecs) max_vecs = P.row_bytes[p] / 16;
+    const int nsplit = row_split(T, max_vecs);
+    const int64_t blocks = T * nsplit;
+    const int64_t grid = blocks < 65536 ? blocks : 65536;
     pack_copy_kernel<<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
-        ids, wts, T, K, E, e_local, W, slots, cap, token_slot, tile_cnt, tile_off,
-        send_cnt, P, send_eloc, send_w, err);
+        ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
+        tile_cnt, tile_off, send_cnt, P, send_eloc, send_w, err);
     return hipGetLastError();
 }
 

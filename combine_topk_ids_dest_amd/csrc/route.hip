@@ -7,8 +7,8 @@
 // Slot of (d, t) = number of tokens t' < t that also go to d. It is built in
 // two levels without atomics, so the result does not depend on scheduling:
 //   route_local: per tile of 256 tokens, a wave64 ballot per destination
-//     gives each token its rank among the tile's tokens for d; the tile's
-//     count per destination goes to the workspace.
+//     gives each token its rank among the tile's tokens for d (kept in the
+//     workspace); the tile's count per destination goes to the workspace.
 //   tile offsets: the exclusive prefix of the tile counts per destination.
 //     With at most kPackFuseTiles tiles, pack_copy sums the counts of the
 //     earlier tiles itself (and block 0 writes send_cnt); otherwise
@@ -20,7 +20,7 @@ namespace moe_ep {
 
 __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
     const int32_t* __restrict__ ids, int64_t T, int K, int E, int e_local,
-    int W, int32_t* __restrict__ token_slot, int32_t* __restrict__ tile_cnt,
+    int W, int32_t* __restrict__ rank, int32_t* __restrict__ tile_cnt,
     uint32_t* __restrict__ err) {
     __shared__ int32_t wave_cnt[kRouteTile / 64][MOE_EP_MAX_WORLD];
     const int tid = threadIdx.x;
@@ -49,18 +49,25 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
         if (lane == 0) wave_cnt[wave][d] = __popcll(b);
     }
     __syncthreads();
+    // Per destination: the tile's count, and wave_cnt[w][d] becomes the
+    // number of the tile's tokens for d in waves before w.
+    if (tid < W) {
+        int32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < kRouteTile / 64; ++w) {
+            const int32_t v = wave_cnt[w][tid];
+            wave_cnt[w][tid] = run;
+            run += v;
+        }
+        tile_cnt[(int64_t)blockIdx.x * W + tid] = run;
+    }
+    __syncthreads();
 
     for (int d = 0; d < W; ++d) {
         const uint64_t b = __ballot((mask >> d) & 1ull);
-        int32_t before = 0;
-        for (int w = 0; w < wave; ++w) before += wave_cnt[w][d];
+        const int32_t before = wave_cnt[wave][d];
         if (t < T)
-            token_slot[t * W + d] = ((mask >> d) & 1ull) ? before + rank_below(b) : -1;
-    }
-    if (tid < W) {
-        int32_t n = 0;
-        for (int w = 0; w < kRouteTile / 64; ++w) n += wave_cnt[w][tid];
-        tile_cnt[(int64_t)blockIdx.x * W + tid] = n;
+            rank[t * W + d] = ((mask >> d) & 1ull) ? before + rank_below(b) : -1;
     }
 }
 
@@ -123,13 +130,13 @@ __global__ __launch_bounds__(1024) void column_scan_kernel(
 }
 
 hipError_t launch_route_local(const int32_t* ids, int64_t T, int K, int E,
-                              int e_local, int W, int32_t* token_slot,
+                              int e_local, int W, int32_t* rank,
                               int32_t* tile_cnt, uint32_t* err,
                               hipStream_t stream) {
     const int64_t ntiles = (T + kRouteTile - 1) / kRouteTile;
     if (ntiles == 0) return hipSuccess;
     route_local_kernel<<<dim3((unsigned)ntiles), dim3(kRouteTile), 0, stream>>>(
-        ids, T, K, E, e_local, W, token_slot, tile_cnt, err);
+        ids, T, K, E, e_local, W, rank, tile_cnt, err);
     return hipGetLastError();
 }
 

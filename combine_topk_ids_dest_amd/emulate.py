@@ -104,6 +104,19 @@ class LogicalEP:
             self.expert_num_tokens[r], self.recv_row[r], self.err,
             self.workspace)
 
+    def _prep_batch_plan(self, r: int):
+        return B.prepare_expert_batch_plan(
+            self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
+            self.K, self.cap, self.expert_num_tokens[r], self.recv_row[r],
+            self.err, self.workspace)
+
+    def _prep_batch_copy(self, r: int):
+        return B.prepare_expert_batch_copy(
+            self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
+            self.K, self.cap,
+            [(self.send[p][:, r], self.b[p]) for p in range(len(self.src))],
+            self.recv_row[r], self.err, self.workspace)
+
     def _prep_reduce(self, r: int):
         return B.prepare_combine_reduce(
             self.Y, self.send_cnt[:, r], self.send_eloc[:, r], self.send_w[:, r],
@@ -119,6 +132,12 @@ class LogicalEP:
 
     def batch(self, r: int, stream=None):
         self._prepared("batch", r)(stream)
+
+    def batch_plan(self, r: int, stream=None):
+        self._prepared("batch_plan", r)(stream)
+
+    def batch_copy(self, r: int, stream=None):
+        self._prepared("batch_copy", r)(stream)
 
     def reduce(self, r: int, stream=None):
         self._prepared("reduce", r)(stream)

@@ -177,6 +177,36 @@ MOE_EP_API int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_str
                         size_t workspace_bytes, void* stream);
 
 /*
+ * The two halves of moe_ep_expert_batch, for callers that overlap them with
+ * the exchange: the plan needs only the counts and local ids (small, sent
+ * ahead of the payload rows), the copy needs the payload rows. Arguments
+ * mean what they mean for moe_ep_expert_batch.
+ *
+ * moe_ep_expert_batch_plan: scans the received metadata; writes
+ * expert_num_tokens and, in the workspace and recv_row, the row plan.
+ * moe_ep_expert_batch_copy: moves every payload row to its expert rows and
+ * completes recv_row. It must follow the plan on the same stream with the
+ * same metadata, recv_row and workspace (which must not be used by another
+ * call in between). plan + copy == moe_ep_expert_batch.
+ */
+MOE_EP_API int moe_ep_expert_batch_plan(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                                        const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                                        int32_t W, int32_t e_local, int32_t K,
+                                        int64_t max_num_tokens,
+                                        int32_t* expert_num_tokens, int32_t* recv_row,
+                                        uint32_t* err_flags, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+MOE_EP_API int moe_ep_expert_batch_copy(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                                        const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                                        int32_t W, int32_t e_local, int32_t K,
+                                        int64_t max_num_tokens,
+                                        const moe_ep_payload* payloads, int32_t n_payloads,
+                                        int32_t* recv_row, uint32_t* err_flags,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
  * Combine, on the destination rank (finalize() on the vLLM page: weight
  * and reduce a token's experts so the return is token-sized). For every
  * valid received slot (s, slot) and column h:

@@ -74,7 +74,7 @@ def expert_out_host(w: wl.Workload, r: int, counts, salt: int, f32: bool):
 
 
 def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
-                    srcs=None, pls=None, corrupt_cnt=None):
+                    srcs=None, pls=None, corrupt_cnt=None, split_batch=False):
     """Whole path on W logical ranks, every output compared element by
     element with the oracle. Returns (ep, oracle result)."""
     if srcs is None:
@@ -155,7 +155,11 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
         ep.send_cnt[s_c, r_c] = v_c
 
     for r in range(w.W):
-        ep.batch(r)
+        if split_batch:
+            ep.batch_plan(r)
+            ep.batch_copy(r)
+        else:
+            ep.batch(r)
         Yd = torch.from_numpy(Ys[r].view(np.int16) if not f32 else Ys[r])
         ep.Y.view(torch.uint8).fill_(SENTINEL)
         ep.Y[:, :Ys[r].shape[1]].copy_(Yd.view(dt) if not f32 else Yd)

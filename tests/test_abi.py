@@ -68,8 +68,12 @@ def test_capacities_and_workspace():
         assert e.value.status == B.EINVAL
     ws = B.moe_ep_workspace_bytes(4096, 8, 256, 8, 4096)
     assert ws > 0 and ws % 128 == 0
-    # receive-scan tiles dominate: 8*4096*8/1024 tiles x 32 experts x 4 B x 2
-    assert ws == 256 * 32 * 4 * 2
+    # send side: 16 token tiles x 8 ranks (counts and offsets, each padded to
+    # 128 B) + in-tile ranks [4096, 8]; receive side: 8*4096*8/1024 tiles x
+    # 32 experts x 4 B x 2. The larger wins.
+    send = 2 * 512 + 4096 * 8 * 4
+    recv = 256 * 32 * 4 * 2
+    assert ws == max(send, recv) == send
     with pytest.raises(B.MoeEpError) as e:
         B.moe_ep_workspace_bytes(5000, 8, 256, 8, 4096)
     assert e.value.status == B.ECAP
@@ -150,6 +154,26 @@ def test_expert_batch_argument_checks():
     assert call(pl=_payloads((FAKE, 16 * 520, FAKE, 64 * 520, 520))) == B.EALIGN
     assert call(ws=None) == B.EWORKSPACE
     assert call(ws_bytes=4) == B.EWORKSPACE
+
+    def plan(W=4, el=2, K=2, cap=16, ent=FAKE, ws_bytes=1 << 20):
+        return lib.moe_ep_expert_batch_plan(FAKE, 1, FAKE, cap * min(K, el), W, el,
+                                            K, cap, ent, FAKE, None, FAKE,
+                                            ws_bytes, None)
+
+    assert plan(el=0) == B.EINVAL
+    assert plan(ent=None) == B.EINVAL
+    assert plan(ws_bytes=4) == B.EWORKSPACE
+
+    def copy(W=4, el=2, K=2, cap=16, pl=None, ws_bytes=1 << 20):
+        if pl is None:
+            pl = _payloads((FAKE, cap * 512, FAKE, W * cap * 512, 512))
+        return lib.moe_ep_expert_batch_copy(FAKE, 1, FAKE, cap * min(K, el), W, el,
+                                            K, cap, ctypes.addressof(pl), 1, FAKE,
+                                            None, FAKE, ws_bytes, None)
+
+    assert copy(W=65) == B.EINVAL
+    assert copy(pl=_payloads((FAKE, 16 * 520, FAKE, 64 * 520, 520))) == B.EALIGN
+    assert copy(ws_bytes=4) == B.EWORKSPACE
 
 
 def test_combine_argument_checks():

@@ -54,6 +54,13 @@ def test_parity_fp32_combine(name):
     run_full_parity(w, salt=5, f32=True)
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode", "multi_small"])
+def test_parity_batch_plan_then_copy(name):
+    """moe_ep_expert_batch_plan + moe_ep_expert_batch_copy == the one call."""
+    say(f"[parity split batch] {name}")
+    run_full_parity(CASES[name], salt=17, split_batch=True)
+
+
 def test_parity_second_seed():
     say("[parity] dsv3_small seed 2")
     run_full_parity(CASES["dsv3_small"], salt=11)
