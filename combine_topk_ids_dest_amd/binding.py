@@ -27,6 +27,7 @@ EXPORTED = (
     "moe_ep_workspace_bytes",
     "moe_ep_status_string",
     "moe_ep_dispatch_pack",
+    "moe_ep_dispatch_pack_fp8",
     "moe_ep_expert_batch",
     "moe_ep_expert_batch_plan",
     "moe_ep_expert_batch_copy",
@@ -72,6 +73,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_ep_dispatch_pack.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
         _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_dispatch_pack_fp8.argtypes = [
+        _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I64, _I64, _I32,
+        _P, _I64, _P, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_ep_expert_batch.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
         _P, _P, _P, _P, _SZ, _P]
@@ -218,6 +222,60 @@ def prepare_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
     return PreparedCall("moe_ep_dispatch_pack", args,
                         (arr, topk_ids, topk_weights, payloads, send_cnt, send_eloc,
                          send_w, token_slot, err_flags, workspace))
+
+
+def scale_pitch(H: int, group: int) -> int:
+    """fp32 scales per row of the quantised layout: H/group rounded up to 4."""
+    return (H // group + 3) // 4 * 4
+
+
+def prepare_dispatch_pack_fp8(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                              E: int, W: int, max_num_tokens: int,
+                              hidden: torch.Tensor, group: int,
+                              send_q: torch.Tensor, send_scale: torch.Tensor,
+                              payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                              send_cnt: torch.Tensor, send_eloc: torch.Tensor,
+                              send_w: torch.Tensor, token_slot: torch.Tensor,
+                              err_flags: Optional[torch.Tensor],
+                              workspace: torch.Tensor) -> PreparedCall:
+    """hidden: bf16 [T, H] (token stride free, rows dense); send_q: fp8 codes
+    [W, cap, H] (uint8 or float8, rank stride free); send_scale: fp32
+    [W, cap, Gp], Gp = H/group rounded up to 4 (rank stride free)."""
+    T, K = topk_ids.shape
+    if hidden.dtype != torch.bfloat16:
+        raise ValueError("hidden must be bfloat16")
+    for t, n in ((topk_ids, "topk_ids"), (topk_weights, "topk_weights"),
+                 (send_eloc, "send_eloc"), (send_w, "send_w"),
+                 (token_slot, "token_slot"), (send_cnt, "send_cnt")):
+        _dense_from(t, 0, n)
+    _dense_from(hidden, 1, "hidden")
+    _dense_from(send_q, 1, "send_q")
+    _dense_from(send_scale, 1, "send_scale")
+    H = hidden.size(1)
+    if send_scale.size(-1) != scale_pitch(H, group):
+        raise ValueError("send_scale rows must hold scale_pitch(H, group) floats")
+    arr = _payload_array(payloads, 1, 2)
+    args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
+            _ptr(hidden), hidden.stride(0) * 2, H, group,
+            _ptr(send_q), send_q.stride(0) * send_q.element_size(),
+            _ptr(send_scale), send_scale.stride(0),
+            ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
+            _ptr(send_w), _ptr(token_slot), _ptr(err_flags), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    return PreparedCall("moe_ep_dispatch_pack_fp8", args,
+                        (arr, topk_ids, topk_weights, hidden, send_q, send_scale,
+                         payloads, send_cnt, send_eloc, send_w, token_slot,
+                         err_flags, workspace))
+
+
+def moe_ep_dispatch_pack_fp8(topk_ids, topk_weights, E, W, max_num_tokens, hidden,
+                             group, send_q, send_scale, payloads, send_cnt,
+                             send_eloc, send_w, token_slot, err_flags, workspace,
+                             stream=None) -> None:
+    prepare_dispatch_pack_fp8(topk_ids, topk_weights, E, W, max_num_tokens, hidden,
+                              group, send_q, send_scale, payloads, send_cnt,
+                              send_eloc, send_w, token_slot, err_flags,
+                              workspace)(stream)
 
 
 def moe_ep_dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens, payloads,

@@ -196,13 +196,16 @@ const char* moe_ep_status_string(int status) {
     }
 }
 
-int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
-                         int64_t T, int32_t K, int32_t E, int32_t W,
-                         int64_t max_num_tokens,
-                         const moe_ep_payload* payloads, int32_t n_payloads,
-                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                         int32_t* token_slot, uint32_t* err_flags,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
+             int32_t K, int32_t E, int32_t W, int64_t max_num_tokens,
+             const moe_ep_payload* payloads, int32_t n_payloads,
+             const QuantArgs* quant, int32_t* send_cnt, int32_t* send_eloc,
+             float* send_w, int32_t* token_slot, uint32_t* err_flags,
+             void* workspace, size_t workspace_bytes, void* stream) {
     if (E <= 0 || W <= 0 || E % W != 0 || T < 0) return MOE_EP_EINVAL;
     Shape sh;
     int rc = check_shape(K, E / W, W, max_num_tokens, &sh);
@@ -214,6 +217,18 @@ int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
     PayloadSet P;
     rc = check_payloads(payloads, n_payloads, 1, sh.cap, T > 0, &P);
     if (rc) return rc;
+    if (quant) {
+        const QuantArgs& Q = *quant;
+        if (Q.group != 32 && Q.group != 64 && Q.group != 128) return MOE_EP_EINVAL;
+        if (Q.H <= 0 || Q.H % Q.group) return MOE_EP_EINVAL;
+        if (T > 0 && (!Q.src || !Q.q || !Q.s)) return MOE_EP_EINVAL;
+        if (Q.src_stride < 2 * Q.H || Q.q_stride < sh.cap * Q.H ||
+            Q.s_stride < sh.cap * Q.s_pitch)
+            return MOE_EP_EINVAL;
+        if (!aligned16(Q.src) || Q.src_stride % 16 || (reinterpret_cast<uintptr_t>(Q.q) & 7) ||
+            Q.q_stride % 8 || (reinterpret_cast<uintptr_t>(Q.s) & 3))
+            return MOE_EP_EALIGN;
+    }
     const PackWs ws = pack_ws(T, W);
     if (ws.bytes > 0 && (!workspace || workspace_bytes < (size_t)ws.bytes))
         return MOE_EP_EWORKSPACE;
@@ -239,8 +254,50 @@ int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
     return hip_status(launch_pack_copy(topk_ids, topk_weights, T, K, E,
                                        sh.e_local, W, sh.slots, sh.cap, rank,
                                        token_slot, fused ? tile_cnt : nullptr,
-                                       tile_off, send_cnt, P, send_eloc,
+                                       tile_off, send_cnt, P, quant, send_eloc,
                                        send_w, err_flags, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
+                         int64_t T, int32_t K, int32_t E, int32_t W,
+                         int64_t max_num_tokens,
+                         const moe_ep_payload* payloads, int32_t n_payloads,
+                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
+                         int32_t* token_slot, uint32_t* err_flags,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
+                    n_payloads, nullptr, send_cnt, send_eloc, send_w, token_slot,
+                    err_flags, workspace, workspace_bytes, stream);
+}
+
+int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
+                             int64_t T, int32_t K, int32_t E, int32_t W,
+                             int64_t max_num_tokens, const void* hidden,
+                             int64_t hidden_stride, int64_t H, int32_t group,
+                             void* send_q, int64_t q_rank_stride,
+                             float* send_scale, int64_t scale_rank_stride,
+                             const moe_ep_payload* payloads, int32_t n_payloads,
+                             int32_t* send_cnt, int32_t* send_eloc, float* send_w,
+                             int32_t* token_slot, uint32_t* err_flags,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    QuantArgs Q;
+    Q.src = static_cast<const uint8_t*>(hidden);
+    Q.src_stride = hidden_stride;
+    Q.q = static_cast<uint8_t*>(send_q);
+    Q.q_stride = q_rank_stride;
+    Q.s = send_scale;
+    Q.s_stride = scale_rank_stride;
+    Q.H = H;
+    Q.group = group;
+    Q.s_pitch = group > 0 ? (H / group + 3) / 4 * 4 : 0;
+    return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
+                    n_payloads, &Q, send_cnt, send_eloc, send_w, token_slot,
+                    err_flags, workspace, workspace_bytes, stream);
 }
 
 int moe_ep_expert_batch_plan(const int32_t* recv_cnt, int64_t cnt_rank_stride,

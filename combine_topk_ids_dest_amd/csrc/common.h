@@ -48,6 +48,22 @@ __device__ __forceinline__ void st_row(uint8_t* p, const u32x4& v) {
     else *reinterpret_cast<u32x4*>(p) = v;
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Quantize-on-pack arguments: bf16 rows in, OCP fp8 e4m3 codes and one fp32
+// scale per `group` columns out, for every destination of the token.
+struct QuantArgs {
+    const uint8_t* src;   // bf16 rows [T, H]
+    int64_t src_stride;   // bytes between tokens
+    uint8_t* q;           // codes [W, cap, H]
+    int64_t q_stride;     // bytes between destination blocks
+    float* s;             // scales [W, cap, s_pitch]
+    int64_t s_stride;     // elements between destination blocks
+    int64_t H;
+    int group;            // 32, 64 or 128 columns
+    int64_t s_pitch;      // H / group rounded up to 4 (16-byte scale rows)
+};
+
 // Payload descriptors passed by value as a kernel argument.
 struct PayloadSet {
     const uint8_t* src[MOE_EP_MAX_PAYLOADS];
@@ -152,13 +168,15 @@ hipError_t launch_column_scan(const int32_t* cnt, int ntiles, int nkeys,
 // tile_cnt != nullptr selects the fused tile offsets (ntiles <=
 // kPackFuseTiles): offsets are summed from tile_cnt and block 0 writes
 // send_cnt; otherwise tile_off holds the offsets from column_scan.
+// quant != nullptr adds quantize-on-pack of a bf16 row (QuantArgs).
 hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             int K, int E, int e_local, int W, int slots,
                             int64_t cap, const int32_t* rank,
                             int32_t* token_slot, const int32_t* tile_cnt,
                             const int32_t* tile_off, int32_t* send_cnt,
-                            const PayloadSet& P, int32_t* send_eloc,
-                            float* send_w, uint32_t* err, hipStream_t stream);
+                            const PayloadSet& P, const QuantArgs* quant,
+                            int32_t* send_eloc, float* send_w, uint32_t* err,
+                            hipStream_t stream);
 
 hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
                               const int32_t* recv_eloc, int64_t eloc_stride,

@@ -31,17 +31,30 @@ from . import binding as B
 class LogicalEP:
     def __init__(self, T: int, H: int, E: int, K: int, W: int, cap: int,
                  row_bytes: Sequence[int], combine_dtype=torch.bfloat16,
-                 device="cuda", fill: Optional[int] = None):
-        """row_bytes: bytes per row of each payload (payload 0 is the hidden
-        row that the combine returns). fill: byte to pre-fill every buffer
-        with (e.g. 0xFF, NaN in bf16/fp32) so unwritten tails stay visible;
-        None leaves buffers uninitialised."""
+                 device="cuda", fill: Optional[int] = None,
+                 quant_group: Optional[int] = None):
+        """row_bytes: bytes per row of each source payload (payload 0 is the
+        bf16 hidden row that the combine returns). fill: byte to pre-fill
+        every buffer with (e.g. 0xFF, NaN in bf16/fp32) so unwritten tails
+        stay visible; None leaves buffers uninitialised. quant_group: if set,
+        the pack quantises payload 0 to fp8 e4m3 with one fp32 scale per
+        quant_group columns (moe_ep_dispatch_pack_fp8), and the codes and
+        the scales travel as the first two payloads instead of it."""
         self.T, self.H, self.E, self.K, self.W, self.cap = T, H, E, K, W, cap
         self.e_local = E // W
         self.cap_, self.slots, self.expert_cap = B.moe_ep_capacities(K, E, W, cap)
         self.dtype = combine_dtype
         self.device = torch.device(device)
+        self.quant_group = quant_group
         self.row_bytes = list(row_bytes)
+        if quant_group is not None:
+            if self.row_bytes[0] != 2 * H:
+                raise ValueError("quantize-on-pack needs payload 0 = bf16 [T, H]")
+            G = B.scale_pitch(H, quant_group)
+            # rows that travel: codes, scales, then the further payloads
+            self.send_row_bytes = [H, 4 * G] + self.row_bytes[1:]
+        else:
+            self.send_row_bytes = list(self.row_bytes)
         W_, el, sl = W, self.e_local, self.slots
 
         def alloc(shape, dtype):
@@ -53,12 +66,12 @@ class LogicalEP:
         self.ids = alloc((W_, T, K), torch.int32)
         self.wts = alloc((W_, T, K), torch.float32)
         self.src = [alloc((W_, T, rb), torch.uint8) for rb in self.row_bytes]
-        self.send = [alloc((W_, W_, cap, rb), torch.uint8) for rb in self.row_bytes]
+        self.send = [alloc((W_, W_, cap, rb), torch.uint8) for rb in self.send_row_bytes]
         self.send_cnt = alloc((W_, W_), torch.int32)
         self.send_eloc = alloc((W_, W_, cap, sl), torch.int32)
         self.send_w = alloc((W_, W_, cap, sl), torch.float32)
         self.token_slot = alloc((W_, T, W_), torch.int32)
-        self.b = [alloc((el, self.expert_cap, rb), torch.uint8) for rb in self.row_bytes]
+        self.b = [alloc((el, self.expert_cap, rb), torch.uint8) for rb in self.send_row_bytes]
         self.expert_num_tokens = alloc((W_, el), torch.int32)
         self.recv_row = alloc((W_, W_, cap, sl), torch.int32)
         self.Y = alloc((el, self.expert_cap, H), combine_dtype)
@@ -90,6 +103,15 @@ class LogicalEP:
         return call
 
     def _prep_pack(self, s: int):
+        if self.quant_group is not None:
+            G = B.scale_pitch(self.H, self.quant_group)
+            return B.prepare_dispatch_pack_fp8(
+                self.ids[s], self.wts[s], self.E, self.W, self.cap,
+                self.src[0][s].view(torch.bfloat16), self.quant_group,
+                self.send[0][s], self.send[1][s].view(torch.float32).view(self.W, self.cap, G),
+                [(self.src[p][s], self.send[p + 1][s]) for p in range(1, len(self.src))],
+                self.send_cnt[s], self.send_eloc[s], self.send_w[s],
+                self.token_slot[s], self.err, self.workspace)
         return B.prepare_dispatch_pack(
             self.ids[s], self.wts[s], self.E, self.W, self.cap,
             [(self.src[p][s], self.send[p][s]) for p in range(len(self.src))],
@@ -100,7 +122,7 @@ class LogicalEP:
         return B.prepare_expert_batch(
             self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
             self.K, self.cap,
-            [(self.send[p][:, r], self.b[p]) for p in range(len(self.src))],
+            [(self.send[p][:, r], self.b[p]) for p in range(len(self.send))],
             self.expert_num_tokens[r], self.recv_row[r], self.err,
             self.workspace)
 
@@ -114,7 +136,7 @@ class LogicalEP:
         return B.prepare_expert_batch_copy(
             self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
             self.K, self.cap,
-            [(self.send[p][:, r], self.b[p]) for p in range(len(self.src))],
+            [(self.send[p][:, r], self.b[p]) for p in range(len(self.send))],
             self.recv_row[r], self.err, self.workspace)
 
     def _prep_reduce(self, r: int):

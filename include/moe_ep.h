@@ -148,6 +148,43 @@ MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_w
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dispatch with quantize-on-pack: moe_ep_dispatch_pack, but the bf16 hidden
+ * row of each token is quantised once, on the send side, to OCP fp8 E4M3
+ * with one fp32 scale per `group` columns, and the codes and scales travel
+ * instead of the bf16 row (about half the bytes). The vLLM all2all page's
+ * FlashInfer one-sided manager sizes its dispatch for quantised hidden rows
+ * plus scale factors; the alltoall_batched page itself supports unquantised
+ * MoE only. For each group of a row: scale = amax / 448 (fp32, rounded to
+ * nearest), 1 when amax = 0; code = e4m3(x / scale), the fp32 quotient
+ * rounded to nearest and the conversion to nearest even.
+ *
+ *   hidden        bf16 [T, H]; hidden_stride = bytes between tokens
+ *                 (16-B aligned, >= 2H).
+ *   group         32, 64 or 128; H % group == 0.
+ *   send_q        e4m3 codes [W, cap, H] (8-B aligned); q_rank_stride =
+ *                 bytes between destination blocks (>= cap * H).
+ *   send_scale    fp32 [W, cap, Gp] with Gp = H / group rounded up to a
+ *                 multiple of 4 (16-byte scale rows, so they batch like any
+ *                 payload); columns from H / group on are written +0.0.
+ *                 scale_rank_stride = elements between destination blocks
+ *                 (>= cap * Gp).
+ *   payloads      further payloads moved as is (may be empty).
+ * Everything else as moe_ep_dispatch_pack. The receive side batches the
+ * codes and the scales as two payloads of moe_ep_expert_batch.
+ */
+MOE_EP_API int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
+                                        int64_t T, int32_t K, int32_t E, int32_t W,
+                                        int64_t max_num_tokens, const void* hidden,
+                                        int64_t hidden_stride, int64_t H, int32_t group,
+                                        void* send_q, int64_t q_rank_stride,
+                                        float* send_scale, int64_t scale_rank_stride,
+                                        const moe_ep_payload* payloads, int32_t n_payloads,
+                                        int32_t* send_cnt, int32_t* send_eloc, float* send_w,
+                                        int32_t* token_slot, uint32_t* err_flags,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
  * Dispatch, receive side of one destination rank (prepare() on the vLLM
  * page after the exchange: a pick (s, slot, j) is valid when
  * slot < recv_cnt[s] and its local id is >= 0; valid picks, taken in

@@ -94,6 +94,10 @@ def _open(path: str):
     lib.oracle_combine_unpack.restype = None
     lib.oracle_round_bf16.argtypes = [ctypes.c_float]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.oracle_quantize_fp8.argtypes = [_P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I64]
+    lib.oracle_quantize_fp8.restype = None
     return lib
 
 
@@ -135,6 +139,42 @@ def capacities(K: int, E: int, W: int, max_num_tokens: int):
 
 def round_bf16(x: float) -> int:
     return int(load().oracle_round_bf16(ctypes.c_float(x)))
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(load().oracle_f32_to_e4m3(ctypes.c_float(x)))
+
+
+def quantize_fp8(hidden_bits: np.ndarray, group: int = 128):
+    """fp8 e4m3 codes uint8 [T, H] and fp32 scales [T, H/group] of bf16 rows
+    (uint16 bit patterns [T, H], dense rows)."""
+    x = np.ascontiguousarray(hidden_bits, dtype=np.uint16)
+    T, H = x.shape
+    G = -(-H // group)
+    q = np.empty((T, H), np.uint8)
+    sc = np.empty((T, G), np.float32)
+    load().oracle_quantize_fp8(_ptr(x), T, H, H, group, _ptr(q), H, _ptr(sc), G)
+    return q, sc
+
+
+def dispatch_pack_fp8(topk_ids: np.ndarray, topk_weights: np.ndarray, E: int,
+                      W: int, max_num_tokens: int, hidden_bits: np.ndarray,
+                      group: int = 128, payloads: Sequence[np.ndarray] = (),
+                      fill: int = 0) -> dict:
+    """Quantize-on-pack: every token row is quantised once (quantize_fp8),
+    then the codes, the scales (rows padded with +0.0 to a multiple of 4
+    floats) and the further payloads are packed like any payload
+    (dispatch_pack). send[0] holds the codes, send[1] the scales as bytes."""
+    q, sc = quantize_fp8(hidden_bits, group)
+    T, G = sc.shape
+    # scale rows padded with +0.0 to a multiple of 4 floats (16-byte rows)
+    Gp = (G + 3) // 4 * 4
+    scp = np.zeros((T, Gp), np.float32)
+    scp[:, :G] = sc
+    pl = [q, scp.view(np.uint8).reshape(T, Gp * 4)] + list(payloads)
+    r = dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens, pl, fill)
+    r.update(q=q, scales=sc)
+    return r
 
 
 def dispatch_pack(topk_ids: np.ndarray, topk_weights: np.ndarray, E: int,

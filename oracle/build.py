@@ -15,7 +15,7 @@ CFLAGS = ["-O2", "-std=c99", "-Wall", "-Wextra", "-ffp-contract=off",
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", SRC]
+    cmd = ["gcc", *CFLAGS, "-o", LIB + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -36,6 +36,7 @@
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fPIC -shared. Floating point
  * is IEEE binary32 on SSE; no contraction, no excess precision.
  */
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -382,3 +383,69 @@ void oracle_combine_unpack(
 
 /* Exposed for the pins on the number format. */
 uint16_t oracle_round_bf16(float f) { return oracle_f32_to_bf16(f); }
+
+/* ------------------------------------------------------------------ */
+/* Quantize-on-pack (the fp8 dispatch that the FlashInfer one-sided    */
+/* manager on the vLLM all2all page sizes its workspace for).           */
+/* ------------------------------------------------------------------ */
+
+/* OCP 8-bit floating point E4M3 ("FN": finite, no infinities): sign bit,
+ * 4 exponent bits with bias 7, 3 fraction bits. Exponent field 0 holds the
+ * subnormals f/8 * 2^-6; S.1111.111 is NaN; the largest finite magnitude is
+ * S.1111.110 = 448. Encoding rounds to nearest, ties to even; a magnitude
+ * that rounds past 448 saturates to 448; NaN stays NaN. */
+uint8_t oracle_f32_to_e4m3(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+    if (f != f)
+        return (uint8_t)(sign | 0x7Fu);
+    const double a = fabs((double)f);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7Eu);
+    if (a < 0x1p-6) {
+        /* subnormal steps of 2^-9; 8 steps is the smallest normal, 0x08 */
+        const double m = rint(a * 512.0);
+        return (uint8_t)(sign | (uint8_t)m);
+    }
+    int e = ilogb(a);                         /* floor(log2 a): -6 .. 8 */
+    double m = rint(ldexp(a, 3 - e));         /* 8 .. 16 */
+    if (m == 16.0) {
+        m = 8.0;
+        e += 1;
+    }
+    if (e > 8 || (e == 8 && m > 14.0))
+        return (uint8_t)(sign | 0x7Eu);
+    return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | ((int)m - 8)));
+}
+
+/* Per-row, per-group fp8 quantisation of bf16 rows. For every group of
+ * `group` consecutive columns: amax = max |x|; scale = amax / 448 (fp32
+ * division, rounded to nearest) or 1 when amax = 0; q = e4m3(x / scale)
+ * with the fp32 quotient rounded to nearest. Row t of x at
+ * x + t*x_row_stride (elements); codes of row t at q + t*q_row_stride
+ * (bytes); scales of row t at scale + t*scale_row_stride (elements). */
+void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
+                         int64_t x_row_stride, int32_t group, uint8_t* q,
+                         int64_t q_row_stride, float* scale,
+                         int64_t scale_row_stride)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t g = 0; g * group < H; ++g) {
+            float amax = 0.0f;
+            for (int64_t h = g * group; h < (g + 1) * group && h < H; ++h) {
+                float v = fabsf(oracle_bf16_to_f32(x[t * x_row_stride + h]));
+                if (v > amax)
+                    amax = v;
+            }
+            const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scale[t * scale_row_stride + g] = s;
+            for (int64_t h = g * group; h < (g + 1) * group && h < H; ++h) {
+                const float v = oracle_bf16_to_f32(x[t * x_row_stride + h]);
+                q[t * q_row_stride + h] = oracle_f32_to_e4m3(v / s);
+            }
+        }
+    }
+}
+

@@ -74,7 +74,8 @@ def expert_out_host(w: wl.Workload, r: int, counts, salt: int, f32: bool):
 
 
 def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
-                    srcs=None, pls=None, corrupt_cnt=None, split_batch=False):
+                    srcs=None, pls=None, corrupt_cnt=None, split_batch=False,
+                    fp8_group=None):
     """Whole path on W logical ranks, every output compared element by
     element with the oracle. Returns (ep, oracle result)."""
     if srcs is None:
@@ -88,8 +89,14 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
         return Ys[r]
 
     # oracle side (host only)
-    packs = [oracle.dispatch_pack(ids_l[s], wts_l[s], w.E, w.W, w.cap, pls[s])
-             for s in range(w.W)]
+    if fp8_group is None:
+        packs = [oracle.dispatch_pack(ids_l[s], wts_l[s], w.E, w.W, w.cap, pls[s])
+                 for s in range(w.W)]
+    else:
+        packs = [oracle.dispatch_pack_fp8(
+            ids_l[s], wts_l[s], w.E, w.W, w.cap,
+            pls[s][0].view(np.uint16).reshape(w.T, w.H), fp8_group, pls[s][1:])
+            for s in range(w.W)]
     send_cnt = np.stack([p["send_cnt"] for p in packs]) if w.W else None
     send_eloc = np.stack([p["send_eloc"] for p in packs])
     send_w = np.stack([p["send_w"] for p in packs])
@@ -97,7 +104,7 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
         s_c, r_c, v_c = corrupt_cnt
         send_cnt = send_cnt.copy()
         send_cnt[s_c, r_c] = v_c
-    n_pl = len(pls[0])
+    n_pl = len(packs[0]["send"])
     batches, rets = [], []
     for r in range(w.W):
         recv_pl = [oracle.stack_ranks([packs[s]["send"][p][r] for s in range(w.W)],
@@ -122,7 +129,7 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
     row_bytes = [p.shape[1] * p.itemsize for p in pls[0]]
     dt = torch.float32 if f32 else torch.bfloat16
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, dt, "cuda",
-                   fill=SENTINEL)
+                   fill=SENTINEL, quant_group=fp8_group)
     for s in range(w.W):
         ep.set_source(s, ids_l[s], wts_l[s], pls[s])
     for s in range(w.W):
@@ -216,20 +223,35 @@ def column_windows(nbytes: int, width: int = 64):
     return np.array(sorted(set(out)), dtype=np.int64)
 
 
-def run_fullsize(w: wl.Workload, seed: int = 0):
+def run_fullsize(w: wl.Workload, seed: int = 0, fp8_group=None):
     """Whole path at full size. Every integer output and every valid payload
     byte is compared; the combine is compared on column windows that the
-    oracle computes exactly (the reduction is independent per column)."""
+    oracle computes exactly (the reduction is independent per column). With
+    fp8_group the pack quantises payload 0; the oracle quantises the same
+    rows and its codes and scales are the expected rows."""
     dev = torch.device("cuda")
     say(f"[fullsize] {w.name}: generating inputs")
     srcs = [wl.routing(w, s, seed) for s in range(w.W)]
     pls = [wl.payloads(w, s, seed, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
     row_bytes = [p.shape[1] for p in pls[0]]
-    n_pl = len(row_bytes)
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
-                   fill=SENTINEL)
+                   fill=SENTINEL, quant_group=fp8_group)
+    n_pl = len(ep.send)
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
+    if fp8_group is None:
+        exp_src = ep.src
+    else:
+        say(f"[fullsize] {w.name}: oracle quantisation")
+        qs, ss = [], []
+        for s in range(w.W):
+            q, sc = oracle.quantize_fp8(pls[s][0].view(np.uint16).reshape(w.T, w.H), fp8_group)
+            Gp = (sc.shape[1] + 3) // 4 * 4
+            scp = np.zeros((w.T, Gp), np.float32)
+            scp[:, :sc.shape[1]] = sc
+            qs.append(torch.from_numpy(q))
+            ss.append(torch.from_numpy(scp.view(np.uint8).reshape(w.T, -1)))
+        exp_src = [torch.stack(qs).to(dev), torch.stack(ss).to(dev)] + ep.src[1:]
     wl.expert_outputs_device(ep.Y, seed=2000 + w.wid)
     # the expert outputs are an input of the combine; the oracle gets a host
     # copy of the column windows it checks
@@ -275,13 +297,13 @@ def run_fullsize(w: wl.Workload, seed: int = 0):
             idx = torch.from_numpy(tok_of[(s, d)]).to(dev)
             c = len(idx)
             for p in range(n_pl):
-                exp = ep.src[p][s].index_select(0, idx)
+                exp = exp_src[p][s].index_select(0, idx)
                 assert torch.equal(ep.send[p][s, d, :c], exp), f"payload {p} {s}->{d}"
                 assert bool((ep.send[p][s, d, c:] == SENTINEL).all()), f"payload {p} tail {s}->{d}"
 
     say(f"[fullsize] {w.name}: batch + reduce on the GPU")
     rets_sub = []
-    src_flat = [x.view(w.W * w.T, -1) for x in ep.src]
+    src_flat = [x.reshape(w.W * w.T, -1) for x in exp_src]
     for r in range(w.W):
         for p in range(n_pl):
             ep.b[p].fill_(SENTINEL)

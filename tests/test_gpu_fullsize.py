@@ -18,3 +18,12 @@ def test_fullsize(wid):
     w = wl.WORKLOADS[wid]
     say(f"[fullsize] start {w.name}")
     run_fullsize(w)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wid", [2, 5])
+def test_fullsize_fp8_pack(wid):
+    """Quantize-on-pack at the DeepSeek-V3 and multi-payload shapes."""
+    w = wl.WORKLOADS[wid]
+    say(f"[fullsize fp8] start {w.name}")
+    run_fullsize(w, fp8_group=128)

@@ -101,3 +101,47 @@ def test_runs_are_bit_identical():
     outs2 = [ep2.out, ep2.ret, ep2.recv_row, ep2.token_slot]
     for a, b in zip(outs1, outs2):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+FP8_CASES = {
+    "tiny": W1,
+    "dsv3_small": W2.scaled(T=300, cap=320, H=1024),
+    "multi_small": W5.scaled(T=300, cap=300, H=1024),
+    "decode": W4,
+    "w64": W1.scaled(W=64, E=128, K=4, T=90, cap=96, H=128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_CASES))
+@pytest.mark.parametrize("group", [128, 32])
+def test_parity_fp8_pack(name, group):
+    """Quantize-on-pack: codes, scales and every other output bit-exact."""
+    w = FP8_CASES[name]
+    say(f"[parity fp8] {name} group {group}")
+    run_full_parity(w, salt=21, fp8_group=group)
+
+
+def test_fp8_conversion_sweep_all_bf16_in_range():
+    """Every bf16 value in [-448, 448] through the quantiser with scale 1
+    (each 128-column group holds a +-448), codes bit-exact with the oracle:
+    checks the hardware conversion's rounding on every input value,
+    including all ties between neighbouring codes."""
+    pos = np.arange(0x0000, 0x43E1, dtype=np.uint32)           # 0 .. 448
+    vals = np.concatenate([pos, pos | 0x8000]).astype(np.uint16)
+    H, group = 1024, 128
+    per_group = group - 1
+    n_groups = -(-len(vals) // per_group)
+    T = -(-n_groups // (H // group))
+    rows = np.zeros((T * (H // group), group), np.uint16)
+    rows[:, 0] = 0x43E0                                          # 448
+    flat = rows[:, 1:].reshape(-1)
+    flat[:len(vals)] = vals
+    rows[:, 1:] = flat.reshape(-1, per_group)
+    rows[1::2, 0] = 0xC3E0                                       # -448 on odd groups
+    hidden = rows.reshape(T, H)
+    w = W1.scaled(W=1, E=2, K=1, T=T, cap=T, H=H, pad_frac=0.0)
+    ids = np.zeros((T, 1), np.int32)
+    wts = np.ones((T, 1), np.float32)
+    say(f"[fp8 sweep] {len(vals)} values in {T} rows")
+    run_full_parity(w, srcs=[(ids, wts)],
+                    pls=[[hidden.view(np.uint8).reshape(T, 2 * H)]], fp8_group=group)

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from oracle import build as obuild
+import test_oracle_fp8 as fp8pins
 import test_oracle_pins as pins
 
 MUTANTS = {
@@ -55,6 +56,24 @@ MUTANTS = {
     "reduce_row_of_first_pick": (
         "                    int32_t row = recv_row[at];",
         "                    int32_t row = recv_row[at - j];"),
+    "quant_scale_wrong_divisor": (
+        "const float s = amax > 0.0f ? amax / 448.0f : 1.0f;",
+        "const float s = amax > 0.0f ? amax / 447.0f : 1.0f;"),
+    "quant_multiplies_by_scale": (
+        "q[t * q_row_stride + h] = oracle_f32_to_e4m3(v / s);",
+        "q[t * q_row_stride + h] = oracle_f32_to_e4m3(v * s);"),
+    "e4m3_subnormal_round_half_up": (
+        "const double m = rint(a * 512.0);",
+        "const double m = floor(a * 512.0 + 0.5);"),
+    "e4m3_normal_round_half_up": (
+        "double m = rint(ldexp(a, 3 - e));",
+        "double m = floor(ldexp(a, 3 - e) + 0.5);"),
+    "e4m3_wrong_bias": (
+        "return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | ((int)m - 8)));",
+        "return (uint8_t)(sign | (uint8_t)(((e + 8) << 3) | ((int)m - 8)));"),
+    "quant_amax_without_abs": (
+        "float v = fabsf(oracle_bf16_to_f32(x[t * x_row_stride + h]));",
+        "float v = oracle_bf16_to_f32(x[t * x_row_stride + h]);"),
     "expert_rows_transposed_stride": (
         "e * y_expert_stride + row * y_row_stride + h",
         "row * y_expert_stride + e * y_row_stride + h"),
@@ -76,6 +95,10 @@ def _pin_battery():
         lambda: pins.test_identity_round_trip_returns_a1(1),
         lambda: pins.test_power_of_two_experts(1),
         lambda: pins.test_invariants_full_size_metadata(1),
+        fp8pins.test_every_finite_code_round_trips,
+        fp8pins.test_midpoints_round_to_even_and_neighbours_to_nearest,
+        fp8pins.test_golden_quantized_row,
+        fp8pins.test_quantize_dequantize_error_bound,
     ]
 
 
@@ -93,13 +116,18 @@ def _child(lib_path, q):
 
 
 def _failing_pins(lib_path):
-    """Number of failing pins; a mutant that crashes its (forked, CPU-only)
-    process counts as caught."""
-    ctx = mp.get_context("fork")
+    """Number of failing pins; a mutant that crashes its (spawned, CPU-only)
+    process counts as caught. Spawned, not forked: the parent may already
+    run torch's CPU thread pool, which a forked child cannot use."""
+    ctx = mp.get_context("spawn")
     q = ctx.Queue()
     p = ctx.Process(target=_child, args=(lib_path, q))
     p.start()
-    p.join(600)
+    p.join(300)
+    if p.is_alive():
+        p.kill()
+        p.join()
+        raise AssertionError(f"pin battery did not finish for {lib_path}")
     if p.exitcode != 0:
         return 1_000
     return q.get(timeout=10)
@@ -110,7 +138,7 @@ def test_unmutated_copy_passes_battery(tmp_path):
     c = tmp_path / "m.c"
     c.write_text(src)
     so = tmp_path / "m.so"
-    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c)], check=True)
+    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c), "-lm"], check=True)
     assert _failing_pins(str(so)) == 0
 
 
@@ -122,5 +150,5 @@ def test_mutant_is_caught(name, tmp_path):
     c = tmp_path / f"{name}.c"
     c.write_text(src.replace(old, new))
     so = tmp_path / f"{name}.so"
-    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c)], check=True)
+    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c), "-lm"], check=True)
     assert _failing_pins(str(so)) > 0, f"no pin caught mutant {name}"
