@@ -87,15 +87,18 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def byte_model(w, row_bytes, slots, send_cnt, ent, routed):
-    """Algorithmic bytes per call kind (lists over ranks)."""
+def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None):
+    """Algorithmic bytes per call kind (lists over ranks). row_bytes: the
+    source rows a pack reads; send_row_bytes: the rows that travel (the
+    same unless the pack quantises)."""
     import numpy as np
-    P = int(sum(row_bytes))
+    P_src = int(sum(row_bytes))
+    P = int(sum(send_row_bytes if send_row_bytes is not None else row_bytes))
     Hb = w.H * 2
     U = send_cnt.sum(axis=1)            # per source
     S = send_cnt.sum(axis=0)            # per destination
     R = ent.sum(axis=1)                 # per destination
-    pack = [8 * w.T * w.K + int(routed[s]) * P + int(U[s]) * P + int(U[s]) * slots * 8
+    pack = [8 * w.T * w.K + int(routed[s]) * P_src + int(U[s]) * P + int(U[s]) * slots * 8
             + 4 * w.W for s in range(w.W)]
     batch_plan = [4 * w.W + int(S[r]) * slots * 4 + 4 * w.e_local for r in range(w.W)]
     batch_copy = [int(S[r]) * P + int(R[r]) * P for r in range(w.W)]
@@ -207,6 +210,9 @@ def main():
     ap.add_argument("--probe", choices=["copy"], default=None)
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays")
+    ap.add_argument("--fp8-group", type=int, default=None,
+                    help="quantize-on-pack: send the bf16 hidden row as fp8 e4m3 "
+                         "with one scale per this many columns")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -236,7 +242,8 @@ def main():
     srcs = [wl.routing(w, s) for s in range(w.W)]
     pls = [wl.payloads(w, s, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
     row_bytes = [p.shape[1] for p in pls[0]]
-    ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev)
+    ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
+                   quant_group=args.fp8_group)
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
     wl.expert_outputs_device(ep.Y, seed=1000 + w.wid)
@@ -301,7 +308,7 @@ def main():
     send_cnt = ep.send_cnt.cpu().numpy().astype(np.int64)
     ent = ep.expert_num_tokens.cpu().numpy().astype(np.int64)
     routed = [int((srcs[s][0] >= 0).any(axis=1).sum()) for s in range(w.W)]
-    bm = byte_model(w, row_bytes, ep.slots, send_cnt, ent, routed)
+    bm = byte_model(w, row_bytes, ep.slots, send_cnt, ent, routed, ep.send_row_bytes)
     step_bytes = sum(sum(bm[k]) for k in KERNEL_OF_CALL)
     gbps = step_bytes / (ms_per_step / 1e3) / 1e9
     tokens = w.W * w.T
@@ -343,7 +350,9 @@ def main():
             "workload": w.name, "T": w.T, "H": w.H, "E": w.E, "K": w.K,
             "W": w.W, "cap": w.cap, "routing": w.routing
             + (f" s={w.zipf_s}" if w.routing == "zipf" else ""),
-            "padding_rows": w.n_pad, "payload_bytes_per_row": int(sum(row_bytes)),
+            "padding_rows": w.n_pad, "payload_bytes_per_row": int(sum(ep.send_row_bytes)),
+            "dispatch_format": (f"fp8_e4m3_g{args.fp8_group}" if args.fp8_group
+                                else "as_given"),
             "combine_accumulation": "fp32",
             "launch": "hip_graph" if args.graph else "eager",
             "parallelism": f"1 GPU, {w.W} logical expert-parallel ranks",

@@ -225,8 +225,8 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
         if (Q.src_stride < 2 * Q.H || Q.q_stride < sh.cap * Q.H ||
             Q.s_stride < sh.cap * Q.s_pitch)
             return MOE_EP_EINVAL;
-        if (!aligned16(Q.src) || Q.src_stride % 16 || (reinterpret_cast<uintptr_t>(Q.q) & 7) ||
-            Q.q_stride % 8 || (reinterpret_cast<uintptr_t>(Q.s) & 3))
+        if (!aligned16(Q.src) || Q.src_stride % 16 || (reinterpret_cast<uintptr_t>(Q.q) & 15) ||
+            Q.q_stride % 16 || (reinterpret_cast<uintptr_t>(Q.s) & 3))
             return MOE_EP_EALIGN;
     }
     const PackWs ws = pack_ws(T, W);

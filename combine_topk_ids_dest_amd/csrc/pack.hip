@@ -34,54 +34,103 @@ __device__ __forceinline__ int32_t sum_tiles(const int32_t* __restrict__ tile_cn
     return s;
 }
 
-// Quantises the vectors [lo, hi) of one bf16 row (8 columns per 16-byte
-// vector) and stores codes and scales to the n destinations in LDS. Scale of
-// a group = its amax / 448 (1 if amax = 0), each code = e4m3(x / scale), the
-// quotient correctly rounded (__fdiv_rn), the conversion the hardware one
-// (round to nearest even). lo and hi are multiples of the group's vectors,
-// so the 16-byte vectors of a group sit in consecutive, aligned lanes and
-// its amax is a butterfly over those lanes.
-__device__ __forceinline__ void quantize_row(const QuantArgs& Q, int64_t t,
-                                             int64_t lo, int64_t hi, int n,
-                                             const int32_t* s_dest,
-                                             const int32_t* s_slot) {
-    const int gv = Q.group >> 3;                 // vectors per group
-    const uint8_t* src = Q.src + t * Q.src_stride;
-    for (int64_t base = lo; base < hi; base += kPackThreads * kPackUnroll) {
+// Maximum over aligned groups of `lanes` lanes (2, 4, 8 or 16 lanes of a
+// DPP row), by lane swaps within the row.
+__device__ __forceinline__ float group_max(float m, int lanes) {
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(
+                     0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));   // quad [1,0,3,2]
+    if (lanes >= 4)
+        m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(
+                         0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));   // quad [2,3,0,1]
+    if (lanes >= 8)
+        m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(
+                         0, __float_as_int(m), 0x141, 0xF, 0xF, false)));  // half mirror
+    if (lanes >= 16)
+        m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(
+                         0, __float_as_int(m), 0x140, 0xF, 0xF, false)));  // row mirror
+    return m;
+}
+
+// Load the first pass of a plain (unquantised) leading row before the
+// destinations are known (1) or after (0).
+#ifndef MOE_EP_PACK_PREFETCH
+#define MOE_EP_PACK_PREFETCH 0
+#endif
+
+#ifndef MOE_EP_QUANT_UNROLL
+#define MOE_EP_QUANT_UNROLL 1
+#endif
+constexpr int kQU = MOE_EP_QUANT_UNROLL;
+
+// One pass of the quantiser over a bf16 row. A lane unit i covers the 16
+// columns 16i .. 16i+15 (two 16-byte loads of bf16, one 16-byte store of
+// codes); the lane's units are i = base + u*kPackThreads + tid, u < kQU,
+// below hi. For a group with amax > 0 the scale is amax / 448 and each code
+// is e4m3(x * r) with r = 448 / amax (correctly rounded divisions, the
+// product rounded to nearest, the hardware conversion to nearest even);
+// scale = r = 1 when amax = 0. base and hi are multiples of the group's
+// units, so a group's units sit in consecutive, aligned lanes and its amax
+// is a reduction within a DPP row. The row's loads are all issued first.
+struct QuantPass {
+    u32x4 codes[kQU];
+    float scale[kQU];
+};
+
+__device__ __forceinline__ void quantize_pass(const uint8_t* __restrict__ src,
+                                              int64_t base, int64_t hi, int gu,
+                                              QuantPass& out) {
+    u32x4 v[kQU][2];
 #pragma unroll
-        for (int u = 0; u < kPackUnroll; ++u) {
-            const int64_t i = base + u * kPackThreads + threadIdx.x;
-            const bool valid = i < hi;
-            float f[8];
-            float m = 0.0f;
-            if (valid) {
-                const u32x4 v = ld_row<MOE_EP_COPY_NT>(src + i * 16);
+    for (int u = 0; u < kQU; ++u) {
+        const int64_t i = base + u * kPackThreads + threadIdx.x;
+        if (i < hi) {
+            v[u][0] = ld_row<MOE_EP_COPY_NT>(src + i * 32);
+            v[u][1] = ld_row<MOE_EP_COPY_NT>(src + i * 32 + 16);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kQU; ++u) {
+        const int64_t i = base + u * kPackThreads + threadIdx.x;
+        float f[16];
+        float m = 0.0f;
+        if (i < hi) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    f[2 * c] = bf16_lo(v[c]);
-                    f[2 * c + 1] = bf16_hi(v[c]);
+                    f[8 * h + 2 * c] = bf16_lo(v[u][h][c]);
+                    f[8 * h + 2 * c + 1] = bf16_hi(v[u][h][c]);
                 }
 #pragma unroll
-                for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(f[c]));
-            }
-            for (int x = 1; x < gv; x <<= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
-            if (!valid) continue;
-            const float scale = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
-            u32x2 codes;
-            int lo16 = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(f[0], scale),
-                                                       __fdiv_rn(f[1], scale), 0, false);
-            codes[0] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-                __fdiv_rn(f[2], scale), __fdiv_rn(f[3], scale), lo16, true);
-            int hi16 = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(f[4], scale),
-                                                       __fdiv_rn(f[5], scale), 0, false);
-            codes[1] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-                __fdiv_rn(f[6], scale), __fdiv_rn(f[7], scale), hi16, true);
-            const bool first = (i % gv) == 0;
-            for (int a = 0; a < n; ++a) {
-                uint8_t* qrow = Q.q + s_dest[a] * Q.q_stride + (int64_t)s_slot[a] * Q.H;
-                *reinterpret_cast<u32x2*>(qrow + i * 8) = codes;
-                if (first)
-                    Q.s[s_dest[a] * Q.s_stride + (int64_t)s_slot[a] * Q.s_pitch + i / gv] = scale;
+            for (int c = 0; c < 16; ++c) m = fmaxf(m, fabsf(f[c]));
+        }
+        m = group_max(m, gu);
+        out.scale[u] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+        const float r = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int lo16 = __builtin_amdgcn_cvt_pk_fp8_f32(
+                __fmul_rn(f[4 * w], r), __fmul_rn(f[4 * w + 1], r), 0, false);
+            out.codes[u][w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                __fmul_rn(f[4 * w + 2], r), __fmul_rn(f[4 * w + 3], r), lo16, true);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_quant_pass(const QuantArgs& Q, int64_t base,
+                                                 int64_t hi, int gu,
+                                                 const QuantPass& qp, int n,
+                                                 const int32_t* s_dest,
+                                                 const int32_t* s_slot) {
+    for (int a = 0; a < n; ++a) {
+        uint8_t* qrow = Q.q + s_dest[a] * Q.q_stride + (int64_t)s_slot[a] * Q.H;
+        float* srow = Q.s + s_dest[a] * Q.s_stride + (int64_t)s_slot[a] * Q.s_pitch;
+#pragma unroll
+        for (int u = 0; u < kQU; ++u) {
+            const int64_t i = base + u * kPackThreads + threadIdx.x;
+            if (i < hi) {
+                st_row<MOE_EP_COPY_NT>(qrow + i * 16, qp.codes[u]);
+                if ((i % gu) == 0) srow[i / gu] = qp.scale[u];
             }
         }
     }
@@ -107,6 +156,41 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     for (int64_t b = blockIdx.x; b < T * nsplit; b += gridDim.x) {
         const int64_t t = b / nsplit;
         const int part = (int)(b - t * nsplit);
+
+        // The first pass over the leading row does not depend on where the
+        // token goes: its loads (and, for the quantised row, its codes) are
+        // issued before the destinations are known, so their latency
+        // overlaps wave 0's slot and metadata work.
+        int64_t q_lo = 0, q_hi = 0, q_mid = 0;
+        int gv = 0;
+        QuantPass qp;
+        int64_t p_lo = 0, p_hi = 0, p_mid = 0;
+        u32x4 pre[kPackUnroll];
+        if (QUANT) {
+            gv = Q.group >> 4;                    // 16-column units per group
+            const int64_t nvq = Q.H >> 4;
+            int64_t per = (nvq + nsplit - 1) / nsplit;
+            per = (per + gv - 1) / gv * gv;
+            q_lo = part * per;
+            q_hi = q_lo + per < nvq ? q_lo + per : nvq;
+            q_mid = q_lo + kPackThreads * kQU < q_hi ? q_lo + kPackThreads * kQU : q_hi;
+            if (q_lo < q_hi)
+                quantize_pass(Q.src + t * Q.src_stride, q_lo, q_mid, gv, qp);
+        } else if (MOE_EP_PACK_PREFETCH && P.n > 0) {
+            const int64_t nvec = P.row_bytes[0] >> 4;
+            const int64_t per = (nvec + nsplit - 1) / nsplit;
+            p_lo = part * per;
+            p_hi = p_lo + per < nvec ? p_lo + per : nvec;
+            p_mid = p_lo + kPackThreads * kPackUnroll < p_hi ? p_lo + kPackThreads * kPackUnroll
+                                                            : p_hi;
+            const uint8_t* src = P.src[0] + t * P.src_stride[0];
+#pragma unroll
+            for (int u = 0; u < kPackUnroll; ++u) {
+                const int64_t i = p_lo + u * kPackThreads + tid;
+                if (i < p_mid) pre[u] = ld_row<MOE_EP_COPY_NT>(src + i * 16);
+            }
+        }
+
         if (tid < 64) {
             const int d = tid;
             int32_t slot = -1;
@@ -150,26 +234,40 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
         const int n = s_n;
 
         if (QUANT) {
-            const int gv = Q.group >> 3;
-            const int64_t nvq = Q.H >> 3;
-            int64_t per = (nvq + nsplit - 1) / nsplit;
-            per = (per + gv - 1) / gv * gv;
-            const int64_t lo = part * per;
-            const int64_t hi = lo + per < nvq ? lo + per : nvq;
-            quantize_row(Q, t, lo, hi, n, s_dest, s_slot);
+            if (q_lo < q_hi) store_quant_pass(Q, q_lo, q_mid, gv, qp, n, s_dest, s_slot);
+            const uint8_t* src = Q.src + t * Q.src_stride;
+            for (int64_t base = q_mid; base < q_hi; base += kPackThreads * kQU) {
+                const int64_t top = base + kPackThreads * kQU < q_hi ? base + kPackThreads * kQU
+                                                                     : q_hi;
+                QuantPass more;
+                quantize_pass(src, base, top, gv, more);
+                store_quant_pass(Q, base, top, gv, more, n, s_dest, s_slot);
+            }
             // the padding of each scale row is +0.0
             const int64_t G = Q.H / Q.group;
             if (part == 0 && tid < n)
                 for (int64_t g = G; g < Q.s_pitch; ++g)
                     Q.s[s_dest[tid] * Q.s_stride + (int64_t)s_slot[tid] * Q.s_pitch + g] = 0.0f;
+        } else if (MOE_EP_PACK_PREFETCH && P.n > 0) {
+            const int64_t rb = P.row_bytes[0];
+            for (int a = 0; a < n; ++a) {
+                uint8_t* dst = P.dst[0] + s_dest[a] * P.dst_stride[0] + (int64_t)s_slot[a] * rb;
+#pragma unroll
+                for (int u = 0; u < kPackUnroll; ++u) {
+                    const int64_t i = p_lo + u * kPackThreads + tid;
+                    if (i < p_mid) st_row<MOE_EP_COPY_NT>(dst + i * 16, pre[u]);
+                }
+            }
         }
 
+        // The rest: further passes of payload 0 and every other payload.
         for (int p = 0; p < P.n; ++p) {
             const int64_t rb = P.row_bytes[p];
             const int64_t nvec = rb >> 4;
             const int64_t per = (nvec + nsplit - 1) / nsplit;
-            const int64_t v_lo = part * per;
+            int64_t v_lo = part * per;
             const int64_t v_hi = v_lo + per < nvec ? v_lo + per : nvec;
+            if (!QUANT && MOE_EP_PACK_PREFETCH && p == 0) v_lo = p_mid;   // first pass done
             const uint8_t* src = P.src[p] + t * P.src_stride[p];
             for (int64_t i0 = v_lo + tid; i0 < v_hi; i0 += kPackThreads * kPackUnroll) {
                 u32x4 v[kPackUnroll];

@@ -154,15 +154,17 @@ MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_w
  * instead of the bf16 row (about half the bytes). The vLLM all2all page's
  * FlashInfer one-sided manager sizes its dispatch for quantised hidden rows
  * plus scale factors; the alltoall_batched page itself supports unquantised
- * MoE only. For each group of a row: scale = amax / 448 (fp32, rounded to
- * nearest), 1 when amax = 0; code = e4m3(x / scale), the fp32 quotient
- * rounded to nearest and the conversion to nearest even.
+ * MoE only. For each group of a row with amax > 0: scale = amax / 448 and
+ * code = e4m3(x * r) with r = 448 / amax (fp32 divisions and product
+ * rounded to nearest, the conversion to nearest even); scale = r = 1 when
+ * amax = 0. Dequantisation is code * scale.
  *
  *   hidden        bf16 [T, H]; hidden_stride = bytes between tokens
  *                 (16-B aligned, >= 2H).
  *   group         32, 64 or 128; H % group == 0.
- *   send_q        e4m3 codes [W, cap, H] (8-B aligned); q_rank_stride =
- *                 bytes between destination blocks (>= cap * H).
+ *   send_q        e4m3 codes [W, cap, H] (16-B aligned); q_rank_stride =
+ *                 bytes between destination blocks (>= cap * H, multiple
+ *                 of 16).
  *   send_scale    fp32 [W, cap, Gp] with Gp = H / group rounded up to a
  *                 multiple of 4 (16-byte scale rows, so they batch like any
  *                 payload); columns from H / group on are written +0.0.

@@ -421,11 +421,12 @@ uint8_t oracle_f32_to_e4m3(float f)
 }
 
 /* Per-row, per-group fp8 quantisation of bf16 rows. For every group of
- * `group` consecutive columns: amax = max |x|; scale = amax / 448 (fp32
- * division, rounded to nearest) or 1 when amax = 0; q = e4m3(x / scale)
- * with the fp32 quotient rounded to nearest. Row t of x at
- * x + t*x_row_stride (elements); codes of row t at q + t*q_row_stride
- * (bytes); scales of row t at scale + t*scale_row_stride (elements). */
+ * `group` consecutive columns: amax = max |x|; the stored scale is
+ * amax / 448 and the codes are q = e4m3(x * r) with r = 448 / amax (both
+ * fp32 divisions and the product rounded to nearest); scale = r = 1 when
+ * amax = 0. Dequantisation is q * scale. Row t of x at x + t*x_row_stride
+ * (elements); codes of row t at q + t*q_row_stride (bytes); scales of row t
+ * at scale + t*scale_row_stride (elements). */
 void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
                          int64_t x_row_stride, int32_t group, uint8_t* q,
                          int64_t q_row_stride, float* scale,
@@ -440,10 +441,11 @@ void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
                     amax = v;
             }
             const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            const float r = amax > 0.0f ? 448.0f / amax : 1.0f;
             scale[t * scale_row_stride + g] = s;
             for (int64_t h = g * group; h < (g + 1) * group && h < H; ++h) {
                 const float v = oracle_bf16_to_f32(x[t * x_row_stride + h]);
-                q[t * q_row_stride + h] = oracle_f32_to_e4m3(v / s);
+                q[t * q_row_stride + h] = oracle_f32_to_e4m3(v * r);
             }
         }
     }

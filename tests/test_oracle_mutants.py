@@ -59,8 +59,11 @@ MUTANTS = {
     "quant_scale_wrong_divisor": (
         "const float s = amax > 0.0f ? amax / 448.0f : 1.0f;",
         "const float s = amax > 0.0f ? amax / 447.0f : 1.0f;"),
+    "quant_codes_wrong_multiplier": (
+        "const float r = amax > 0.0f ? 448.0f / amax : 1.0f;",
+        "const float r = amax > 0.0f ? 447.0f / amax : 1.0f;"),
     "quant_multiplies_by_scale": (
-        "q[t * q_row_stride + h] = oracle_f32_to_e4m3(v / s);",
+        "q[t * q_row_stride + h] = oracle_f32_to_e4m3(v * r);",
         "q[t * q_row_stride + h] = oracle_f32_to_e4m3(v * s);"),
     "e4m3_subnormal_round_half_up": (
         "const double m = rint(a * 512.0);",
