@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     moe_ep_expert_batch,
     moe_ep_expert_batch_copy,
     moe_ep_expert_batch_plan,
+    moe_ep_sanitize_expert_ids,
     moe_ep_workspace_bytes,
     status_string,
 )

@@ -31,6 +31,7 @@ EXPORTED = (
     "moe_ep_expert_batch",
     "moe_ep_expert_batch_plan",
     "moe_ep_expert_batch_copy",
+    "moe_ep_sanitize_expert_ids",
     "moe_ep_combine_reduce",
     "moe_ep_combine_unpack",
 )
@@ -83,6 +84,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _SZ, _P]
     lib.moe_ep_expert_batch_copy.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_sanitize_expert_ids.argtypes = [
+        _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _I32, _P, _I64, _P, _P]
     lib.moe_ep_combine_reduce.argtypes = [
         _P, _I64, _I32, _I64, _P, _I64, _P, _P, _I64, _P,
         _I32, _I32, _I32, _I64, _P, _I64, _P]
@@ -364,6 +367,27 @@ def moe_ep_expert_batch_copy(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
                              stream=None) -> None:
     prepare_expert_batch_copy(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
                               payloads, recv_row, err_flags, workspace)(stream)
+
+
+def prepare_sanitize_expert_ids(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
+                                W: int, e_local: int, K: int, max_num_tokens: int,
+                                invalid_id: int, out: torch.Tensor,
+                                err_flags: Optional[torch.Tensor]) -> PreparedCall:
+    """recv_eloc / out: [W, cap, slots] views (rank stride free); out may be
+    recv_eloc itself."""
+    _dense_from(recv_eloc, 1, "recv_eloc")
+    _dense_from(out, 1, "out")
+    args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
+            W, e_local, K, max_num_tokens, invalid_id, _ptr(out), out.stride(0),
+            _ptr(err_flags))
+    return PreparedCall("moe_ep_sanitize_expert_ids", args,
+                        (recv_cnt, recv_eloc, out, err_flags))
+
+
+def moe_ep_sanitize_expert_ids(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
+                               invalid_id, out, err_flags=None, stream=None) -> None:
+    prepare_sanitize_expert_ids(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
+                                invalid_id, out, err_flags)(stream)
 
 
 def prepare_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,

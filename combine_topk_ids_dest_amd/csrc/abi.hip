@@ -367,6 +367,26 @@ int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_stride,
                        P, recv_row, err_flags, workspace, st);
 }
 
+int moe_ep_sanitize_expert_ids(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                               const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                               int32_t W, int32_t e_local, int32_t K,
+                               int64_t max_num_tokens, int32_t invalid_id,
+                               int32_t* out, int64_t out_rank_stride,
+                               uint32_t* err_flags, void* stream) {
+    Shape sh;
+    int rc = check_shape(K, e_local, W, max_num_tokens, &sh);
+    if (rc) return rc;
+    if (!recv_cnt || !recv_eloc || !out) return MOE_EP_EINVAL;
+    if (cnt_rank_stride < 1 || eloc_rank_stride < sh.cap * sh.slots ||
+        out_rank_stride < sh.cap * sh.slots)
+        return MOE_EP_EINVAL;
+    if (out == recv_eloc && out_rank_stride != eloc_rank_stride) return MOE_EP_EINVAL;
+    return hip_status(launch_sanitize_ids(recv_cnt, cnt_rank_stride, recv_eloc,
+                                          eloc_rank_stride, W, e_local, sh.slots,
+                                          sh.cap, invalid_id, out, out_rank_stride,
+                                          err_flags, static_cast<hipStream_t>(stream)));
+}
+
 int moe_ep_combine_reduce(const void* expert_out, int64_t expert_stride,
                           int32_t dtype, int64_t H,
                           const int32_t* recv_cnt, int64_t cnt_rank_stride,

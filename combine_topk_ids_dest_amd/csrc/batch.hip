@@ -181,6 +181,54 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
     }
 }
 
+// Received expert ids for consumers that read the received slots in place:
+// every entry of the [W, cap, slots] layout is written, with the local id of
+// a valid pick (slot < count, id in [0, e_local)) or invalid_id. May run in
+// place (out == recv_eloc with the same stride): each entry is read and
+// written by one lane.
+__global__ __launch_bounds__(256) void sanitize_ids_kernel(
+    const int32_t* recv_cnt, int64_t cnt_stride, const int32_t* recv_eloc,
+    int64_t eloc_stride, int W, int e_local, int slots, int64_t cap,
+    int32_t invalid_id, int32_t* out, int64_t out_stride,
+    uint32_t* __restrict__ err) {
+    __shared__ int32_t pre[MOE_EP_MAX_WORLD + 1];
+    if (threadIdx.x < 64) load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre, err);
+    __syncthreads();
+    const int32_t per_rank = (int32_t)cap * slots;
+    const int32_t total = W * per_rank;
+    uint32_t bad = 0;
+    for (int32_t idx = blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += gridDim.x * 256) {
+        const int32_t s = idx / per_rank;
+        const int32_t rem = idx - s * per_rank;
+        const int32_t slot = rem / slots;
+        int32_t v = invalid_id;
+        if (slot < pre[s + 1] - pre[s]) {
+            const int32_t e = recv_eloc[s * eloc_stride + rem];
+            if (e >= e_local) bad |= MOE_EP_ERR_ELOC;
+            if (e >= 0 && e < e_local) v = e;
+        }
+        out[s * out_stride + rem] = v;
+    }
+    report(err, bad);
+}
+
+hipError_t launch_sanitize_ids(const int32_t* recv_cnt, int64_t cnt_stride,
+                               const int32_t* recv_eloc, int64_t eloc_stride,
+                               int W, int e_local, int slots, int64_t cap,
+                               int32_t invalid_id, int32_t* out,
+                               int64_t out_stride, uint32_t* err,
+                               hipStream_t stream) {
+    const int64_t total = (int64_t)W * cap * slots;
+    if (total == 0) return hipSuccess;
+    int64_t grid = (total + 255) / 256;
+    if (grid > 4096) grid = 4096;
+    sanitize_ids_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+        recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
+        invalid_id, out, out_stride, err);
+    return hipGetLastError();
+}
+
 hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
                               const int32_t* recv_eloc, int64_t eloc_stride,
                               int W, int e_local, int slots, int64_t cap,

@@ -191,6 +191,13 @@ hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
                              const PayloadSet& P, uint32_t* err,
                              hipStream_t stream);
 
+hipError_t launch_sanitize_ids(const int32_t* recv_cnt, int64_t cnt_stride,
+                               const int32_t* recv_eloc, int64_t eloc_stride,
+                               int W, int e_local, int slots, int64_t cap,
+                               int32_t invalid_id, int32_t* out,
+                               int64_t out_stride, uint32_t* err,
+                               hipStream_t stream);
+
 hipError_t launch_combine_reduce(const void* Y, int64_t y_expert_stride,
                                  int dtype, int64_t H, const int32_t* recv_cnt,
                                  int64_t cnt_stride, const int32_t* recv_eloc,

@@ -246,6 +246,28 @@ MOE_EP_API int moe_ep_expert_batch_copy(const int32_t* recv_cnt, int64_t cnt_ran
                                         void* stream);
 
 /*
+ * Received expert ids for consumers that read the received slots in place
+ * (the [W, cap, row] receive buffers, no expert batching), as the FlashInfer
+ * module's moe_a2a_sanitize_expert_ids marks the ids of received entries
+ * that are not valid tokens with a sentinel. Every entry of the
+ * [W, cap, slots] layout is written: out[s, slot, j] = the local id of pick
+ * j when slot < recv_cnt[s] and the id is in [0, e_local), else invalid_id.
+ *
+ *   recv_cnt, recv_eloc  as for moe_ep_expert_batch.
+ *   out           int32; source s block [cap, slots] at
+ *                 out + s * out_rank_stride (elements, >= cap * slots).
+ *                 May be recv_eloc itself with the same stride (in place);
+ *                 otherwise it must not overlap it.
+ *   err_flags     nullable; bits MOE_EP_ERR_ELOC, MOE_EP_ERR_CNT.
+ */
+MOE_EP_API int moe_ep_sanitize_expert_ids(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                                          const int32_t* recv_eloc, int64_t eloc_rank_stride,
+                                          int32_t W, int32_t e_local, int32_t K,
+                                          int64_t max_num_tokens, int32_t invalid_id,
+                                          int32_t* out, int64_t out_rank_stride,
+                                          uint32_t* err_flags, void* stream);
+
+/*
  * Combine, on the destination rank (finalize() on the vLLM page: weight
  * and reduce a token's experts so the return is token-sized). For every
  * valid received slot (s, slot) and column h:

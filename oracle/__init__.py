@@ -94,6 +94,9 @@ def _open(path: str):
     lib.oracle_combine_unpack.restype = None
     lib.oracle_round_bf16.argtypes = [ctypes.c_float]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_sanitize_expert_ids.argtypes = [
+        _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _I32, _P, _I64]
+    lib.oracle_sanitize_expert_ids.restype = ctypes.c_uint32
     lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
     lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
     lib.oracle_quantize_fp8.argtypes = [_P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I64]
@@ -276,6 +279,25 @@ def expert_batch(recv_cnt: np.ndarray, recv_eloc: np.ndarray, W: int,
         raise ValueError("oracle_expert_batch rejected its arguments")
     return dict(expert_num_tokens=ent, recv_row=recv_row, b=dsts,
                 err=int(err), cap=cap, slots=slots, expert_cap=ecap)
+
+
+def sanitize_expert_ids(recv_cnt: np.ndarray, recv_eloc: np.ndarray, W: int,
+                        e_local: int, K: int, max_num_tokens: int,
+                        invalid_id: int) -> dict:
+    """The received local ids [W, cap, slots] with every entry that is not a
+    valid pick set to invalid_id (all entries written)."""
+    cap, slots, _ = capacities(K, e_local * W, W, max_num_tokens)
+    _inner_contiguous(recv_eloc, "recv_eloc", 3)
+    if recv_eloc.shape != (W, cap, slots):
+        raise ValueError(f"recv_eloc must be {(W, cap, slots)}")
+    out = np.full((W, cap, slots), -7, np.int32)
+    err = load().oracle_sanitize_expert_ids(
+        _ptr(recv_cnt), recv_cnt.strides[0] // 4, _ptr(recv_eloc),
+        recv_eloc.strides[0] // 4, W, e_local, K, max_num_tokens, invalid_id,
+        _ptr(out), cap * slots)
+    if err == 0xFFFFFFFF:
+        raise ValueError("oracle_sanitize_expert_ids rejected its arguments")
+    return dict(ids=out, err=int(err))
 
 
 def _dtype_code(a: np.ndarray) -> int:

@@ -451,3 +451,47 @@ void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
     }
 }
 
+/* ------------------------------------------------------------------ */
+/* Received expert ids for consumers that read the received slots in   */
+/* place (FlashInfer module, moe_a2a_sanitize_expert_ids: the ids of   */
+/* received entries that are not valid tokens are set to a sentinel).  */
+/*                                                                      */
+/* out[s, slot, j] = recv_eloc[s, slot, j] when slot < recv_cnt[s]      */
+/* (clamped to [0, cap]) and the id is in [0, e_local); invalid_id      */
+/* otherwise. Every entry of the [W, cap, slots] layout is written.     */
+/* ------------------------------------------------------------------ */
+uint32_t oracle_sanitize_expert_ids(
+    const int32_t* recv_cnt, int64_t cnt_rank_stride,
+    const int32_t* recv_eloc, int64_t eloc_rank_stride,
+    int32_t W, int32_t e_local, int32_t K, int64_t max_num_tokens,
+    int32_t invalid_id, int32_t* out, int64_t out_rank_stride)
+{
+    int64_t cap, expert_cap;
+    int32_t slots;
+    uint32_t err = 0;
+    if (oracle_capacities(K, e_local * W, W, max_num_tokens, &cap, &slots,
+                          &expert_cap))
+        return 0xFFFFFFFFu;
+    for (int32_t s = 0; s < W; ++s) {
+        int64_t cnt = recv_cnt[s * cnt_rank_stride];
+        if (cnt < 0 || cnt > cap) {
+            err |= ORACLE_ERR_CNT;
+            cnt = cnt < 0 ? 0 : cap;
+        }
+        for (int64_t slot = 0; slot < cap; ++slot) {
+            for (int32_t j = 0; j < slots; ++j) {
+                int32_t v = invalid_id;
+                if (slot < cnt) {
+                    int32_t e = recv_eloc[s * eloc_rank_stride + slot * slots + j];
+                    if (e >= e_local)
+                        err |= ORACLE_ERR_ELOC;
+                    if (e >= 0 && e < e_local)
+                        v = e;
+                }
+                out[s * out_rank_stride + slot * slots + j] = v;
+            }
+        }
+    }
+    return err;
+}
+

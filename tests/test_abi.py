@@ -176,6 +176,27 @@ def test_expert_batch_argument_checks():
     assert copy(ws_bytes=4) == B.EWORKSPACE
 
 
+def test_sanitize_argument_checks():
+    lib = B.load()
+
+    def call(W=4, el=2, K=2, cap=16, es=None, os_=None, cnt=FAKE, eloc=FAKE, out=FAKE):
+        slots = min(K, el)
+        es = cap * slots if es is None else es
+        os_ = cap * slots if os_ is None else os_
+        return lib.moe_ep_sanitize_expert_ids(cnt, 1, eloc, es, W, el, K, cap, -1,
+                                              out, os_, None, None)
+
+    assert call(W=0) == B.EINVAL
+    assert call(el=0) == B.EINVAL
+    assert call(cap=-1) == B.EINVAL
+    assert call(cnt=None) == B.EINVAL
+    assert call(eloc=None) == B.EINVAL
+    assert call(out=None) == B.EINVAL
+    assert call(es=31) == B.EINVAL
+    assert call(os_=31) == B.EINVAL
+    assert call(es=40, os_=32) == B.EINVAL            # in place with another stride
+
+
 def test_combine_argument_checks():
     lib = B.load()
 

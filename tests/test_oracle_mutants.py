@@ -15,6 +15,7 @@ import oracle
 from oracle import build as obuild
 import test_oracle_fp8 as fp8pins
 import test_oracle_pins as pins
+import test_oracle_sanitize as sanpins
 
 MUTANTS = {
     "slots_descending_tokens": (
@@ -80,6 +81,12 @@ MUTANTS = {
     "expert_rows_transposed_stride": (
         "e * y_expert_stride + row * y_row_stride + h",
         "row * y_expert_stride + e * y_row_stride + h"),
+    "sanitize_keeps_negative_ids": (
+        "if (e >= 0 && e < e_local)\n                        v = e;",
+        "if (e < e_local)\n                        v = e;"),
+    "sanitize_keeps_row_past_count": (
+        "                if (slot < cnt) {\n                    int32_t e = recv_eloc",
+        "                if (slot <= cnt) {\n                    int32_t e = recv_eloc"),
 }
 
 
@@ -102,6 +109,8 @@ def _pin_battery():
         fp8pins.test_midpoints_round_to_even_and_neighbours_to_nearest,
         fp8pins.test_golden_quantized_row,
         fp8pins.test_quantize_dequantize_error_bound,
+        sanpins.test_sanitize_hand_example,
+        lambda: sanpins.test_sanitize_matches_brute_force_from_routing(4, 8, 3),
     ]
 
 
