@@ -16,6 +16,11 @@ the run's actual counts):
 
 with P = payload bytes per token row, Hb = combine row bytes, U = slots a
 source sends, S = slots a destination receives, R = expert rows it batches.
+With --fused-local the local slice (source s = destination r, S_own slots
+with R_own expert rows) leaves the reduce and enters the fused unpack:
+
+  reduce_peers (dest r)   (R - R_own)*Hb + (S - S_own)*(slots*8 + Hb)
+  unpack_fused (source s) (U - S_own)*Hb + R_own*Hb + S_own*slots*8 + T*Hb
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -42,6 +47,8 @@ KERNEL_OF_CALL = {
     "batch_copy": "batch_copy_kernel",
     "reduce": "combine_reduce_kernel",
     "unpack": "combine_unpack_kernel",
+    "reduce_peers": "combine_reduce_kernel",
+    "unpack_fused": "combine_unpack_fused_kernel",
 }
 ABI_OF_CALL = {
     "pack": "moe_ep_dispatch_pack",
@@ -49,6 +56,8 @@ ABI_OF_CALL = {
     "batch_copy": "moe_ep_expert_batch_copy",
     "reduce": "moe_ep_combine_reduce",
     "unpack": "moe_ep_combine_unpack",
+    "reduce_peers": "moe_ep_combine_reduce_peers",
+    "unpack_fused": "moe_ep_combine_unpack_fused",
 }
 
 
@@ -87,10 +96,12 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None):
+def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None,
+               r_own=None):
     """Algorithmic bytes per call kind (lists over ranks). row_bytes: the
     source rows a pack reads; send_row_bytes: the rows that travel (the
-    same unless the pack quantises)."""
+    same unless the pack quantises); r_own[s]: expert rows of rank s's
+    local slice (for the fused combine)."""
     import numpy as np
     P_src = int(sum(row_bytes))
     P = int(sum(send_row_bytes if send_row_bytes is not None else row_bytes))
@@ -104,8 +115,16 @@ def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None):
     batch_copy = [int(S[r]) * P + int(R[r]) * P for r in range(w.W)]
     reduce = [int(R[r]) * Hb + int(S[r]) * slots * 8 + int(S[r]) * Hb for r in range(w.W)]
     unpack = [int(U[s]) * Hb + w.T * Hb for s in range(w.W)]
-    return {"pack": pack, "batch_plan": batch_plan, "batch_copy": batch_copy,
-            "reduce": reduce, "unpack": unpack, "U": U, "S": S, "R": R}
+    out = {"pack": pack, "batch_plan": batch_plan, "batch_copy": batch_copy,
+           "reduce": reduce, "unpack": unpack, "U": U, "S": S, "R": R}
+    if r_own is not None:
+        S_own = [int(send_cnt[s, s]) for s in range(w.W)]
+        out["reduce_peers"] = [(int(R[r]) - int(r_own[r])) * Hb
+                               + (int(S[r]) - S_own[r]) * (slots * 8 + Hb)
+                               for r in range(w.W)]
+        out["unpack_fused"] = [(int(U[s]) - S_own[s]) * Hb + int(r_own[s]) * Hb
+                               + S_own[s] * slots * 8 + w.T * Hb for s in range(w.W)]
+    return out
 
 
 def cpu_baseline(w, srcs, pls, shares: int):
@@ -210,6 +229,9 @@ def main():
     ap.add_argument("--probe", choices=["copy"], default=None)
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays")
+    ap.add_argument("--fused-local", action="store_true",
+                    help="combine each rank's local slice with the fused unpack "
+                         "(moe_ep_combine_reduce_peers + moe_ep_combine_unpack_fused)")
     ap.add_argument("--fp8-group", type=int, default=None,
                     help="quantize-on-pack: send the bf16 hidden row as fp8 e4m3 "
                          "with one scale per this many columns")
@@ -251,23 +273,26 @@ def main():
     log(f"[bench] {w.name}: inputs generated and resident in "
         f"{time.perf_counter() - t_gen:.1f} s")
 
+    fused = args.fused_local
     for _ in range(args.warmup):
-        ep.step()
+        ep.step(fused_local=fused)
     torch.cuda.synchronize()
 
     # Timed region: K whole steps, nothing else enqueued between them.
     stream = torch.cuda.current_stream()
-    run_step = ep.step
+    def run_step():
+        ep.step(fused_local=fused)
+
     if args.graph:
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            ep.step()
+            ep.step(fused_local=fused)
         stream.wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph):
-            ep.step()
+            ep.step(fused_local=fused)
         torch.cuda.synchronize()
         graph.replay()
         run_step = graph.replay
@@ -284,8 +309,11 @@ def main():
     # call, on the stream the library launches on (torch's current stream).
     # The events add a few microseconds between calls, so these steps are
     # timed separately from the region above.
-    kinds = (["pack"] * w.W + ["batch_plan", "batch_copy", "reduce"] * w.W
-             + ["unpack"] * w.W)
+    k_red, k_unp = ("reduce_peers", "unpack_fused") if fused else ("reduce", "unpack")
+    kinds = (["pack"] * w.W + ["batch_plan", "batch_copy", k_red] * w.W
+             + [k_unp] * w.W)
+    red_call = ep.reduce_peers if fused else ep.reduce
+    unp_call = ep.unpack_fused if fused else ep.unpack
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in kinds] for _ in range(args.steps)]
     for k in range(args.steps):
@@ -295,12 +323,13 @@ def main():
         for r in range(w.W):
             ev[k][i][0].record(stream); ep.batch_plan(r); ev[k][i][1].record(stream); i += 1
             ev[k][i][0].record(stream); ep.batch_copy(r); ev[k][i][1].record(stream); i += 1
-            ev[k][i][0].record(stream); ep.reduce(r); ev[k][i][1].record(stream); i += 1
+            ev[k][i][0].record(stream); red_call(r); ev[k][i][1].record(stream); i += 1
         for s in range(w.W):
-            ev[k][i][0].record(stream); ep.unpack(s); ev[k][i][1].record(stream); i += 1
+            ev[k][i][0].record(stream); unp_call(s); ev[k][i][1].record(stream); i += 1
     torch.cuda.synchronize()
 
-    per_kind = {k: [] for k in KERNEL_OF_CALL}
+    calls = ["pack", "batch_plan", "batch_copy", k_red, k_unp]
+    per_kind = {k: [] for k in calls}
     for k in range(args.steps):
         for i, kind in enumerate(kinds):
             per_kind[kind].append(ev[k][i][0].elapsed_time(ev[k][i][1]))
@@ -308,8 +337,13 @@ def main():
     send_cnt = ep.send_cnt.cpu().numpy().astype(np.int64)
     ent = ep.expert_num_tokens.cpu().numpy().astype(np.int64)
     routed = [int((srcs[s][0] >= 0).any(axis=1).sum()) for s in range(w.W)]
-    bm = byte_model(w, row_bytes, ep.slots, send_cnt, ent, routed, ep.send_row_bytes)
-    step_bytes = sum(sum(bm[k]) for k in KERNEL_OF_CALL)
+    r_own = None
+    if fused:
+        r_own = [int((ep.recv_row[s, s, :int(send_cnt[s, s])] >= 0).sum().item())
+                 for s in range(w.W)]
+    bm = byte_model(w, row_bytes, ep.slots, send_cnt, ent, routed, ep.send_row_bytes,
+                    r_own)
+    step_bytes = sum(sum(bm[k]) for k in calls)
     gbps = step_bytes / (ms_per_step / 1e3) / 1e9
     tokens = w.W * w.T
     value = tokens / (ms_per_step / 1e3)
@@ -355,6 +389,7 @@ def main():
                                 else "as_given"),
             "combine_accumulation": "fp32",
             "launch": "hip_graph" if args.graph else "eager",
+            "local_slice_combine": "fused" if fused else "reduce_then_unpack",
             "parallelism": f"1 GPU, {w.W} logical expert-parallel ranks",
         },
         "effective_gbps": round(gbps, 1),
@@ -362,7 +397,7 @@ def main():
         "algorithmic_bytes_per_step": int(step_bytes),
         "per_call_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
         "per_call_gbps": {k: round(float(np.sum(bm[k])) / (total_ms[k] / args.steps / 1e3) / 1e9, 1)
-                          for k in KERNEL_OF_CALL},
+                          for k in calls},
         "per_call_note": "per-call times come from a separate pass with HIP events around each call",
         "roofline": roofline,
         "cpu_baseline": None,

@@ -11,7 +11,9 @@ from .binding import (  # noqa: F401
     load,
     moe_ep_capacities,
     moe_ep_combine_reduce,
+    moe_ep_combine_reduce_peers,
     moe_ep_combine_unpack,
+    moe_ep_combine_unpack_fused,
     moe_ep_dispatch_pack,
     moe_ep_dispatch_pack_fp8,
     moe_ep_expert_batch,

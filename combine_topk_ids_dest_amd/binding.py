@@ -34,6 +34,8 @@ EXPORTED = (
     "moe_ep_sanitize_expert_ids",
     "moe_ep_combine_reduce",
     "moe_ep_combine_unpack",
+    "moe_ep_combine_reduce_peers",
+    "moe_ep_combine_unpack_fused",
 )
 
 
@@ -91,6 +93,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         _I32, _I32, _I32, _I64, _P, _I64, _P]
     lib.moe_ep_combine_unpack.argtypes = [
         _P, _I64, _I32, _I64, _P, _I64, _I32, _I64, _P, _P]
+    lib.moe_ep_combine_reduce_peers.argtypes = [
+        _P, _I64, _I32, _I64, _P, _I64, _P, _P, _I64, _P,
+        _I32, _I32, _I32, _I64, _I32, _P, _I64, _P]
+    lib.moe_ep_combine_unpack_fused.argtypes = [
+        _P, _I64, _I32, _I64, _P, _I64, _I32, _I64, _I32, _P, _I64, _P, _P, _P,
+        _I32, _I32, _P, _P]
     for name in EXPORTED:
         if name != "moe_ep_status_string":
             getattr(lib, name).restype = ctypes.c_int
@@ -393,10 +401,12 @@ def moe_ep_sanitize_expert_ids(recv_cnt, recv_eloc, W, e_local, K, max_num_token
 def prepare_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,
                            recv_eloc: torch.Tensor, recv_w: torch.Tensor,
                            recv_row: torch.Tensor, W: int, e_local: int, K: int,
-                           max_num_tokens: int, ret: torch.Tensor) -> PreparedCall:
+                           max_num_tokens: int, ret: torch.Tensor,
+                           self_src: Optional[int] = None) -> PreparedCall:
     """expert_out: [e_local, W*cap, H] (expert stride free, rows dense);
     recv_eloc / recv_w: [W, cap, slots] views with one rank stride;
-    ret: [W, cap, H] view (rank stride free)."""
+    ret: [W, cap, H] view (rank stride free). With self_src, the call is
+    moe_ep_combine_reduce_peers (that source's block is skipped)."""
     dt = _dtype_code(expert_out)
     if ret.dtype != expert_out.dtype:
         raise ValueError("ret and expert_out differ in dtype")
@@ -408,11 +418,15 @@ def prepare_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,
     if recv_eloc.stride(0) != recv_w.stride(0):
         raise ValueError("recv_eloc and recv_w must share a rank stride")
     H = expert_out.size(2)
-    args = (_ptr(expert_out), expert_out.stride(0), dt, H, _ptr(recv_cnt),
+    head = (_ptr(expert_out), expert_out.stride(0), dt, H, _ptr(recv_cnt),
             recv_cnt.stride(0), _ptr(recv_eloc), _ptr(recv_w), recv_eloc.stride(0),
-            _ptr(recv_row), W, e_local, K, max_num_tokens, _ptr(ret), ret.stride(0))
-    return PreparedCall("moe_ep_combine_reduce", args,
-                        (expert_out, recv_cnt, recv_eloc, recv_w, recv_row, ret))
+            _ptr(recv_row), W, e_local, K, max_num_tokens)
+    keep = (expert_out, recv_cnt, recv_eloc, recv_w, recv_row, ret)
+    if self_src is None:
+        return PreparedCall("moe_ep_combine_reduce",
+                            head + (_ptr(ret), ret.stride(0)), keep)
+    return PreparedCall("moe_ep_combine_reduce_peers",
+                        head + (self_src, _ptr(ret), ret.stride(0)), keep)
 
 
 def moe_ep_combine_reduce(expert_out, recv_cnt, recv_eloc, recv_w, recv_row, W,
@@ -440,3 +454,43 @@ def prepare_combine_unpack(back: torch.Tensor, token_slot: torch.Tensor,
 
 def moe_ep_combine_unpack(back, token_slot, max_num_tokens, out, stream=None) -> None:
     prepare_combine_unpack(back, token_slot, max_num_tokens, out)(stream)
+
+
+def moe_ep_combine_reduce_peers(expert_out, recv_cnt, recv_eloc, recv_w, recv_row, W,
+                                e_local, K, max_num_tokens, self_src, ret,
+                                stream=None) -> None:
+    prepare_combine_reduce(expert_out, recv_cnt, recv_eloc, recv_w, recv_row, W,
+                           e_local, K, max_num_tokens, ret, self_src)(stream)
+
+
+def prepare_combine_unpack_fused(back: torch.Tensor, token_slot: torch.Tensor,
+                                 max_num_tokens: int, self_rank: int,
+                                 expert_out: torch.Tensor, self_eloc: torch.Tensor,
+                                 self_w: torch.Tensor, self_row: torch.Tensor,
+                                 e_local: int, K: int, out: torch.Tensor) -> PreparedCall:
+    """back: [W, cap, H] view; token_slot: [T, W]; expert_out: the rank's own
+    [e_local, W*cap, H]; self_eloc / self_w / self_row: [cap, slots] dense
+    blocks of the rank's own source; out: [T, H] dense."""
+    dt = _dtype_code(back)
+    if out.dtype != back.dtype or expert_out.dtype != back.dtype:
+        raise ValueError("out, back and expert_out must share a dtype")
+    _dense_from(back, 1, "back")
+    _dense_from(token_slot, 0, "token_slot")
+    _dense_from(out, 0, "out")
+    _dense_from(expert_out, 1, "expert_out")
+    for t, n in ((self_eloc, "self_eloc"), (self_w, "self_w"), (self_row, "self_row")):
+        _dense_from(t, 0, n)
+    T, W = token_slot.shape
+    H = back.size(2)
+    args = (_ptr(back), back.stride(0), dt, H, _ptr(token_slot), T, W,
+            max_num_tokens, self_rank, _ptr(expert_out), expert_out.stride(0),
+            _ptr(self_eloc), _ptr(self_w), _ptr(self_row), e_local, K, _ptr(out))
+    return PreparedCall("moe_ep_combine_unpack_fused", args,
+                        (back, token_slot, expert_out, self_eloc, self_w, self_row, out))
+
+
+def moe_ep_combine_unpack_fused(back, token_slot, max_num_tokens, self_rank, expert_out,
+                                self_eloc, self_w, self_row, e_local, K, out,
+                                stream=None) -> None:
+    prepare_combine_unpack_fused(back, token_slot, max_num_tokens, self_rank, expert_out,
+                                 self_eloc, self_w, self_row, e_local, K, out)(stream)

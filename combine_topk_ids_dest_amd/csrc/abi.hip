@@ -196,6 +196,35 @@ const char* moe_ep_status_string(int status) {
     }
 }
 
+int moe_ep_combine_unpack_fused(const void* back, int64_t back_rank_stride,
+                                int32_t dtype, int64_t H, const int32_t* token_slot,
+                                int64_t T, int32_t W, int64_t max_num_tokens,
+                                int32_t self_rank, const void* expert_out,
+                                int64_t expert_stride, const int32_t* self_eloc,
+                                const float* self_w, const int32_t* self_row,
+                                int32_t e_local, int32_t K, void* out, void* stream) {
+    Shape sh;
+    int rc = check_shape(K, e_local, W, max_num_tokens, &sh);
+    if (rc) return rc;
+    if (T < 0 || H <= 0 || self_rank < 0 || self_rank >= W) return MOE_EP_EINVAL;
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return MOE_EP_EDTYPE;
+    if (T > max_num_tokens) return MOE_EP_ECAP;
+    if (T * W > kI32Max) return MOE_EP_EINVAL;
+    if (T > 0 && (!back || !token_slot || !out || !expert_out || !self_eloc ||
+                  !self_w || !self_row))
+        return MOE_EP_EINVAL;
+    if (back_rank_stride < max_num_tokens * H || expert_stride < sh.expert_cap * H)
+        return MOE_EP_EINVAL;
+    if ((H * eb) % 16 || (back_rank_stride * eb) % 16 || (expert_stride * eb) % 16 ||
+        !aligned16(back) || !aligned16(out) || !aligned16(expert_out))
+        return MOE_EP_EALIGN;
+    return hip_status(launch_combine_unpack_fused(
+        back, back_rank_stride, dtype, H, token_slot, T, W, sh.cap, self_rank,
+        expert_out, expert_stride, self_eloc, self_w, self_row, e_local, sh.slots,
+        out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 namespace {
@@ -387,14 +416,14 @@ int moe_ep_sanitize_expert_ids(const int32_t* recv_cnt, int64_t cnt_rank_stride,
                                           err_flags, static_cast<hipStream_t>(stream)));
 }
 
-int moe_ep_combine_reduce(const void* expert_out, int64_t expert_stride,
+static int combine_reduce(const void* expert_out, int64_t expert_stride,
                           int32_t dtype, int64_t H,
                           const int32_t* recv_cnt, int64_t cnt_rank_stride,
                           const int32_t* recv_eloc, const float* recv_w,
                           int64_t meta_rank_stride, const int32_t* recv_row,
                           int32_t W, int32_t e_local, int32_t K,
                           int64_t max_num_tokens, void* ret,
-                          int64_t ret_rank_stride, void* stream) {
+                          int64_t ret_rank_stride, int32_t skip_src, void* stream) {
     Shape sh;
     int rc = check_shape(K, e_local, W, max_num_tokens, &sh);
     if (rc) return rc;
@@ -412,7 +441,36 @@ int moe_ep_combine_reduce(const void* expert_out, int64_t expert_stride,
     return hip_status(launch_combine_reduce(
         expert_out, expert_stride, dtype, H, recv_cnt, cnt_rank_stride,
         recv_eloc, recv_w, meta_rank_stride, recv_row, W, e_local, sh.slots,
-        sh.cap, ret, ret_rank_stride, static_cast<hipStream_t>(stream)));
+        sh.cap, ret, ret_rank_stride, skip_src, static_cast<hipStream_t>(stream)));
+}
+
+int moe_ep_combine_reduce(const void* expert_out, int64_t expert_stride,
+                          int32_t dtype, int64_t H,
+                          const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                          const int32_t* recv_eloc, const float* recv_w,
+                          int64_t meta_rank_stride, const int32_t* recv_row,
+                          int32_t W, int32_t e_local, int32_t K,
+                          int64_t max_num_tokens, void* ret,
+                          int64_t ret_rank_stride, void* stream) {
+    return combine_reduce(expert_out, expert_stride, dtype, H, recv_cnt,
+                          cnt_rank_stride, recv_eloc, recv_w, meta_rank_stride,
+                          recv_row, W, e_local, K, max_num_tokens, ret,
+                          ret_rank_stride, -1, stream);
+}
+
+int moe_ep_combine_reduce_peers(const void* expert_out, int64_t expert_stride,
+                                int32_t dtype, int64_t H,
+                                const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                                const int32_t* recv_eloc, const float* recv_w,
+                                int64_t meta_rank_stride, const int32_t* recv_row,
+                                int32_t W, int32_t e_local, int32_t K,
+                                int64_t max_num_tokens, int32_t self_src, void* ret,
+                                int64_t ret_rank_stride, void* stream) {
+    if (W > 0 && (self_src < 0 || self_src >= W)) return MOE_EP_EINVAL;
+    return combine_reduce(expert_out, expert_stride, dtype, H, recv_cnt,
+                          cnt_rank_stride, recv_eloc, recv_w, meta_rank_stride,
+                          recv_row, W, e_local, K, max_num_tokens, ret,
+                          ret_rank_stride, self_src, stream);
 }
 
 int moe_ep_combine_unpack(const void* back, int64_t back_rank_stride,

@@ -112,11 +112,11 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
 __device__ __forceinline__ void load_recv_prefix(const int32_t* recv_cnt,
                                                  int64_t cnt_stride, int W,
                                                  int64_t cap, int32_t* pre,
-                                                 uint32_t* err) {
+                                                 uint32_t* err, int skip = -1) {
     const int lane = threadIdx.x & 63;
     int32_t c = 0;
     uint32_t bad = 0;
-    if (lane < W) {
+    if (lane < W && lane != skip) {
         int64_t v = recv_cnt[(int64_t)lane * cnt_stride];
         if (v < 0 || v > cap) {
             bad = MOE_EP_ERR_CNT;
@@ -204,11 +204,19 @@ hipError_t launch_combine_reduce(const void* Y, int64_t y_expert_stride,
                                  const float* recv_w, int64_t meta_stride,
                                  const int32_t* recv_row, int W, int e_local,
                                  int slots, int64_t cap, void* ret,
-                                 int64_t ret_stride, hipStream_t stream);
+                                 int64_t ret_stride, int skip_src,
+                                 hipStream_t stream);
 
 hipError_t launch_combine_unpack(const void* back, int64_t back_stride,
                                  int dtype, int64_t H,
                                  const int32_t* token_slot, int64_t T, int W,
                                  int64_t cap, void* out, hipStream_t stream);
+
+hipError_t launch_combine_unpack_fused(
+    const void* back, int64_t back_stride, int dtype, int64_t H,
+    const int32_t* token_slot, int64_t T, int W, int64_t cap, int self_rank,
+    const void* Y, int64_t y_expert_stride, const int32_t* self_eloc,
+    const float* self_w, const int32_t* self_row, int e_local, int slots,
+    void* out, hipStream_t stream);
 
 }  // namespace moe_ep

@@ -149,6 +149,19 @@ class LogicalEP:
         return B.prepare_combine_unpack(self.ret[:, s], self.token_slot[s],
                                         self.cap, self.out[s])
 
+    def _prep_reduce_peers(self, r: int):
+        return B.prepare_combine_reduce(
+            self.Y, self.send_cnt[:, r], self.send_eloc[:, r], self.send_w[:, r],
+            self.recv_row[r], self.W, self.e_local, self.K, self.cap,
+            self.ret[r], self_src=r)
+
+    def _prep_unpack_fused(self, s: int, Y=None):
+        # rank s's own source block as rank s receives it: send[s][s]
+        return B.prepare_combine_unpack_fused(
+            self.ret[:, s], self.token_slot[s], self.cap, s,
+            self.Y if Y is None else Y, self.send_eloc[s, s], self.send_w[s, s],
+            self.recv_row[s, s], self.e_local, self.K, self.out[s])
+
     def pack(self, s: int, stream=None):
         self._prepared("pack", s)(stream)
 
@@ -167,14 +180,32 @@ class LogicalEP:
     def unpack(self, s: int, stream=None):
         self._prepared("unpack", s)(stream)
 
-    def step(self, stream=None):
+    def reduce_peers(self, r: int, stream=None):
+        self._prepared("reduce_peers", r)(stream)
+
+    def unpack_fused(self, s: int, stream=None, Y=None):
+        """Y: rank s's expert output (default: the shared Y buffer)."""
+        if Y is None:
+            self._prepared("unpack_fused", s)(stream)
+        else:
+            self._prep_unpack_fused(s, Y)(stream)
+
+    def step(self, stream=None, fused_local=False):
         """One pass of the whole path over all W logical ranks: W packs,
         then batch + reduce per destination (reusing b and Y), then W
-        unpacks."""
+        unpacks. fused_local: each rank's local slice is combined by the
+        fused unpack (the shared Y stands in for every rank's own expert
+        output)."""
         for s in range(self.W):
             self.pack(s, stream)
         for r in range(self.W):
             self.batch(r, stream)
-            self.reduce(r, stream)
+            if fused_local:
+                self.reduce_peers(r, stream)
+            else:
+                self.reduce(r, stream)
         for s in range(self.W):
-            self.unpack(s, stream)
+            if fused_local:
+                self.unpack_fused(s, stream)
+            else:
+                self.unpack(s, stream)

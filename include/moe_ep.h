@@ -310,6 +310,52 @@ MOE_EP_API int moe_ep_combine_unpack(const void* back, int64_t back_rank_stride,
                           int64_t T, int32_t W, int64_t max_num_tokens,
                           void* out, void* stream);
 
+/*
+ * Fused combine of the local slice: the rank's own tokens that it also
+ * serves as a destination. The FlashInfer module lets the expert kernel
+ * write its output straight into the combine's input region to avoid a
+ * staging copy; on one rank the same idea removes the partial of the local
+ * slice altogether. The destination's reduce skips its own source and the
+ * unpack reduces that term from the rank's own expert output. The result is
+ * bit-identical to moe_ep_combine_reduce + moe_ep_combine_unpack: the local
+ * term is summed over its picks and rounded to the data type exactly as the
+ * reduce stores it, then added in its place in the ascending rank order.
+ *
+ * moe_ep_combine_reduce_peers: moe_ep_combine_reduce for every source except
+ * self_src (in [0, W)), whose block of ret is neither read nor written.
+ */
+MOE_EP_API int moe_ep_combine_reduce_peers(const void* expert_out, int64_t expert_stride,
+                          int32_t dtype, int64_t H,
+                          const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                          const int32_t* recv_eloc, const float* recv_w,
+                          int64_t meta_rank_stride, const int32_t* recv_row,
+                          int32_t W, int32_t e_local, int32_t K,
+                          int64_t max_num_tokens, int32_t self_src, void* ret,
+                          int64_t ret_rank_stride, void* stream);
+
+/*
+ * moe_ep_combine_unpack_fused: moe_ep_combine_unpack on rank self_rank
+ * (in [0, W)) where the term of destination self_rank is not read from back
+ * but computed as moe_ep_combine_reduce computes it for received slot
+ * token_slot[t, self_rank] of source self_rank:
+ *
+ *   expert_out, expert_stride   the rank's own expert output, as for
+ *                 moe_ep_combine_reduce.
+ *   self_eloc, self_w   [cap, slots] received metadata of the rank's own
+ *                 source block (the receive view of source self_rank).
+ *   self_row      [cap, slots] the moe_ep_expert_batch context of that block.
+ *   e_local, K    as for moe_ep_expert_batch.
+ * back's block of destination self_rank is not read. Every row of out is
+ * written.
+ */
+MOE_EP_API int moe_ep_combine_unpack_fused(const void* back, int64_t back_rank_stride,
+                          int32_t dtype, int64_t H, const int32_t* token_slot,
+                          int64_t T, int32_t W, int64_t max_num_tokens,
+                          int32_t self_rank, const void* expert_out,
+                          int64_t expert_stride, const int32_t* self_eloc,
+                          const float* self_w, const int32_t* self_row,
+                          int32_t e_local, int32_t K, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -75,7 +75,7 @@ def expert_out_host(w: wl.Workload, r: int, counts, salt: int, f32: bool):
 
 def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
                     srcs=None, pls=None, corrupt_cnt=None, split_batch=False,
-                    fp8_group=None):
+                    fp8_group=None, fused_local=False):
     """Whole path on W logical ranks, every output compared element by
     element with the oracle. Returns (ep, oracle result)."""
     if srcs is None:
@@ -170,7 +170,10 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
         Yd = torch.from_numpy(Ys[r].view(np.int16) if not f32 else Ys[r])
         ep.Y.view(torch.uint8).fill_(SENTINEL)
         ep.Y[:, :Ys[r].shape[1]].copy_(Yd.view(dt) if not f32 else Yd)
-        ep.reduce(r)
+        if fused_local:
+            ep.reduce_peers(r)
+        else:
+            ep.reduce(r)
         torch.cuda.synchronize()
         b = batches[r]
         exp_err |= b["err"]
@@ -193,12 +196,25 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
         gret = gret.view(torch.int16).numpy().view(np.uint16) if not f32 else gret.numpy()
         for s in range(w.W):
             c = int(cnt[s])
+            if fused_local and s == r:
+                assert (gret[s].view(np.uint8) == SENTINEL).all(), "own block of ret written"
+                continue
             assert_combine_close(gret[s, :c], rets[r][s, :c], f"ret {s}->{r}")
             tail = gret[s, c:]
             assert (tail.view(np.uint8) == SENTINEL).all(), "ret tail written"
 
     for s in range(w.W):
-        ep.unpack(s)
+        if fused_local:
+            # rank s's own expert output, as its reduce saw it
+            Yown = torch.empty_like(ep.Y)
+            Yown.view(torch.uint8).fill_(SENTINEL)
+            Yd = torch.from_numpy(Ys[s].view(np.int16) if not f32 else Ys[s])
+            Yown[:, :Ys[s].shape[1]].copy_(Yd.view(dt) if not f32 else Yd)
+            ep.unpack_fused(s, Y=Yown)
+            torch.cuda.synchronize()
+            del Yown
+        else:
+            ep.unpack(s)
     torch.cuda.synchronize()
     gout = ep.out.cpu()
     gout = gout.view(torch.int16).numpy().view(np.uint16) if not f32 else gout.numpy()

@@ -232,6 +232,31 @@ def test_combine_argument_checks():
     assert unpack(out=None) == B.EINVAL
     assert unpack(H=12) == B.EALIGN
 
+    def peers(self_src=0, W=4, y=FAKE):
+        return lib.moe_ep_combine_reduce_peers(y, W * 16 * 256, B.BF16, 256, FAKE, 1,
+                                               FAKE, FAKE, 16 * 2, FAKE, W, 2, 2, 16,
+                                               self_src, FAKE, 16 * 256, None)
+
+    assert peers(self_src=-1) == B.EINVAL
+    assert peers(self_src=4) == B.EINVAL
+    assert peers(y=None) == B.EINVAL
+    assert peers(y=FAKE + 2) == B.EALIGN
+
+    def fused(self_rank=0, T=8, W=4, el=2, H=256, estride=None, row=FAKE, y=FAKE):
+        estride = W * 16 * H if estride is None else estride
+        return lib.moe_ep_combine_unpack_fused(FAKE, 16 * H, B.BF16, H, FAKE, T, W, 16,
+                                               self_rank, y, estride, FAKE, FAKE, row,
+                                               el, 2, FAKE, None)
+
+    assert fused(self_rank=-1) == B.EINVAL
+    assert fused(self_rank=4) == B.EINVAL
+    assert fused(T=17) == B.ECAP
+    assert fused(el=0) == B.EINVAL
+    assert fused(row=None) == B.EINVAL
+    assert fused(estride=4 * 16 * 256 - 8) == B.EINVAL
+    assert fused(y=FAKE + 2) == B.EALIGN
+    assert fused(H=12, estride=4 * 16 * 16) == B.EALIGN
+
 
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):

@@ -5,9 +5,10 @@ the device with the source row the oracle's slot and row maps name; the
 combine is compared element by element on column windows the oracle
 computes exactly."""
 import pytest
+import torch
 
 import workloads as wl
-from parity import run_fullsize, say
+from parity import SENTINEL, run_fullsize, say
 
 pytestmark = pytest.mark.gpu
 
@@ -27,3 +28,28 @@ def test_fullsize_fp8_pack(wid):
     w = wl.WORKLOADS[wid]
     say(f"[fullsize fp8] start {w.name}")
     run_fullsize(w, fp8_group=128)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wid", [2, 3, 4])
+def test_fullsize_fused_local_combine(wid):
+    """The fused combine of each rank's local slice at full size (the shared
+    expert output stands in for every rank's own, as in bench.py): out
+    bit-identical to the unfused path checked above, and the own block of
+    ret neither read (it is overwritten with NaN bytes first) nor written."""
+    w = wl.WORKLOADS[wid]
+    say(f"[fullsize fused] start {w.name}")
+    ep = run_fullsize(w)
+    out_ref = ep.out.clone()
+    ep.out.view(torch.uint8).fill_(SENTINEL)
+    for r in range(w.W):
+        ep.ret[r, r].view(torch.uint8).fill_(SENTINEL)
+    for r in range(w.W):
+        ep.reduce_peers(r)
+    for s in range(w.W):
+        ep.unpack_fused(s)
+    torch.cuda.synchronize()
+    assert torch.equal(ep.out.view(torch.uint8), out_ref.view(torch.uint8))
+    for r in range(w.W):
+        assert bool((ep.ret[r, r].view(torch.uint8) == SENTINEL).all())
+    say(f"[fullsize fused] {w.name}: ok")

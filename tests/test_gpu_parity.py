@@ -145,3 +145,27 @@ def test_fp8_conversion_sweep_all_bf16_in_range():
     say(f"[fp8 sweep] {len(vals)} values in {T} rows")
     run_full_parity(w, srcs=[(ids, wts)],
                     pls=[[hidden.view(np.uint8).reshape(T, 2 * H)]], fp8_group=group)
+
+
+FUSED_CASES = ["tiny", "dsv3_small", "mixtral_small", "decode", "w64", "k1",
+               "all_padding", "empty", "e_local_512"]
+
+
+@pytest.mark.parametrize("name", FUSED_CASES)
+def test_parity_fused_local_combine(name):
+    """moe_ep_combine_reduce_peers + moe_ep_combine_unpack_fused: every
+    output against the oracle's reduce + unpack; the own block of ret is
+    never written."""
+    say(f"[parity fused local] {name}")
+    run_full_parity(CASES[name], salt=23, fused_local=True)
+
+
+@pytest.mark.parametrize("name,f32", [("dsv3_small", False), ("mixtral_small", False),
+                                      ("tiny", True)])
+def test_fused_local_combine_is_bit_identical_to_unfused(name, f32):
+    say(f"[fused == unfused] {name} f32={f32}")
+    ep1, _ = run_full_parity(CASES[name], salt=29, f32=f32)
+    out1 = ep1.out.clone()
+    del ep1
+    ep2, _ = run_full_parity(CASES[name], salt=29, f32=f32, fused_local=True)
+    assert torch.equal(out1.view(torch.uint8), ep2.out.view(torch.uint8))
