@@ -25,7 +25,6 @@ with R_own expert rows) leaves the reduce and enters the fused unpack:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -65,12 +64,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    """sha256 over the HIP sources: a counter summary taken from an older
-    build of the kernels no longer describes them."""
+# The source file of each kernel; with the shared header and the build
+# flags it determines the kernel's code.
+KERNEL_SOURCE = {
+    "pack_copy_kernel": "pack.hip",
+    "batch_copy_kernel": "batch.hip",
+    "combine_reduce_kernel": "combine.hip",
+    "combine_unpack_kernel": "combine.hip",
+    "combine_unpack_fused_kernel": "combine.hip",
+}
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 over the kernel's source file, the shared header and the build
+    script: a counter summary taken from an older build of the kernel no
+    longer describes it."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "combine_topk_ids_dest_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+    pkg = os.path.join(ROOT, "combine_topk_ids_dest_amd")
+    for f in (os.path.join(pkg, "csrc", KERNEL_SOURCE[kernel]),
+              os.path.join(pkg, "csrc", "common.h"), os.path.join(pkg, "build.py")):
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()
@@ -79,7 +91,7 @@ def source_digest() -> str:
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
     profiles/<kernel>.<workload>.pmc.txt, or None when it is absent or was
-    taken on other kernel sources."""
+    taken on other sources of the kernel."""
     path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.pmc.txt")
     if not os.path.exists(path):
         return None
@@ -88,7 +100,7 @@ def read_traffic(kernel: str, workload: str):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != source_digest():
+    if vals.get("source_sha256") != source_digest(kernel):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])

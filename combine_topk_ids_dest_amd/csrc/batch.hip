@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
 #pragma unroll
                 for (int u = 0; u < kBatchUnroll; ++u) {
                     const int64_t i = i0 + u * kBatchThreads;
-                    if (i < nvec) x[u] = ld_row<MOE_EP_COPY_NT>(src + i * 16);
+                    if (i < nvec) x[u] = ld_row<MOE_EP_BATCH_LD_NT>(src + i * 16);
                 }
                 for (int a = 0; a < n; ++a) {
                     uint8_t* dst = P.dst[p] + s_exp[a] * P.dst_stride[p] +
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
 #pragma unroll
                     for (int u = 0; u < kBatchUnroll; ++u) {
                         const int64_t i = i0 + u * kBatchThreads;
-                        if (i < nvec) st_row<MOE_EP_COPY_NT>(dst + i * 16, x[u]);
+                        if (i < nvec) st_row<MOE_EP_BATCH_ST_NT>(dst + i * 16, x[u]);
                     }
                 }
             }

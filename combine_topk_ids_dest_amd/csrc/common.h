@@ -20,20 +20,26 @@ constexpr int kBatchChunks = kBatchTile / 64;   // wave-sized chunks per tile
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Row data is touched once per call. The combine kernels (many scattered
-// reads per written row) load and store it with the nontemporal hint, which
-// measured faster on gfx950; the copy kernels (one read, several writes) use
-// plain loads and stores, which measured faster for them. Knobs for tuning
-// builds; the defaults are the product settings.
-#ifndef MOE_EP_COPY_NT
-#define MOE_EP_COPY_NT 0
+// Row data is touched once per call. The combine kernels and the expert
+// batch copy load and store it with the nontemporal hint, which measured
+// faster on gfx950; the pack (one read, several writes per token) uses plain
+// loads and stores, which measured faster for it. Knobs for tuning builds;
+// the defaults are the product settings.
+#ifndef MOE_EP_PACK_NT
+#define MOE_EP_PACK_NT 0
+#endif
+#ifndef MOE_EP_BATCH_LD_NT
+#define MOE_EP_BATCH_LD_NT 1
+#endif
+#ifndef MOE_EP_BATCH_ST_NT
+#define MOE_EP_BATCH_ST_NT 1
 #endif
 #ifndef MOE_EP_COMBINE_NT
 #define MOE_EP_COMBINE_NT 1
 #endif
 // Grid cap of the kernels that walk received slot rows (grid-stride).
 #ifndef MOE_EP_ROW_GRID
-#define MOE_EP_ROW_GRID 32768
+#define MOE_EP_ROW_GRID 16384
 #endif
 
 template <bool NT>
@@ -147,8 +153,11 @@ __device__ __forceinline__ uint32_t to_bf16_rne(float f) {
 // ---------------------------------------------------------------------
 // Column parts a row is cut into so that `rows` rows still give enough
 // blocks to fill the chip; no part is narrower than one pass of 256 lanes.
+#ifndef MOE_EP_SPLIT_BLOCKS
+#define MOE_EP_SPLIT_BLOCKS 2048
+#endif
 inline int row_split(int64_t rows, int64_t max_vecs) {
-    int64_t s = rows > 0 ? (2048 + rows - 1) / rows : 1;
+    int64_t s = rows > 0 ? (MOE_EP_SPLIT_BLOCKS + rows - 1) / rows : 1;
     const int64_t by_width = max_vecs / 256 > 0 ? max_vecs / 256 : 1;
     if (s > by_width) s = by_width;
     if (s < 1) s = 1;

@@ -84,8 +84,8 @@ __device__ __forceinline__ void quantize_pass(const uint8_t* __restrict__ src,
     for (int u = 0; u < kQU; ++u) {
         const int64_t i = base + u * kPackThreads + threadIdx.x;
         if (i < hi) {
-            v[u][0] = ld_row<MOE_EP_COPY_NT>(src + i * 32);
-            v[u][1] = ld_row<MOE_EP_COPY_NT>(src + i * 32 + 16);
+            v[u][0] = ld_row<MOE_EP_PACK_NT>(src + i * 32);
+            v[u][1] = ld_row<MOE_EP_PACK_NT>(src + i * 32 + 16);
         }
     }
 #pragma unroll
@@ -129,7 +129,7 @@ __device__ __forceinline__ void store_quant_pass(const QuantArgs& Q, int64_t bas
         for (int u = 0; u < kQU; ++u) {
             const int64_t i = base + u * kPackThreads + threadIdx.x;
             if (i < hi) {
-                st_row<MOE_EP_COPY_NT>(qrow + i * 16, qp.codes[u]);
+                st_row<MOE_EP_PACK_NT>(qrow + i * 16, qp.codes[u]);
                 if ((i % gu) == 0) srow[i / gu] = qp.scale[u];
             }
         }
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
             for (int u = 0; u < kPackUnroll; ++u) {
                 const int64_t i = p_lo + u * kPackThreads + tid;
-                if (i < p_mid) pre[u] = ld_row<MOE_EP_COPY_NT>(src + i * 16);
+                if (i < p_mid) pre[u] = ld_row<MOE_EP_PACK_NT>(src + i * 16);
             }
         }
 
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                 for (int u = 0; u < kPackUnroll; ++u) {
                     const int64_t i = p_lo + u * kPackThreads + tid;
-                    if (i < p_mid) st_row<MOE_EP_COPY_NT>(dst + i * 16, pre[u]);
+                    if (i < p_mid) st_row<MOE_EP_PACK_NT>(dst + i * 16, pre[u]);
                 }
             }
         }
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                 for (int u = 0; u < kPackUnroll; ++u) {
                     const int64_t i = i0 + u * kPackThreads;
-                    if (i < v_hi) v[u] = ld_row<MOE_EP_COPY_NT>(src + i * 16);
+                    if (i < v_hi) v[u] = ld_row<MOE_EP_PACK_NT>(src + i * 16);
                 }
                 for (int a = 0; a < n; ++a) {
                     uint8_t* dst = P.dst[p] + s_dest[a] * P.dst_stride[p] +
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                     for (int u = 0; u < kPackUnroll; ++u) {
                         const int64_t i = i0 + u * kPackThreads;
-                        if (i < v_hi) st_row<MOE_EP_COPY_NT>(dst + i * 16, v[u]);
+                        if (i < v_hi) st_row<MOE_EP_PACK_NT>(dst + i * 16, v[u]);
                     }
                 }
             }
