@@ -101,6 +101,12 @@ def _open(path: str):
     lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
     lib.oracle_quantize_fp8.argtypes = [_P, _I64, _I64, _I64, _I32, _P, _I64, _P, _I64]
     lib.oracle_quantize_fp8.restype = None
+    lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_e2m1.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_e2m1.restype = ctypes.c_uint8
+    lib.oracle_quantize_fp4.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _P, _I64]
+    lib.oracle_quantize_fp4.restype = None
     return lib
 
 
@@ -176,6 +182,50 @@ def dispatch_pack_fp8(topk_ids: np.ndarray, topk_weights: np.ndarray, E: int,
     scp[:, :G] = sc
     pl = [q, scp.view(np.uint8).reshape(T, Gp * 4)] + list(payloads)
     r = dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens, pl, fill)
+    r.update(q=q, scales=sc)
+    return r
+
+
+def e4m3_to_f32(code: int) -> float:
+    return float(load().oracle_e4m3_to_f32(ctypes.c_uint8(code)))
+
+
+def f32_to_e2m1(x: float) -> int:
+    return int(load().oracle_f32_to_e2m1(ctypes.c_float(x)))
+
+
+def fp4_scale_pitch(H: int) -> int:
+    """Bytes of a 4-bit row's scale row: H/16, padded to a multiple of 16."""
+    return (H // 16 + 15) // 16 * 16
+
+
+def quantize_fp4(hidden_bits: np.ndarray):
+    """4-bit e2m1 codes uint8 [T, H/2] (two per byte, even column low) and
+    e4m3 scale codes uint8 [T, H/16] of bf16 rows (uint16 [T, H], H a
+    multiple of 16)."""
+    x = np.ascontiguousarray(hidden_bits, dtype=np.uint16)
+    T, H = x.shape
+    if H % 16:
+        raise ValueError("H must be a multiple of 16")
+    q = np.empty((T, H // 2), np.uint8)
+    sc = np.empty((T, H // 16), np.uint8)
+    load().oracle_quantize_fp4(_ptr(x), T, H, H, _ptr(q), H // 2, _ptr(sc), H // 16)
+    return q, sc
+
+
+def dispatch_pack_fp4(topk_ids: np.ndarray, topk_weights: np.ndarray, E: int,
+                      W: int, max_num_tokens: int, hidden_bits: np.ndarray,
+                      payloads: Sequence[np.ndarray] = (), fill: int = 0) -> dict:
+    """4-bit quantize-on-pack: every token row is quantised once
+    (quantize_fp4), then the codes, the scale codes (rows padded with 0x00,
+    +0.0 in e4m3, to a multiple of 16 bytes) and the further payloads are
+    packed like any payload (dispatch_pack)."""
+    q, sc = quantize_fp4(hidden_bits)
+    T, nb = sc.shape
+    scp = np.zeros((T, fp4_scale_pitch(nb * 16)), np.uint8)
+    scp[:, :nb] = sc
+    r = dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens,
+                      [q, scp] + list(payloads), fill)
     r.update(q=q, scales=sc)
     return r
 

@@ -451,6 +451,87 @@ void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
     }
 }
 
+/* OCP E4M3 code -> value (exact in binary32): exponent field 0 holds the
+ * subnormals f/8 * 2^-6, otherwise (1 + f/8) * 2^(e-7); S.1111.111 is NaN. */
+float oracle_e4m3_to_f32(uint8_t c)
+{
+    const int e = (c >> 3) & 0xF;
+    const int f = c & 0x7;
+    double v;
+    if (e == 0xF && f == 0x7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)f, -9);
+    else
+        v = ldexp(8.0 + f, e - 10);
+    return (float)((c & 0x80) ? -v : v);
+}
+
+/* OCP 4-bit floating point E2M1: sign bit, 2 exponent bits with bias 1,
+ * 1 fraction bit; the eight magnitudes of codes 0..7 are 0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6 (no infinities, no NaN). Encoding takes the nearest
+ * magnitude; a tie goes to the code whose last bit is 0 (ties to even);
+ * magnitudes above 6 saturate to 6. A NaN (not produced from finite bf16
+ * rows) encodes as a zero of its sign. Returns the 4-bit code. */
+uint8_t oracle_f32_to_e2m1(float f)
+{
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint8_t sign = (uint8_t)((u >> 28) & 0x8u);
+    if (f != f)
+        return sign;
+    const double a = fabs((double)f);
+    if (a >= 6.0)                  /* saturation (distances to 4 and 6 */
+        return (uint8_t)(sign | 7);  /* would tie in double for huge a) */
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        const double dc = fabs(a - mag[c]);
+        const double db = fabs(a - mag[best]);
+        if (dc < db || (dc == db && (c & 1) == 0))
+            best = c;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* 4-bit quantisation of bf16 rows with 8-bit scales, in blocks of 16
+ * columns (the dispatch that FlashInferNVLinkOneSidedManager on the vLLM
+ * "device_communicators.all2all" documentation page sizes as H/2 code
+ * bytes plus H/16 scale bytes per token). For every block: amax = max |x|;
+ * the stored scale is the E4M3 code of amax / 6 (fp32 division, then
+ * rounded to nearest even, saturating at 448); with s its value, the codes
+ * are q = e2m1(x * r), r = 1 / s (fp32 division) or r = 0 when s = 0.
+ * Dequantisation is value(q) * s. Two codes per byte: the even column in
+ * the low nibble. Row t of x at x + t*x_row_stride (elements); codes of
+ * row t at q + t*q_row_stride (bytes, H/2 of them); scales of row t at
+ * scale + t*scale_row_stride (bytes, H/16 of them). H is a multiple of 16. */
+void oracle_quantize_fp4(const uint16_t* x, int64_t T, int64_t H,
+                         int64_t x_row_stride, uint8_t* q, int64_t q_row_stride,
+                         uint8_t* scale, int64_t scale_row_stride)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t b = 0; b * 16 < H; ++b) {
+            float amax = 0.0f;
+            for (int64_t h = b * 16; h < b * 16 + 16; ++h) {
+                float v = fabsf(oracle_bf16_to_f32(x[t * x_row_stride + h]));
+                if (v > amax)
+                    amax = v;
+            }
+            const uint8_t s8 = oracle_f32_to_e4m3(amax / 6.0f);
+            const float s = oracle_e4m3_to_f32(s8);
+            const float r = s > 0.0f ? 1.0f / s : 0.0f;
+            scale[t * scale_row_stride + b] = s8;
+            for (int64_t h = b * 16; h < b * 16 + 16; h += 2) {
+                const float v0 = oracle_bf16_to_f32(x[t * x_row_stride + h]);
+                const float v1 = oracle_bf16_to_f32(x[t * x_row_stride + h + 1]);
+                const uint8_t c0 = oracle_f32_to_e2m1(v0 * r);
+                const uint8_t c1 = oracle_f32_to_e2m1(v1 * r);
+                q[t * q_row_stride + h / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Received expert ids for consumers that read the received slots in   */
 /* place (FlashInfer module, moe_a2a_sanitize_expert_ids: the ids of   */

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from oracle import build as obuild
+import test_oracle_fp4 as fp4pins
 import test_oracle_fp8 as fp8pins
 import test_oracle_pins as pins
 import test_oracle_sanitize as sanpins
@@ -76,8 +77,11 @@ MUTANTS = {
         "return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | ((int)m - 8)));",
         "return (uint8_t)(sign | (uint8_t)(((e + 8) << 3) | ((int)m - 8)));"),
     "quant_amax_without_abs": (
-        "float v = fabsf(oracle_bf16_to_f32(x[t * x_row_stride + h]));",
-        "float v = oracle_bf16_to_f32(x[t * x_row_stride + h]);"),
+        "(g + 1) * group && h < H; ++h) {\n                float v = fabsf(oracle_bf16_to_f32(x[t * x_row_stride + h]));",
+        "(g + 1) * group && h < H; ++h) {\n                float v = oracle_bf16_to_f32(x[t * x_row_stride + h]);"),
+    "fp4_amax_without_abs": (
+        "h < b * 16 + 16; ++h) {\n                float v = fabsf(oracle_bf16_to_f32(x[t * x_row_stride + h]));",
+        "h < b * 16 + 16; ++h) {\n                float v = oracle_bf16_to_f32(x[t * x_row_stride + h]);"),
     "expert_rows_transposed_stride": (
         "e * y_expert_stride + row * y_row_stride + h",
         "row * y_expert_stride + e * y_row_stride + h"),
@@ -87,6 +91,24 @@ MUTANTS = {
     "sanitize_keeps_row_past_count": (
         "                if (slot < cnt) {\n                    int32_t e = recv_eloc",
         "                if (slot <= cnt) {\n                    int32_t e = recv_eloc"),
+    "e2m1_ties_to_odd": (
+        "(dc == db && (c & 1) == 0)",
+        "(dc == db && (c & 1) == 1)"),
+    "e2m1_saturates_to_4": (
+        "        return (uint8_t)(sign | 7);  /* would tie",
+        "        return (uint8_t)(sign | 6);  /* would tie"),
+    "fp4_nibbles_swapped": (
+        "(uint8_t)(c0 | (c1 << 4))",
+        "(uint8_t)(c1 | (c0 << 4))"),
+    "fp4_scale_divisor": (
+        "oracle_f32_to_e4m3(amax / 6.0f)",
+        "oracle_f32_to_e4m3(amax / 4.0f)"),
+    "fp4_codes_from_unrounded_scale": (
+        "const float r = s > 0.0f ? 1.0f / s : 0.0f;",
+        "const float r = amax > 0.0f ? 6.0f / amax : 0.0f;"),
+    "e4m3_decode_wrong_bias": (
+        "v = ldexp(8.0 + f, e - 10);",
+        "v = ldexp(8.0 + f, e - 9);"),
 }
 
 
@@ -110,6 +132,11 @@ def _pin_battery():
         fp8pins.test_golden_quantized_row,
         fp8pins.test_quantize_dequantize_error_bound,
         sanpins.test_sanitize_hand_example,
+        fp4pins.test_e4m3_decoder_matches_definition_and_torch,
+        fp4pins.test_e2m1_every_code_round_trips,
+        fp4pins.test_e2m1_midpoints_neighbours_and_random_match_exact_rounding,
+        fp4pins.test_golden_fp4_rows,
+        fp4pins.test_fp4_dequantisation_error_bound,
         lambda: sanpins.test_sanitize_matches_brute_force_from_routing(4, 8, 3),
     ]
 
