@@ -244,6 +244,9 @@ def main():
     ap.add_argument("--fused-local", action="store_true",
                     help="combine each rank's local slice with the fused unpack "
                          "(moe_ep_combine_reduce_peers + moe_ep_combine_unpack_fused)")
+    ap.add_argument("--fp4", action="store_true",
+                    help="quantize-on-pack: send the bf16 hidden row as 4-bit e2m1 "
+                         "codes with one e4m3 scale per 16 columns")
     ap.add_argument("--fp8-group", type=int, default=None,
                     help="quantize-on-pack: send the bf16 hidden row as fp8 e4m3 "
                          "with one scale per this many columns")
@@ -276,8 +279,11 @@ def main():
     srcs = [wl.routing(w, s) for s in range(w.W)]
     pls = [wl.payloads(w, s, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
     row_bytes = [p.shape[1] for p in pls[0]]
+    if args.fp4 and args.fp8_group:
+        print("--fp4 and --fp8-group exclude each other", file=sys.stderr)
+        sys.exit(2)
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
-                   quant_group=args.fp8_group)
+                   quant_group=args.fp8_group, quant_fp4=args.fp4)
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
     wl.expert_outputs_device(ep.Y, seed=1000 + w.wid)
@@ -398,7 +404,7 @@ def main():
             + (f" s={w.zipf_s}" if w.routing == "zipf" else ""),
             "padding_rows": w.n_pad, "payload_bytes_per_row": int(sum(ep.send_row_bytes)),
             "dispatch_format": (f"fp8_e4m3_g{args.fp8_group}" if args.fp8_group
-                                else "as_given"),
+                                else "fp4_e2m1_e4m3_g16" if args.fp4 else "as_given"),
             "combine_accumulation": "fp32",
             "launch": "hip_graph" if args.graph else "eager",
             "local_slice_combine": "fused" if fused else "reduce_then_unpack",

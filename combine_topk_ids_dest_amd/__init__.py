@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     moe_ep_combine_unpack,
     moe_ep_combine_unpack_fused,
     moe_ep_dispatch_pack,
+    moe_ep_dispatch_pack_fp4,
     moe_ep_dispatch_pack_fp8,
     moe_ep_expert_batch,
     moe_ep_expert_batch_copy,

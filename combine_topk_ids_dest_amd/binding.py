@@ -32,6 +32,7 @@ EXPORTED = (
     "moe_ep_expert_batch_plan",
     "moe_ep_expert_batch_copy",
     "moe_ep_sanitize_expert_ids",
+    "moe_ep_dispatch_pack_fp4",
     "moe_ep_combine_reduce",
     "moe_ep_combine_unpack",
     "moe_ep_combine_reduce_peers",
@@ -86,6 +87,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _SZ, _P]
     lib.moe_ep_expert_batch_copy.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_dispatch_pack_fp4.argtypes = [
+        _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I64, _I64, _P, _I64, _P, _I64,
+        _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_ep_sanitize_expert_ids.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _I32, _P, _I64, _P, _P]
     lib.moe_ep_combine_reduce.argtypes = [
@@ -287,6 +291,60 @@ def moe_ep_dispatch_pack_fp8(topk_ids, topk_weights, E, W, max_num_tokens, hidde
                               group, send_q, send_scale, payloads, send_cnt,
                               send_eloc, send_w, token_slot, err_flags,
                               workspace)(stream)
+
+
+def fp4_scale_pitch(H: int) -> int:
+    """Bytes of a 4-bit row's scale row: H/16 rounded up to 16."""
+    return (H // 16 + 15) // 16 * 16
+
+
+def prepare_dispatch_pack_fp4(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                              E: int, W: int, max_num_tokens: int,
+                              hidden: torch.Tensor, send_q: torch.Tensor,
+                              send_scale: torch.Tensor,
+                              payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                              send_cnt: torch.Tensor, send_eloc: torch.Tensor,
+                              send_w: torch.Tensor, token_slot: torch.Tensor,
+                              err_flags: Optional[torch.Tensor],
+                              workspace: torch.Tensor) -> PreparedCall:
+    """hidden: bf16 [T, H] (token stride free, rows dense); send_q: codes
+    [W, cap, H/2] bytes; send_scale: e4m3 scale codes [W, cap, Sp] bytes,
+    Sp = fp4_scale_pitch(H) (rank strides free)."""
+    T, K = topk_ids.shape
+    if hidden.dtype != torch.bfloat16:
+        raise ValueError("hidden must be bfloat16")
+    for t, n in ((topk_ids, "topk_ids"), (topk_weights, "topk_weights"),
+                 (send_eloc, "send_eloc"), (send_w, "send_w"),
+                 (token_slot, "token_slot"), (send_cnt, "send_cnt")):
+        _dense_from(t, 0, n)
+    for t, n in ((hidden, "hidden"), (send_q, "send_q"), (send_scale, "send_scale")):
+        _dense_from(t, 1, n)
+    H = hidden.size(1)
+    if send_q.size(-1) * send_q.element_size() != H // 2:
+        raise ValueError("send_q rows must hold H/2 bytes")
+    if send_scale.size(-1) * send_scale.element_size() != fp4_scale_pitch(H):
+        raise ValueError("send_scale rows must hold fp4_scale_pitch(H) bytes")
+    arr = _payload_array(payloads, 1, 2)
+    args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
+            _ptr(hidden), hidden.stride(0) * 2, H,
+            _ptr(send_q), send_q.stride(0) * send_q.element_size(),
+            _ptr(send_scale), send_scale.stride(0) * send_scale.element_size(),
+            ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
+            _ptr(send_w), _ptr(token_slot), _ptr(err_flags), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    return PreparedCall("moe_ep_dispatch_pack_fp4", args,
+                        (arr, topk_ids, topk_weights, hidden, send_q, send_scale,
+                         payloads, send_cnt, send_eloc, send_w, token_slot,
+                         err_flags, workspace))
+
+
+def moe_ep_dispatch_pack_fp4(topk_ids, topk_weights, E, W, max_num_tokens, hidden,
+                             send_q, send_scale, payloads, send_cnt, send_eloc,
+                             send_w, token_slot, err_flags, workspace,
+                             stream=None) -> None:
+    prepare_dispatch_pack_fp4(topk_ids, topk_weights, E, W, max_num_tokens, hidden,
+                              send_q, send_scale, payloads, send_cnt, send_eloc,
+                              send_w, token_slot, err_flags, workspace)(stream)
 
 
 def moe_ep_dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens, payloads,

@@ -246,7 +246,7 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
     PayloadSet P;
     rc = check_payloads(payloads, n_payloads, 1, sh.cap, T > 0, &P);
     if (rc) return rc;
-    if (quant) {
+    if (quant && quant->mode == 1) {
         const QuantArgs& Q = *quant;
         if (Q.group != 32 && Q.group != 64 && Q.group != 128) return MOE_EP_EINVAL;
         if (Q.H <= 0 || Q.H % Q.group) return MOE_EP_EINVAL;
@@ -256,6 +256,17 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
             return MOE_EP_EINVAL;
         if (!aligned16(Q.src) || Q.src_stride % 16 || (reinterpret_cast<uintptr_t>(Q.q) & 15) ||
             Q.q_stride % 16 || (reinterpret_cast<uintptr_t>(Q.s) & 3))
+            return MOE_EP_EALIGN;
+    } else if (quant) {
+        const QuantArgs& Q = *quant;
+        if (Q.H <= 0) return MOE_EP_EINVAL;
+        if (T > 0 && (!Q.src || !Q.q || !Q.s)) return MOE_EP_EINVAL;
+        if (Q.src_stride < 2 * Q.H || Q.q_stride < sh.cap * (Q.H / 2) ||
+            Q.s_stride < sh.cap * Q.s_pitch)
+            return MOE_EP_EINVAL;
+        // code rows of H/2 bytes, like every travelling row, are 16-byte multiples
+        if (Q.H % 32 || !aligned16(Q.src) || Q.src_stride % 16 || !aligned16(Q.q) ||
+            Q.q_stride % 16 || !aligned16(Q.s) || Q.s_stride % 16)
             return MOE_EP_EALIGN;
     }
     const PackWs ws = pack_ws(T, W);
@@ -324,6 +335,34 @@ int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
     Q.H = H;
     Q.group = group;
     Q.s_pitch = group > 0 ? (H / group + 3) / 4 * 4 : 0;
+    Q.mode = 1;
+    return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
+                    n_payloads, &Q, send_cnt, send_eloc, send_w, token_slot,
+                    err_flags, workspace, workspace_bytes, stream);
+}
+
+int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
+                             int64_t T, int32_t K, int32_t E, int32_t W,
+                             int64_t max_num_tokens, const void* hidden,
+                             int64_t hidden_stride, int64_t H, void* send_q,
+                             int64_t q_rank_stride, void* send_scale,
+                             int64_t scale_rank_stride,
+                             const moe_ep_payload* payloads, int32_t n_payloads,
+                             int32_t* send_cnt, int32_t* send_eloc, float* send_w,
+                             int32_t* token_slot, uint32_t* err_flags,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    QuantArgs Q;
+    Q.src = static_cast<const uint8_t*>(hidden);
+    Q.src_stride = hidden_stride;
+    Q.q = static_cast<uint8_t*>(send_q);
+    Q.q_stride = q_rank_stride;
+    Q.s = static_cast<float*>(send_scale);
+    Q.s_stride = scale_rank_stride;
+    Q.H = H;
+    Q.group = 16;
+    Q.s_pitch = (H / 16 + 15) / 16 * 16;
+    Q.mode = 2;
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
                     n_payloads, &Q, send_cnt, send_eloc, send_w, token_slot,
                     err_flags, workspace, workspace_bytes, stream);

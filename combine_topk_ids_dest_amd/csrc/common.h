@@ -58,16 +58,22 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Quantize-on-pack arguments: bf16 rows in, OCP fp8 e4m3 codes and one fp32
 // scale per `group` columns out, for every destination of the token.
+// mode 1, fp8: codes [W, cap, H] bytes, fp32 scales [W, cap, s_pitch]
+// (s_stride, s_pitch in floats). mode 2, fp4: two E2M1 codes per byte
+// [W, cap, H/2], E4M3 scale codes [W, cap, s_pitch] bytes (s_stride,
+// s_pitch in bytes; group 16).
 struct QuantArgs {
     const uint8_t* src;   // bf16 rows [T, H]
     int64_t src_stride;   // bytes between tokens
-    uint8_t* q;           // codes [W, cap, H]
+    uint8_t* q;           // codes
     int64_t q_stride;     // bytes between destination blocks
-    float* s;             // scales [W, cap, s_pitch]
-    int64_t s_stride;     // elements between destination blocks
+    float* s;             // scales (fp4: the bytes of the scale codes)
+    int64_t s_stride;     // between destination blocks (see above)
     int64_t H;
-    int group;            // 32, 64 or 128 columns
-    int64_t s_pitch;      // H / group rounded up to 4 (16-byte scale rows)
+    int group;            // fp8: 32, 64 or 128 columns; fp4: 16
+    int64_t s_pitch;      // fp8: H / group rounded up to 4; fp4: H / 16
+                          // rounded up to 16 (16-byte scale rows)
+    int mode;             // 1 fp8, 2 fp4
 };
 
 // Payload descriptors passed by value as a kernel argument.

@@ -71,10 +71,19 @@ constexpr int kQU = MOE_EP_QUANT_UNROLL;
 // scale = r = 1 when amax = 0. base and hi are multiples of the group's
 // units, so a group's units sit in consecutive, aligned lanes and its amax
 // is a reduction within a DPP row. The row's loads are all issued first.
+// NaN entries never become the amax (a compare-and-select, not fmaxf,
+// whose result for a signaling NaN is NaN), and each code carries the sign
+// bit of its input: the sign of a NaN product is left open by IEEE 754.
 struct QuantPass {
     u32x4 codes[kQU];
     float scale[kQU];
 };
+
+// max(m, |x|) where a NaN x leaves m as it is
+__device__ __forceinline__ float abs_max(float m, float x) {
+    const float a = fabsf(x);
+    return a > m ? a : m;
+}
 
 __device__ __forceinline__ void quantize_pass(const uint8_t* __restrict__ src,
                                               int64_t base, int64_t hi, int gu,
@@ -102,7 +111,7 @@ __device__ __forceinline__ void quantize_pass(const uint8_t* __restrict__ src,
                     f[8 * h + 2 * c + 1] = bf16_hi(v[u][h][c]);
                 }
 #pragma unroll
-            for (int c = 0; c < 16; ++c) m = fmaxf(m, fabsf(f[c]));
+            for (int c = 0; c < 16; ++c) m = abs_max(m, f[c]);
         }
         m = group_max(m, gu);
         out.scale[u] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
@@ -111,8 +120,107 @@ __device__ __forceinline__ void quantize_pass(const uint8_t* __restrict__ src,
         for (int w = 0; w < 4; ++w) {
             const int lo16 = __builtin_amdgcn_cvt_pk_fp8_f32(
                 __fmul_rn(f[4 * w], r), __fmul_rn(f[4 * w + 1], r), 0, false);
-            out.codes[u][w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+            const uint32_t codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
                 __fmul_rn(f[4 * w + 2], r), __fmul_rn(f[4 * w + 3], r), lo16, true);
+            const uint32_t signs = ((__float_as_uint(f[4 * w]) >> 24) & 0x80u) |
+                                   ((__float_as_uint(f[4 * w + 1]) >> 16) & 0x8000u) |
+                                   ((__float_as_uint(f[4 * w + 2]) >> 8) & 0x800000u) |
+                                   (__float_as_uint(f[4 * w + 3]) & 0x80000000u);
+            out.codes[u][w] = (codes & 0x7F7F7F7Fu) | signs;
+        }
+    }
+}
+
+// 4-bit pass: a lane unit i covers columns 16i .. 16i+15, which are one
+// scale block. amax is lane-local (NaN entries skipped, as above); the scale code is the hardware OCP e4m3
+// conversion of amax / 6 (correctly rounded division, then nearest even,
+// saturating at 448); with s its value, r = 1 / s (0 when s = 0) and each
+// code is the E2M1 code of x * r (product rounded to nearest).
+struct Fp4Pass {
+    u32x2 codes[kQU];
+    uint32_t scale[kQU];
+};
+
+// Value of a non-negative OCP e4m3 code below 0x7F (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = c >> 3, f = c & 7u;
+    return e ? __uint_as_float(((e + 120u) << 23) | (f << 20)) : (float)f * 0x1p-9f;
+}
+
+// OCP E2M1 code of y: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 by
+// counting the midpoints below |y| (a midpoint counts when |y| passes it,
+// or reaches it where the upper neighbour's code is even: ties to even),
+// saturating at 6 (a NaN counts none); the sign bit is x's, the input that
+// y was scaled from.
+__device__ __forceinline__ uint32_t e2m1_code(float y, float x) {
+    const float a = fabsf(y);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) +
+                       (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                       (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+__device__ __forceinline__ void quantize_pass_fp4(const uint8_t* __restrict__ src,
+                                                  int64_t base, int64_t hi,
+                                                  Fp4Pass& out) {
+    u32x4 v[kQU][2];
+#pragma unroll
+    for (int u = 0; u < kQU; ++u) {
+        const int64_t i = base + u * kPackThreads + threadIdx.x;
+        if (i < hi) {
+            v[u][0] = ld_row<MOE_EP_PACK_NT>(src + i * 32);
+            v[u][1] = ld_row<MOE_EP_PACK_NT>(src + i * 32 + 16);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kQU; ++u) {
+        const int64_t i = base + u * kPackThreads + threadIdx.x;
+        if (i >= hi) continue;
+        float f[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                f[8 * h + 2 * c] = bf16_lo(v[u][h][c]);
+                f[8 * h + 2 * c + 1] = bf16_hi(v[u][h][c]);
+            }
+        float m = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) m = abs_max(m, f[c]);
+        // amax / 6 at or above 448 saturates to 448 (also for an infinite
+        // amax): the conversion sees at most 448
+        const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                                fminf(__fdiv_rn(m, 6.0f), 448.0f), 0.0f, 0, false) & 0xFFu;
+        const float sv = e4m3_value(s8);
+        const float r = sv > 0.0f ? __fdiv_rn(1.0f, sv) : 0.0f;
+        out.scale[u] = s8;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                word |= e2m1_code(__fmul_rn(f[8 * w + c], r), f[8 * w + c]) << (4 * c);
+            out.codes[u][w] = word;
+        }
+    }
+}
+
+__device__ __forceinline__ void store_quant_pass_fp4(const QuantArgs& Q, int64_t base,
+                                                     int64_t hi, const Fp4Pass& qp,
+                                                     int n, const int32_t* s_dest,
+                                                     const int32_t* s_slot) {
+    uint8_t* sbase = reinterpret_cast<uint8_t*>(Q.s);
+    for (int a = 0; a < n; ++a) {
+        uint8_t* qrow = Q.q + s_dest[a] * Q.q_stride + (int64_t)s_slot[a] * (Q.H >> 1);
+        uint8_t* srow = sbase + s_dest[a] * Q.s_stride + (int64_t)s_slot[a] * Q.s_pitch;
+#pragma unroll
+        for (int u = 0; u < kQU; ++u) {
+            const int64_t i = base + u * kPackThreads + threadIdx.x;
+            if (i < hi) {
+                *reinterpret_cast<u32x2*>(qrow + i * 8) = qp.codes[u];
+                srow[i] = (uint8_t)qp.scale[u];
+            }
         }
     }
 }
@@ -136,7 +244,8 @@ __device__ __forceinline__ void store_quant_pass(const QuantArgs& Q, int64_t bas
     }
 }
 
-template <bool QUANT>
+// QMODE 0: plain rows; 1: payload 0 quantised to fp8; 2: to fp4.
+template <int QMODE>
 __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t T,
     int K, int E, int e_local, int W, int slots, int64_t cap, int nsplit,
@@ -164,18 +273,21 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
         int64_t q_lo = 0, q_hi = 0, q_mid = 0;
         int gv = 0;
         QuantPass qp;
+        Fp4Pass qp4;
         int64_t p_lo = 0, p_hi = 0, p_mid = 0;
         u32x4 pre[kPackUnroll];
-        if (QUANT) {
-            gv = Q.group >> 4;                    // 16-column units per group
+        if (QMODE != 0) {
+            gv = QMODE == 2 ? 1 : Q.group >> 4;   // 16-column units per group
             const int64_t nvq = Q.H >> 4;
             int64_t per = (nvq + nsplit - 1) / nsplit;
             per = (per + gv - 1) / gv * gv;
             q_lo = part * per;
             q_hi = q_lo + per < nvq ? q_lo + per : nvq;
             q_mid = q_lo + kPackThreads * kQU < q_hi ? q_lo + kPackThreads * kQU : q_hi;
-            if (q_lo < q_hi)
-                quantize_pass(Q.src + t * Q.src_stride, q_lo, q_mid, gv, qp);
+            if (q_lo < q_hi) {
+                if (QMODE == 2) quantize_pass_fp4(Q.src + t * Q.src_stride, q_lo, q_mid, qp4);
+                else quantize_pass(Q.src + t * Q.src_stride, q_lo, q_mid, gv, qp);
+            }
         } else if (MOE_EP_PACK_PREFETCH && P.n > 0) {
             const int64_t nvec = P.row_bytes[0] >> 4;
             const int64_t per = (nvec + nsplit - 1) / nsplit;
@@ -233,7 +345,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
         __syncthreads();
         const int n = s_n;
 
-        if (QUANT) {
+        if (QMODE == 1) {
             if (q_lo < q_hi) store_quant_pass(Q, q_lo, q_mid, gv, qp, n, s_dest, s_slot);
             const uint8_t* src = Q.src + t * Q.src_stride;
             for (int64_t base = q_mid; base < q_hi; base += kPackThreads * kQU) {
@@ -248,6 +360,21 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             if (part == 0 && tid < n)
                 for (int64_t g = G; g < Q.s_pitch; ++g)
                     Q.s[s_dest[tid] * Q.s_stride + (int64_t)s_slot[tid] * Q.s_pitch + g] = 0.0f;
+        } else if (QMODE == 2) {
+            if (q_lo < q_hi) store_quant_pass_fp4(Q, q_lo, q_mid, qp4, n, s_dest, s_slot);
+            const uint8_t* src = Q.src + t * Q.src_stride;
+            for (int64_t base = q_mid; base < q_hi; base += kPackThreads * kQU) {
+                const int64_t top = base + kPackThreads * kQU < q_hi ? base + kPackThreads * kQU
+                                                                     : q_hi;
+                Fp4Pass more;
+                quantize_pass_fp4(src, base, top, more);
+                store_quant_pass_fp4(Q, base, top, more, n, s_dest, s_slot);
+            }
+            // the padding of each scale row is 0x00 (e4m3 +0.0)
+            uint8_t* sbase = reinterpret_cast<uint8_t*>(Q.s);
+            if (part == 0 && tid < n)
+                for (int64_t g = Q.H >> 4; g < Q.s_pitch; ++g)
+                    sbase[s_dest[tid] * Q.s_stride + (int64_t)s_slot[tid] * Q.s_pitch + g] = 0;
         } else if (MOE_EP_PACK_PREFETCH && P.n > 0) {
             const int64_t rb = P.row_bytes[0];
             for (int a = 0; a < n; ++a) {
@@ -267,7 +394,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             const int64_t per = (nvec + nsplit - 1) / nsplit;
             int64_t v_lo = part * per;
             const int64_t v_hi = v_lo + per < nvec ? v_lo + per : nvec;
-            if (!QUANT && MOE_EP_PACK_PREFETCH && p == 0) v_lo = p_mid;   // first pass done
+            if (QMODE == 0 && MOE_EP_PACK_PREFETCH && p == 0) v_lo = p_mid;   // first pass done
             const uint8_t* src = P.src[p] + t * P.src_stride[p];
             for (int64_t i0 = v_lo + tid; i0 < v_hi; i0 += kPackThreads * kPackUnroll) {
                 u32x4 v[kPackUnroll];
@@ -306,12 +433,16 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
     const int nsplit = row_split(T, max_vecs);
     const int64_t blocks = T * nsplit;
     const int64_t grid = blocks < 65536 ? blocks : 65536;
-    if (quant)
-        pack_copy_kernel<true><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
+    if (quant && quant->mode == 2)
+        pack_copy_kernel<2><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
+            ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
+            tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, err);
+    else if (quant)
+        pack_copy_kernel<1><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
             tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, err);
     else
-        pack_copy_kernel<false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
+        pack_copy_kernel<0><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
             tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, err);
     return hipGetLastError();

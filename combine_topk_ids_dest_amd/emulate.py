@@ -32,22 +32,31 @@ class LogicalEP:
     def __init__(self, T: int, H: int, E: int, K: int, W: int, cap: int,
                  row_bytes: Sequence[int], combine_dtype=torch.bfloat16,
                  device="cuda", fill: Optional[int] = None,
-                 quant_group: Optional[int] = None):
+                 quant_group: Optional[int] = None, quant_fp4: bool = False):
         """row_bytes: bytes per row of each source payload (payload 0 is the
         bf16 hidden row that the combine returns). fill: byte to pre-fill
         every buffer with (e.g. 0xFF, NaN in bf16/fp32) so unwritten tails
         stay visible; None leaves buffers uninitialised. quant_group: if set,
         the pack quantises payload 0 to fp8 e4m3 with one fp32 scale per
         quant_group columns (moe_ep_dispatch_pack_fp8), and the codes and
-        the scales travel as the first two payloads instead of it."""
+        the scales travel as the first two payloads instead of it.
+        quant_fp4: the same with 4-bit E2M1 codes and E4M3 scales per 16
+        columns (moe_ep_dispatch_pack_fp4)."""
         self.T, self.H, self.E, self.K, self.W, self.cap = T, H, E, K, W, cap
         self.e_local = E // W
         self.cap_, self.slots, self.expert_cap = B.moe_ep_capacities(K, E, W, cap)
         self.dtype = combine_dtype
         self.device = torch.device(device)
         self.quant_group = quant_group
+        self.quant_fp4 = quant_fp4
         self.row_bytes = list(row_bytes)
-        if quant_group is not None:
+        if quant_fp4:
+            if quant_group is not None:
+                raise ValueError("choose one quantised format")
+            if self.row_bytes[0] != 2 * H:
+                raise ValueError("quantize-on-pack needs payload 0 = bf16 [T, H]")
+            self.send_row_bytes = [H // 2, B.fp4_scale_pitch(H)] + self.row_bytes[1:]
+        elif quant_group is not None:
             if self.row_bytes[0] != 2 * H:
                 raise ValueError("quantize-on-pack needs payload 0 = bf16 [T, H]")
             G = B.scale_pitch(H, quant_group)
@@ -103,6 +112,13 @@ class LogicalEP:
         return call
 
     def _prep_pack(self, s: int):
+        if self.quant_fp4:
+            return B.prepare_dispatch_pack_fp4(
+                self.ids[s], self.wts[s], self.E, self.W, self.cap,
+                self.src[0][s].view(torch.bfloat16), self.send[0][s], self.send[1][s],
+                [(self.src[p][s], self.send[p + 1][s]) for p in range(1, len(self.src))],
+                self.send_cnt[s], self.send_eloc[s], self.send_w[s],
+                self.token_slot[s], self.err, self.workspace)
         if self.quant_group is not None:
             G = B.scale_pitch(self.H, self.quant_group)
             return B.prepare_dispatch_pack_fp8(

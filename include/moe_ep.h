@@ -157,7 +157,10 @@ MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_w
  * MoE only. For each group of a row with amax > 0: scale = amax / 448 and
  * code = e4m3(x * r) with r = 448 / amax (fp32 divisions and product
  * rounded to nearest, the conversion to nearest even); scale = r = 1 when
- * amax = 0. Dequantisation is code * scale.
+ * amax = 0. NaN entries do not take part in amax, and every code carries
+ * the sign bit of its input (so a NaN input, or an infinite one when the
+ * group's amax is infinite and r = 0, gives the NaN code with that sign).
+ * Dequantisation is code * scale.
  *
  *   hidden        bf16 [T, H]; hidden_stride = bytes between tokens
  *                 (16-B aligned, >= 2H).
@@ -180,6 +183,46 @@ MOE_EP_API int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* to
                                         int64_t hidden_stride, int64_t H, int32_t group,
                                         void* send_q, int64_t q_rank_stride,
                                         float* send_scale, int64_t scale_rank_stride,
+                                        const moe_ep_payload* payloads, int32_t n_payloads,
+                                        int32_t* send_cnt, int32_t* send_eloc, float* send_w,
+                                        int32_t* token_slot, uint32_t* err_flags,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
+ * Dispatch with 4-bit quantize-on-pack: the FlashInfer one-sided manager on
+ * the vLLM all2all page (FlashInferNVLinkOneSidedManager) sizes its dispatch
+ * row as H/2 bytes of 4-bit hidden values plus H/16 bytes of fp8 scale
+ * factors. Here each bf16 hidden row is quantised once, on the send side,
+ * in blocks of 16 columns: amax = max |x|, the scale is the OCP E4M3 code
+ * of amax / 6 (fp32 division, then nearest even, saturating at 448), and
+ * with s its value each code is the OCP E2M1 code of x * r, r = 1 / s
+ * (r = 0 when s = 0), to nearest with ties to even, saturating at 6. E2M1
+ * magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6. NaN entries do not take part
+ * in amax, and every code carries the sign bit of its input (a NaN input
+ * gives a zero of its sign). Dequantisation is value(code) * s. Two codes
+ * per byte, the even column in the low nibble.
+ *
+ *   hidden        bf16 [T, H]; hidden_stride = bytes between tokens
+ *                 (16-B aligned, >= 2H). H % 32 == 0 (EALIGN otherwise:
+ *                 the code row of H/2 bytes is a multiple of 16).
+ *   send_q        codes [W, cap, H/2] bytes (16-B aligned); q_rank_stride =
+ *                 bytes between destination blocks (>= cap * H/2, multiple
+ *                 of 16).
+ *   send_scale    E4M3 scale codes [W, cap, Sp] bytes with Sp = H/16 rounded
+ *                 up to a multiple of 16; bytes from H/16 on are written
+ *                 0x00 (+0.0). scale_rank_stride = bytes between destination
+ *                 blocks (>= cap * Sp, multiple of 16; 16-B aligned).
+ *   payloads      further payloads moved as is (may be empty).
+ * Everything else as moe_ep_dispatch_pack. The receive side batches the
+ * codes and the scales as two payloads of moe_ep_expert_batch.
+ */
+MOE_EP_API int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
+                                        int64_t T, int32_t K, int32_t E, int32_t W,
+                                        int64_t max_num_tokens, const void* hidden,
+                                        int64_t hidden_stride, int64_t H,
+                                        void* send_q, int64_t q_rank_stride,
+                                        void* send_scale, int64_t scale_rank_stride,
                                         const moe_ep_payload* payloads, int32_t n_payloads,
                                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
                                         int32_t* token_slot, uint32_t* err_flags,

@@ -421,10 +421,13 @@ uint8_t oracle_f32_to_e4m3(float f)
 }
 
 /* Per-row, per-group fp8 quantisation of bf16 rows. For every group of
- * `group` consecutive columns: amax = max |x|; the stored scale is
- * amax / 448 and the codes are q = e4m3(x * r) with r = 448 / amax (both
- * fp32 divisions and the product rounded to nearest); scale = r = 1 when
- * amax = 0. Dequantisation is q * scale. Row t of x at x + t*x_row_stride
+ * `group` consecutive columns: amax = max |x| over the non-NaN entries;
+ * the stored scale is amax / 448 and the codes are q = e4m3(x * r) with
+ * r = 448 / amax (both fp32 divisions and the product rounded to nearest);
+ * scale = r = 1 when amax = 0. Each code carries the sign bit of its input
+ * x (IEEE 754 leaves the sign of a NaN product open: a NaN input, or an
+ * infinite one times r = 0, gives the NaN code with x's sign).
+ * Dequantisation is q * scale. Row t of x at x + t*x_row_stride
  * (elements); codes of row t at q + t*q_row_stride (bytes); scales of row t
  * at scale + t*scale_row_stride (elements). */
 void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
@@ -445,7 +448,8 @@ void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
             scale[t * scale_row_stride + g] = s;
             for (int64_t h = g * group; h < (g + 1) * group && h < H; ++h) {
                 const float v = oracle_bf16_to_f32(x[t * x_row_stride + h]);
-                q[t * q_row_stride + h] = oracle_f32_to_e4m3(v * r);
+                const uint8_t c = oracle_f32_to_e4m3(v * r);
+                q[t * q_row_stride + h] = (uint8_t)((c & 0x7Fu) | (signbit(v) ? 0x80u : 0u));
             }
         }
     }
@@ -501,6 +505,8 @@ uint8_t oracle_f32_to_e2m1(float f)
  * the stored scale is the E4M3 code of amax / 6 (fp32 division, then
  * rounded to nearest even, saturating at 448); with s its value, the codes
  * are q = e2m1(x * r), r = 1 / s (fp32 division) or r = 0 when s = 0.
+ * NaN entries do not take part in amax, and each code carries the sign
+ * bit of its input x (a NaN input gives a zero of its sign).
  * Dequantisation is value(q) * s. Two codes per byte: the even column in
  * the low nibble. Row t of x at x + t*x_row_stride (elements); codes of
  * row t at q + t*q_row_stride (bytes, H/2 of them); scales of row t at
@@ -524,8 +530,10 @@ void oracle_quantize_fp4(const uint16_t* x, int64_t T, int64_t H,
             for (int64_t h = b * 16; h < b * 16 + 16; h += 2) {
                 const float v0 = oracle_bf16_to_f32(x[t * x_row_stride + h]);
                 const float v1 = oracle_bf16_to_f32(x[t * x_row_stride + h + 1]);
-                const uint8_t c0 = oracle_f32_to_e2m1(v0 * r);
-                const uint8_t c1 = oracle_f32_to_e2m1(v1 * r);
+                const uint8_t c0 = (uint8_t)((oracle_f32_to_e2m1(v0 * r) & 7u) |
+                                             (signbit(v0) ? 8u : 0u));
+                const uint8_t c1 = (uint8_t)((oracle_f32_to_e2m1(v1 * r) & 7u) |
+                                             (signbit(v1) ? 8u : 0u));
                 q[t * q_row_stride + h / 2] = (uint8_t)(c0 | (c1 << 4));
             }
         }

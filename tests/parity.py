@@ -73,9 +73,20 @@ def expert_out_host(w: wl.Workload, r: int, counts, salt: int, f32: bool):
     return Y
 
 
+def assert_bytes_equal(got: np.ndarray, exp: np.ndarray, what: str):
+    """Byte arrays equal; on a mismatch the message names the first few
+    differing positions with both values."""
+    if np.array_equal(got, exp):
+        return
+    bad = np.argwhere(got != exp)
+    shown = ", ".join(f"{tuple(int(i) for i in ix)}: got {int(got[tuple(ix)]):#x} "
+                      f"want {int(exp[tuple(ix)]):#x}" for ix in bad[:6])
+    raise AssertionError(f"{what}: {len(bad)} bytes differ; first {shown}")
+
+
 def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
                     srcs=None, pls=None, corrupt_cnt=None, split_batch=False,
-                    fp8_group=None, fused_local=False):
+                    fp8_group=None, fused_local=False, fp4=False):
     """Whole path on W logical ranks, every output compared element by
     element with the oracle. Returns (ep, oracle result)."""
     if srcs is None:
@@ -89,7 +100,12 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
         return Ys[r]
 
     # oracle side (host only)
-    if fp8_group is None:
+    if fp4:
+        packs = [oracle.dispatch_pack_fp4(
+            ids_l[s], wts_l[s], w.E, w.W, w.cap,
+            pls[s][0].view(np.uint16).reshape(w.T, w.H), pls[s][1:])
+            for s in range(w.W)]
+    elif fp8_group is None:
         packs = [oracle.dispatch_pack(ids_l[s], wts_l[s], w.E, w.W, w.cap, pls[s])
                  for s in range(w.W)]
     else:
@@ -129,7 +145,7 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
     row_bytes = [p.shape[1] * p.itemsize for p in pls[0]]
     dt = torch.float32 if f32 else torch.bfloat16
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, dt, "cuda",
-                   fill=SENTINEL, quant_group=fp8_group)
+                   fill=SENTINEL, quant_group=fp8_group, quant_fp4=fp4)
     for s in range(w.W):
         ep.set_source(s, ids_l[s], wts_l[s], pls[s])
     for s in range(w.W):
@@ -153,8 +169,8 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
                                   p["send_w"][d, :c].view(np.uint32)), f"w {s}->{d}"
             assert (g_eloc[s, d, c:].view(np.uint32) == 0xFFFFFFFF).all(), "eloc tail written"
             for q in range(n_pl):
-                assert np.array_equal(g_send[q][s, d, :c], p["send"][q][d, :c]), \
-                    f"payload {q} {s}->{d}"
+                assert_bytes_equal(g_send[q][s, d, :c], p["send"][q][d, :c],
+                                   f"payload {q} {s}->{d}")
                 assert (g_send[q][s, d, c:] == SENTINEL).all(), f"payload {q} tail written"
 
     if corrupt_cnt is not None:
@@ -239,7 +255,7 @@ def column_windows(nbytes: int, width: int = 64):
     return np.array(sorted(set(out)), dtype=np.int64)
 
 
-def run_fullsize(w: wl.Workload, seed: int = 0, fp8_group=None):
+def run_fullsize(w: wl.Workload, seed: int = 0, fp8_group=None, fp4=False):
     """Whole path at full size. Every integer output and every valid payload
     byte is compared; the combine is compared on column windows that the
     oracle computes exactly (the reduction is independent per column). With
@@ -251,11 +267,21 @@ def run_fullsize(w: wl.Workload, seed: int = 0, fp8_group=None):
     pls = [wl.payloads(w, s, seed, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
     row_bytes = [p.shape[1] for p in pls[0]]
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
-                   fill=SENTINEL, quant_group=fp8_group)
+                   fill=SENTINEL, quant_group=fp8_group, quant_fp4=fp4)
     n_pl = len(ep.send)
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
-    if fp8_group is None:
+    if fp4:
+        say(f"[fullsize] {w.name}: oracle 4-bit quantisation")
+        qs, ss = [], []
+        for s in range(w.W):
+            q, sc = oracle.quantize_fp4(pls[s][0].view(np.uint16).reshape(w.T, w.H))
+            scp = np.zeros((w.T, oracle.fp4_scale_pitch(w.H)), np.uint8)
+            scp[:, :sc.shape[1]] = sc
+            qs.append(torch.from_numpy(q))
+            ss.append(torch.from_numpy(scp))
+        exp_src = [torch.stack(qs).to(dev), torch.stack(ss).to(dev)] + ep.src[1:]
+    elif fp8_group is None:
         exp_src = ep.src
     else:
         say(f"[fullsize] {w.name}: oracle quantisation")

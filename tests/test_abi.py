@@ -130,6 +130,32 @@ def test_dispatch_pack_argument_checks():
     assert _pack(T=0, cap=1 << 28, K=8, E=64, W=8) == B.EINVAL
 
 
+def test_dispatch_pack_fp4_argument_checks():
+    lib = B.load()
+
+    def call(H=256, hs=None, q=FAKE, qs=None, sc=FAKE, ss=None, cap=16):
+        hs = 2 * H if hs is None else hs
+        qs = cap * H // 2 if qs is None else qs
+        sp = B.fp4_scale_pitch(H)
+        ss = cap * sp if ss is None else ss
+        pl = _payloads()
+        return lib.moe_ep_dispatch_pack_fp4(FAKE, FAKE, 16, 2, 8, 4, cap, FAKE, hs, H,
+                                            q, qs, sc, ss, ctypes.addressof(pl), 0,
+                                            FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+                                            None)
+
+    assert B.fp4_scale_pitch(7168) == 448 and B.fp4_scale_pitch(544) == 48
+    assert call(H=0) == B.EINVAL
+    assert call(H=272) == B.EALIGN                   # H/2 = 136 bytes
+    assert call(hs=2 * 256 - 16) == B.EINVAL
+    assert call(qs=16 * 128 - 16) == B.EINVAL
+    assert call(ss=16 * 16 - 16) == B.EINVAL
+    assert call(q=None) == B.EINVAL
+    assert call(q=FAKE + 8) == B.EALIGN
+    assert call(sc=FAKE + 4) == B.EALIGN
+    assert call(ss=16 * 16 + 8) == B.EALIGN
+
+
 def test_expert_batch_argument_checks():
     lib = B.load()
 

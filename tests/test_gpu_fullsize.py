@@ -31,6 +31,15 @@ def test_fullsize_fp8_pack(wid):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("wid", [2, 5])
+def test_fullsize_fp4_pack(wid):
+    """4-bit quantize-on-pack at the DeepSeek-V3 and multi-payload shapes."""
+    w = wl.WORKLOADS[wid]
+    say(f"[fullsize fp4] start {w.name}")
+    run_fullsize(w, fp4=True)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("wid", [2, 3, 4])
 def test_fullsize_fused_local_combine(wid):
     """The fused combine of each rank's local slice at full size (the shared

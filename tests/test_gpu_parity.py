@@ -169,3 +169,63 @@ def test_fused_local_combine_is_bit_identical_to_unfused(name, f32):
     del ep1
     ep2, _ = run_full_parity(CASES[name], salt=29, f32=f32, fused_local=True)
     assert torch.equal(out1.view(torch.uint8), ep2.out.view(torch.uint8))
+
+
+FP4_CASES = dict(FP8_CASES, ragged_scales=W1.scaled(T=70, cap=70, H=544))
+
+
+@pytest.mark.parametrize("name", sorted(FP4_CASES))
+def test_parity_fp4_pack(name):
+    """4-bit quantize-on-pack: codes, scale codes (with their 0x00 padding)
+    and every other output bit-exact."""
+    w = FP4_CASES[name]
+    say(f"[parity fp4] {name}")
+    run_full_parity(w, salt=37, fp4=True)
+
+
+def test_fp4_every_bf16_bit_pattern():
+    """All 65,536 bf16 bit patterns (zeros, subnormals, normals, infinities,
+    NaNs) in 16-column blocks through the 4-bit quantiser: the scales cover
+    underflow to 0x00, every normal range and saturation at 448; the codes
+    cover every midpoint. Bit-exact with the oracle."""
+    rng = np.random.default_rng(41)
+    vals = rng.permutation(np.arange(0x10000, dtype=np.uint32)).astype(np.uint16)
+    H = 1024
+    T = len(vals) // H
+    hidden = vals.reshape(T, H)
+    w = W1.scaled(W=1, E=2, K=1, T=T, cap=T, H=H, pad_frac=0.0)
+    ids = np.zeros((T, 1), np.int32)
+    wts = np.ones((T, 1), np.float32)
+    say(f"[fp4 sweep] all bf16 patterns in {T} rows")
+    try:
+        run_full_parity(w, srcs=[(ids, wts)],
+                        pls=[[hidden.view(np.uint8).reshape(T, 2 * H)]], fp4=True)
+    except AssertionError as e:
+        # name the inputs of the first differing code byte (row, byte)
+        import re
+        m = re.search(r"\((\d+), (\d+)\)", str(e))
+        if m:
+            t, b = int(m.group(1)), int(m.group(2))
+            blk = hidden[t, (2 * b) // 16 * 16:(2 * b) // 16 * 16 + 16]
+            say(f"[fp4 sweep] row {t} byte {b}: columns {2 * b}, {2 * b + 1} = "
+                f"{hidden[t, 2 * b]:#06x}, {hidden[t, 2 * b + 1]:#06x}; block "
+                + " ".join(f"{v:04x}" for v in blk))
+        raise
+
+
+def test_fp8_every_bf16_bit_pattern():
+    """All 65,536 bf16 bit patterns through the fp8 quantiser (groups of
+    128): NaN entries never set a group's amax; groups with an infinite
+    amax get scale inf and r = 0; codes carry their input's sign. Codes and
+    scales bit-exact with the oracle."""
+    rng = np.random.default_rng(43)
+    vals = rng.permutation(np.arange(0x10000, dtype=np.uint32)).astype(np.uint16)
+    H = 1024
+    T = len(vals) // H
+    hidden = vals.reshape(T, H)
+    w = W1.scaled(W=1, E=2, K=1, T=T, cap=T, H=H, pad_frac=0.0)
+    ids = np.zeros((T, 1), np.int32)
+    wts = np.ones((T, 1), np.float32)
+    say(f"[fp8 sweep] all bf16 patterns in {T} rows")
+    run_full_parity(w, srcs=[(ids, wts)],
+                    pls=[[hidden.view(np.uint8).reshape(T, 2 * H)]], fp8_group=128)

@@ -136,3 +136,19 @@ def test_pack_fp4_is_quantize_then_pack_with_zero_scale_padding():
     plain = oracle.dispatch_pack(ids, wts, w.E, w.W, w.cap)
     for k in ("send_cnt", "send_eloc", "token_slot"):
         assert np.array_equal(r[k], plain[k])
+
+
+def test_fp4_nonfinite_inputs():
+    """Hand-derived: NaN never becomes a block's amax, even followed by
+    smaller values; an infinite amax saturates the scale at 448; every code
+    carries its input's sign bit (a NaN gives a zero of its sign)."""
+    row = np.zeros(32, np.uint16)
+    # block 0: -sNaN, +inf, 1.0, -2.0: amax = inf, scale 0x7E (448), r = 1/448
+    row[0:4] = [0xFFBC, 0x7F80, 0x3F80, 0xC000]
+    # block 1: 1.0, +sNaN, 0.5: amax = 1, 1/6 -> e4m3 0.171875 (0x23),
+    # r = 5.818: 1.0 -> 5.82 -> 7; 0.5 -> 2.91 -> 3 (code 5); NaN -> +0
+    row[16:19] = [0x3F80, 0x7FA0, 0x3F00]
+    q, sc = oracle.quantize_fp4(row[None, :])
+    assert sc[0].tolist() == [0x7E, 0x23]
+    want = [0x78, 0x80, 0, 0, 0, 0, 0, 0, 0x07, 0x05, 0, 0, 0, 0, 0, 0]
+    assert q[0].tolist() == want

@@ -76,7 +76,8 @@ def test_matches_torch_conversion_in_range():
 
 
 def test_golden_quantized_row():
-    g = json.load(open(os.path.join(GOLD, "fp8_quant.json")))
+    with open(os.path.join(GOLD, "fp8_quant.json")) as fh:
+        g = json.load(fh)
     H, group = g["H"], g["group"]
     row = np.zeros(H, np.float32)
     for k, v in g["row_values"].items():
@@ -124,3 +125,19 @@ def test_pack_fp8_is_quantize_then_pack():
         assert got.shape[1] == Gp
         assert np.array_equal(got[:, :sc.shape[1]], sc[toks])
         assert (got[:, sc.shape[1]:].view(np.uint32) == 0).all()
+
+
+def test_fp8_nonfinite_inputs():
+    """Hand-derived, groups of 32: NaN never becomes a group's amax; an
+    infinite amax gives scale inf and r = 0; every code carries its input's
+    sign bit (NaN, and inf * 0, give the NaN code with x's sign)."""
+    row = np.zeros(64, np.uint16)
+    row[0:4] = [0xFFBC, 0x7F80, 0x3F80, 0xC000]     # -sNaN, +inf, 1.0, -2.0
+    row[32:35] = [0x3F80, 0x7FA0, 0x3F00]           # 1.0, +sNaN, 0.5
+    q, sc = oracle.quantize_fp8(row[None, :], 32)
+    assert np.isinf(sc[0, 0]) and sc[0, 1] == np.float32(1.0) / np.float32(448.0)
+    assert q[0, :4].tolist() == [0xFF, 0x7F, 0x00, 0x80]
+    assert (q[0, 4:32] == 0).all()
+    # r = 448: 1.0 -> 448 (0x7E); NaN -> 0x7F; 0.5 -> 224 = 1.75 * 2^7 (0x76)
+    assert q[0, 32:35].tolist() == [0x7E, 0x7F, 0x76]
+    assert (q[0, 35:] == 0).all()
