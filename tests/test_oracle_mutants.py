@@ -65,8 +65,14 @@ MUTANTS = {
         "const float r = amax > 0.0f ? 448.0f / amax : 1.0f;",
         "const float r = amax > 0.0f ? 447.0f / amax : 1.0f;"),
     "quant_multiplies_by_scale": (
-        "q[t * q_row_stride + h] = oracle_f32_to_e4m3(v * r);",
-        "q[t * q_row_stride + h] = oracle_f32_to_e4m3(v * s);"),
+        "const uint8_t c = oracle_f32_to_e4m3(v * r);",
+        "const uint8_t c = oracle_f32_to_e4m3(v * s);"),
+    "quant_sign_from_product": (
+        "(uint8_t)((c & 0x7Fu) | (signbit(v) ? 0x80u : 0u));",
+        "c;"),
+    "fp4_amax_takes_nan": (
+        "float v = fabsf(oracle_bf16_to_f32(x[t * x_row_stride + h]));\n                if (v > amax)\n                    amax = v;\n            }\n            const uint8_t s8",
+        "float v = fabsf(oracle_bf16_to_f32(x[t * x_row_stride + h]));\n                if (!(v <= amax))\n                    amax = v;\n            }\n            const uint8_t s8"),
     "e4m3_subnormal_round_half_up": (
         "const double m = rint(a * 512.0);",
         "const double m = floor(a * 512.0 + 0.5);"),
@@ -137,6 +143,8 @@ def _pin_battery():
         fp4pins.test_e2m1_midpoints_neighbours_and_random_match_exact_rounding,
         fp4pins.test_golden_fp4_rows,
         fp4pins.test_fp4_dequantisation_error_bound,
+        fp4pins.test_fp4_nonfinite_inputs,
+        fp8pins.test_fp8_nonfinite_inputs,
         lambda: sanpins.test_sanitize_matches_brute_force_from_routing(4, 8, 3),
     ]
 
