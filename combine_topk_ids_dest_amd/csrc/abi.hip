@@ -280,6 +280,13 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
     int32_t* tile_off = reinterpret_cast<int32_t*>(wsb + ws.off_off);
     int32_t* rank = reinterpret_cast<int32_t*>(wsb + ws.rank_off);
 
+    // One tile of tokens (decode-sized batches): pack_copy routes by itself
+    // and writes send_cnt; no separate routing launch.
+    if (T > 0 && T <= kRouteTile)
+        return hip_status(launch_pack_copy(topk_ids, topk_weights, T, K, E,
+                                           sh.e_local, W, sh.slots, sh.cap, nullptr,
+                                           token_slot, nullptr, nullptr, send_cnt, P,
+                                           quant, send_eloc, send_w, err_flags, st));
     rc = hip_status(launch_route_local(topk_ids, T, K, E, sh.e_local, W,
                                        rank, tile_cnt, err_flags, st));
     if (rc) return rc;

@@ -17,8 +17,15 @@
 
 namespace moe_ep {
 
-constexpr int kPackThreads = 256;
-constexpr int kPackUnroll = 4;
+#ifndef MOE_EP_PACK_THREADS
+#define MOE_EP_PACK_THREADS 512
+#endif
+#ifndef MOE_EP_PACK_UNROLL
+#define MOE_EP_PACK_UNROLL 2
+#endif
+constexpr int kPackThreads = MOE_EP_PACK_THREADS;
+constexpr int kPackUnroll = MOE_EP_PACK_UNROLL;
+static_assert(kPackThreads >= kRouteTile, "own routing holds one tile of masks");
 
 // Sum of tile_cnt[j][d] over tiles j < tiles (loads issued 8 at a time).
 __device__ __forceinline__ int32_t sum_tiles(const int32_t* __restrict__ tile_cnt,
@@ -257,10 +264,49 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     __shared__ int32_t s_dest[MOE_EP_MAX_WORLD];
     __shared__ int32_t s_slot[MOE_EP_MAX_WORLD];
     __shared__ int s_n;
+    // Own routing (rank == nullptr, at most one tile of tokens): every
+    // block derives the destination masks of all T tokens and counts, per
+    // destination, the tokens before its own with one ballot per wave.
+    __shared__ uint64_t s_mask[kPackThreads];
+    __shared__ int32_t s_wcnt[kPackThreads / 64][MOE_EP_MAX_WORLD];
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const bool own_route = rank == nullptr;
 
     if (tile_cnt && blockIdx.x == 0 && tid < W)
         send_cnt[tid] = sum_tiles(tile_cnt, (T + kRouteTile - 1) / kRouteTile, W, tid);
+
+    if (own_route) {
+        uint64_t mask = 0;
+        uint32_t bad = 0;
+        if (tid < T) {
+            const int32_t* row = ids + (int64_t)tid * K;
+#pragma unroll 8
+            for (int k = 0; k < K; ++k) {
+                const int32_t id = row[k];
+                if (id < 0) continue;
+                if (id >= E) { bad |= MOE_EP_ERR_ID_RANGE; continue; }
+                mask |= 1ull << (id / e_local);
+            }
+        }
+        s_mask[tid] = mask;
+        if (blockIdx.x == 0) {
+            report(err, bad);
+            for (int d = 0; d < W; ++d) {
+                const uint64_t bl = __ballot((mask >> d) & 1ull);
+                if (lane == 0) s_wcnt[wave][d] = __popcll(bl);
+            }
+        }
+        __syncthreads();
+        if (blockIdx.x == 0 && tid < W) {
+            int32_t c = 0;
+#pragma unroll
+            for (int w = 0; w < kPackThreads / 64; ++w) c += s_wcnt[w][tid];
+            send_cnt[tid] = c;
+        }
+        __syncthreads();
+    }
 
     for (int64_t b = blockIdx.x; b < T * nsplit; b += gridDim.x) {
         const int64_t t = b / nsplit;
@@ -303,42 +349,40 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             }
         }
 
+        if (own_route) {
+            const uint64_t before = tid < t ? s_mask[tid] : 0;
+            for (int d = 0; d < W; ++d) {
+                const uint64_t bl = __ballot((before >> d) & 1ull);
+                if (lane == 0) s_wcnt[wave][d] = __popcll(bl);
+            }
+            __syncthreads();
+        }
+
+        // Wave 0: the token's final slot per destination (lane d), and the
+        // list of its destinations in LDS for the copy.
+        int32_t slot = -1;
         if (tid < 64) {
             const int d = tid;
-            int32_t slot = -1;
             if (d < W) {
-                slot = rank[t * W + d];
-                if (slot >= 0)
-                    slot += tile_cnt ? sum_tiles(tile_cnt, t / kRouteTile, W, d)
-                                     : tile_off[(t / kRouteTile) * W + d];
+                if (own_route) {
+                    if ((s_mask[t] >> d) & 1ull) {
+                        slot = 0;
+#pragma unroll
+                        for (int w = 0; w < kPackThreads / 64; ++w) slot += s_wcnt[w][d];
+                    }
+                } else {
+                    slot = rank[d * T + t];
+                    if (slot >= 0)
+                        slot += tile_cnt ? sum_tiles(tile_cnt, t / kRouteTile, W, d)
+                                         : tile_off[(t / kRouteTile) * W + d];
+                }
+                if (part == 0) token_slot[t * W + d] = slot;
             }
             const uint64_t act = __ballot(slot >= 0);
             if (slot >= 0) {
                 const int pos = rank_below(act);
                 s_dest[pos] = d;
                 s_slot[pos] = slot;
-            }
-            if (part == 0 && d < W) {
-                token_slot[t * W + d] = slot;
-                uint32_t bad = 0;
-                if (slot >= 0) {
-                    const int64_t meta = ((int64_t)d * cap + slot) * slots;
-                    int j = 0;
-#pragma unroll 8
-                    for (int k = 0; k < K; ++k) {
-                        const int32_t id = ids[t * K + k];
-                        if (id < 0 || id >= E || id / e_local != d) continue;
-                        if (j >= slots) { bad |= MOE_EP_ERR_PICKS; continue; }
-                        send_eloc[meta + j] = id - d * e_local;
-                        send_w[meta + j] = wts[t * K + k];
-                        ++j;
-                    }
-                    for (; j < slots; ++j) {
-                        send_eloc[meta + j] = -1;
-                        send_w[meta + j] = 0.0f;
-                    }
-                }
-                report(err, bad);
             }
             if (tid == 0) s_n = __popcll(act);
         }
@@ -413,6 +457,30 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
                     }
                 }
             }
+        }
+        // Wave 0, after its share of the copy: the pick metadata of each
+        // destination slot (block of part 0 only).
+        if (tid < W && part == 0) {
+            const int d = tid;
+            uint32_t bad = 0;
+            if (slot >= 0) {
+                const int64_t meta = ((int64_t)d * cap + slot) * slots;
+                int j = 0;
+#pragma unroll 8
+                for (int k = 0; k < K; ++k) {
+                    const int32_t id = ids[t * K + k];
+                    if (id < 0 || id >= E || id / e_local != d) continue;
+                    if (j >= slots) { bad |= MOE_EP_ERR_PICKS; continue; }
+                    send_eloc[meta + j] = id - d * e_local;
+                    send_w[meta + j] = wts[t * K + k];
+                    ++j;
+                }
+                for (; j < slots; ++j) {
+                    send_eloc[meta + j] = -1;
+                    send_w[meta + j] = 0.0f;
+                }
+            }
+            report(err, bad);
         }
         __syncthreads();   // s_dest / s_slot are rewritten for the next token
     }

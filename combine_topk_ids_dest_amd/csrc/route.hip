@@ -8,12 +8,15 @@
 // two levels without atomics, so the result does not depend on scheduling:
 //   route_local: per tile of 256 tokens, a wave64 ballot per destination
 //     gives each token its rank among the tile's tokens for d (kept in the
-//     workspace); the tile's count per destination goes to the workspace.
+//     workspace, destination-major [W][T] so that every store of a wave is
+//     contiguous); the tile's count per destination goes to the workspace.
 //   tile offsets: the exclusive prefix of the tile counts per destination.
 //     With at most kPackFuseTiles tiles, pack_copy sums the counts of the
 //     earlier tiles itself (and block 0 writes send_cnt); otherwise
 //     column_scan computes them and send_cnt.
-// pack_copy adds the tile offset to the in-tile rank.
+// pack_copy adds the tile offset to the in-tile rank. With a single tile
+// (T <= 256, decode-sized batches) neither kernel runs: every pack_copy
+// block derives the ranks of its token from the masks of all T tokens.
 #include "common.h"
 
 namespace moe_ep {
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
         const uint64_t b = __ballot((mask >> d) & 1ull);
         const int32_t before = wave_cnt[wave][d];
         if (t < T)
-            rank[t * W + d] = ((mask >> d) & 1ull) ? before + rank_below(b) : -1;
+            rank[d * T + t] = ((mask >> d) & 1ull) ? before + rank_below(b) : -1;
     }
 }
 
