@@ -105,7 +105,15 @@ __global__ __launch_bounds__(256) void batch_local_kernel(
 
 constexpr int kBatchThreads = 256;
 constexpr int kBatchUnroll = 4;
+// Rows of the leading payload above this many 16-byte vectors have their
+// first pass loaded before the slot's expert rows are known (the loads
+// overlap wave 0's planning; it costs registers, which narrower rows, with
+// less to overlap, need more).
+#ifndef MOE_EP_BATCH_PREFETCH_VECS
+#define MOE_EP_BATCH_PREFETCH_VECS 512
+#endif
 
+template <bool PREFETCH>
 __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
     const int32_t* __restrict__ recv_cnt, int64_t cnt_stride,
     const int32_t* __restrict__ recv_eloc, int64_t eloc_stride, int W,
@@ -126,6 +134,21 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
     for (int32_t v = blockIdx.x; v < S; v += gridDim.x) {
         const int s = find_source(pre, W, v);
         const int32_t slot = v - pre[s];
+        // The source row does not depend on the expert rows: with the
+        // prefetch its first pass is in flight while wave 0 plans the rows.
+        u32x4 x0[kBatchUnroll];
+        int64_t first = 0;
+        if (PREFETCH && P.n > 0) {
+            const int64_t rb = P.row_bytes[0];
+            const int64_t nvec = rb >> 4;
+            const uint8_t* src = P.src[0] + s * P.src_stride[0] + (int64_t)slot * rb;
+#pragma unroll
+            for (int u = 0; u < kBatchUnroll; ++u) {
+                const int64_t i = tid + u * kBatchThreads;
+                if (i < nvec) x0[u] = ld_row<MOE_EP_BATCH_LD_NT>(src + i * 16);
+            }
+            first = kBatchThreads * kBatchUnroll;
+        }
         if (tid < 64) {
             const int j = tid;
             int32_t row = -1;
@@ -155,11 +178,24 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
         __syncthreads();
         const int n = s_n;
 
+        if (PREFETCH && P.n > 0) {
+            const int64_t rb = P.row_bytes[0];
+            const int64_t nvec = rb >> 4;
+            for (int a = 0; a < n; ++a) {
+                uint8_t* dst = P.dst[0] + s_exp[a] * P.dst_stride[0] + (int64_t)s_row[a] * rb;
+#pragma unroll
+                for (int u = 0; u < kBatchUnroll; ++u) {
+                    const int64_t i = tid + u * kBatchThreads;
+                    if (i < nvec) st_row<MOE_EP_BATCH_ST_NT>(dst + i * 16, x0[u]);
+                }
+            }
+        }
         for (int p = 0; p < P.n; ++p) {
             const int64_t rb = P.row_bytes[p];
             const uint8_t* src = P.src[p] + s * P.src_stride[p] + (int64_t)slot * rb;
             const int64_t nvec = rb >> 4;
-            for (int64_t i0 = tid; i0 < nvec; i0 += kBatchThreads * kBatchUnroll) {
+            for (int64_t i0 = tid + (p == 0 ? first : 0); i0 < nvec;
+                 i0 += kBatchThreads * kBatchUnroll) {
                 u32x4 x[kBatchUnroll];
 #pragma unroll
                 for (int u = 0; u < kBatchUnroll; ++u) {
@@ -253,9 +289,14 @@ hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
     const int64_t max_rows = (int64_t)W * cap;
     if (max_rows == 0) return hipSuccess;
     const int64_t grid = max_rows < MOE_EP_ROW_GRID ? max_rows : MOE_EP_ROW_GRID;
-    batch_copy_kernel<<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>(
-        recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
-        tile_off, recv_row, P, err);
+    if (P.n > 0 && P.row_bytes[0] / 16 > MOE_EP_BATCH_PREFETCH_VECS)
+        batch_copy_kernel<true><<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>(
+            recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
+            tile_off, recv_row, P, err);
+    else
+        batch_copy_kernel<false><<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>(
+            recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
+            tile_off, recv_row, P, err);
     return hipGetLastError();
 }
 

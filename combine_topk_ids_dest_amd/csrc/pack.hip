@@ -18,10 +18,10 @@
 namespace moe_ep {
 
 #ifndef MOE_EP_PACK_THREADS
-#define MOE_EP_PACK_THREADS 512
+#define MOE_EP_PACK_THREADS 256
 #endif
 #ifndef MOE_EP_PACK_UNROLL
-#define MOE_EP_PACK_UNROLL 2
+#define MOE_EP_PACK_UNROLL 4
 #endif
 constexpr int kPackThreads = MOE_EP_PACK_THREADS;
 constexpr int kPackUnroll = MOE_EP_PACK_UNROLL;
