@@ -104,8 +104,9 @@ def test_fp4_dequantisation_error_bound():
     q, sc = oracle.quantize_fp4(x)
     f = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(w.T, -1, 16)
     codes = np.stack([q & 0xF, q >> 4], axis=2).reshape(w.T, -1, 16)
-    vals = np.vectorize(e2m1_value)(codes)
-    s = np.vectorize(e4m3_value)(sc)[:, :, None]
+    vals = np.vectorize(lambda c: e2m1_value(int(c)))(codes)
+    s = np.vectorize(lambda c: e4m3_value(int(c)))(sc)[:, :, None]
+    assert (s > 0).all() and (s < 448).all()
     y = np.abs(f) / np.where(s > 0, s, 1)
     half = np.where(y < 2, 0.25, np.where(y < 4, 0.5, 1.0))
     sat = np.maximum(y - 6, 0)
