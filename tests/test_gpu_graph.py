@@ -14,11 +14,11 @@ from parity import say
 pytestmark = pytest.mark.gpu
 
 
-def _setup(w, seed):
+def _setup(w, seed, **mode):
     srcs = [wl.routing(w, s, seed) for s in range(w.W)]
     pls = [wl.payloads(w, s, seed, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, [p.shape[1] for p in pls[0]],
-                   torch.bfloat16, "cuda", fill=0xFF)
+                   torch.bfloat16, "cuda", fill=0xFF, **mode)
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
     wl.expert_outputs_device(ep.Y, seed=3000 + seed)
@@ -31,12 +31,24 @@ def _outputs(ep):
            [x.clone() for x in ep.send]
 
 
-@pytest.mark.parametrize("wid,scale", [(4, None), (1, None), (2, dict(T=600, cap=640, H=1024))])
-def test_graph_replay_matches_eager(wid, scale):
+SMALL_DSV3 = dict(T=600, cap=640, H=1024)
+CASES = [
+    (4, None, {}, False),
+    (1, None, {}, False),
+    (2, SMALL_DSV3, {}, False),
+    # the other forms of the path: quantised packs and the fused local combine
+    (2, SMALL_DSV3, dict(quant_group=128), False),
+    (4, None, dict(quant_fp4=True), False),
+    (2, SMALL_DSV3, {}, True),
+]
+
+
+@pytest.mark.parametrize("wid,scale,mode,fused", CASES)
+def test_graph_replay_matches_eager(wid, scale, mode, fused):
     w = wl.WORKLOADS[wid] if scale is None else wl.WORKLOADS[wid].scaled(**scale)
-    say(f"[graph] {w.name} T={w.T} W={w.W}")
-    ep = _setup(w, 1)
-    ep.step()
+    say(f"[graph] {w.name} T={w.T} W={w.W} {mode} fused={fused}")
+    ep = _setup(w, 1, **mode)
+    ep.step(fused_local=fused)
     torch.cuda.synchronize()
     eager = _outputs(ep)
 
@@ -44,11 +56,11 @@ def test_graph_replay_matches_eager(wid, scale):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        ep.step()                     # warm the prepared calls on this stream
+        ep.step(fused_local=fused)    # warm the prepared calls on this stream
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        ep.step()
+        ep.step(fused_local=fused)
     torch.cuda.synchronize()
     for rep in range(4):
         # eager work between replays: scribble over the outputs that the
