@@ -42,6 +42,25 @@ constexpr int kCombineThreads = 256;
 #endif
 constexpr int kVU = MOE_EP_COMBINE_VU;
 
+// fp32 -> bf16 by gfx950's conversion instruction (v_cvt_pk_bf16_f32, two
+// values per instruction: round to nearest even, NaN kept quiet with its
+// upper payload bits, the same bits as to_bf16_rne on every input), or by
+// to_bf16_rne (0).
+#ifndef MOE_EP_HW_BF16
+#define MOE_EP_HW_BF16 1
+#endif
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to bf16 (nearest even), packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    if (MOE_EP_HW_BF16) {
+        const f32x2 f = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    }
+    return to_bf16_rne(lo) | (to_bf16_rne(hi) << 16);
+}
+
 struct Bf16Elems {
     static constexpr int kPerVec = 8;
     __device__ static void to_f32(const u32x4& v, float* f) {
@@ -54,12 +73,13 @@ struct Bf16Elems {
     __device__ static u32x4 from_f32(const float* f) {
         u32x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v[i] = to_bf16_rne(f[2 * i]) | (to_bf16_rne(f[2 * i + 1]) << 16);
+        for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
         return v;
     }
     // the value the data type stores for x
-    __device__ static float round(float x) { return __uint_as_float(to_bf16_rne(x) << 16); }
+    __device__ static float round(float x) {
+        return __uint_as_float(pack_bf16x2(x, 0.0f) << 16);
+    }
 };
 
 struct F32Elems {

@@ -12,7 +12,10 @@ namespace moe_ep {
 // Tokens per block of the routing kernel (4 waves, one token per lane).
 constexpr int kRouteTile = 256;
 // Up to this many token tiles, pack_copy derives tile offsets itself.
-constexpr int kPackFuseTiles = 64;
+#ifndef MOE_EP_PACK_FUSE_TILES
+#define MOE_EP_PACK_FUSE_TILES 64
+#endif
+constexpr int kPackFuseTiles = MOE_EP_PACK_FUSE_TILES;
 // Pick entries per block of the receive-scan kernel (256 lanes x 4 rounds).
 constexpr int kBatchTile = 1024;
 constexpr int kBatchRounds = kBatchTile / 256;
