@@ -168,6 +168,42 @@ __device__ __forceinline__ uint32_t e2m1_code(float y, float x) {
     return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
+// The E2M1 codes of x[c] * r for 8 values, two per byte (x[0] in the low
+// nibble of byte 0). gfx950's pair conversion (v_cvt_scalef32_pk_fp4_f32,
+// scale 1) rounds to nearest even and saturates at 6 like e2m1_code, but
+// turns a NaN into the largest code; a NaN product is therefore replaced by
+// a zero with x's sign first, which gives e2m1_code's result on every input.
+// (0: e2m1_code for each value.)
+#ifndef MOE_EP_HW_FP4
+#define MOE_EP_HW_FP4 1
+#endif
+// x * r, or a zero with x's sign when that is NaN
+__device__ __forceinline__ float scaled_or_zero(float x, float r) {
+    const float y = __fmul_rn(x, r);
+    return y == y ? y : __uint_as_float(__float_as_uint(x) & 0x80000000u);
+}
+
+// byte SEL of word <- the codes of the pair (x[2*SEL], x[2*SEL+1])
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t word, const float* x, float r) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
+        word, scaled_or_zero(x[2 * SEL], r), scaled_or_zero(x[2 * SEL + 1], r), 1.0f, SEL);
+}
+
+__device__ __forceinline__ uint32_t e2m1_word(const float* x, float r) {
+    uint32_t word = 0;
+    if (MOE_EP_HW_FP4) {
+        word = e2m1_pair<0>(word, x, r);
+        word = e2m1_pair<1>(word, x, r);
+        word = e2m1_pair<2>(word, x, r);
+        word = e2m1_pair<3>(word, x, r);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) word |= e2m1_code(__fmul_rn(x[c], r), x[c]) << (4 * c);
+    }
+    return word;
+}
+
 __device__ __forceinline__ void quantize_pass_fp4(const uint8_t* __restrict__ src,
                                                   int64_t base, int64_t hi,
                                                   Fp4Pass& out) {
@@ -202,14 +238,8 @@ __device__ __forceinline__ void quantize_pass_fp4(const uint8_t* __restrict__ sr
         const float sv = e4m3_value(s8);
         const float r = sv > 0.0f ? __fdiv_rn(1.0f, sv) : 0.0f;
         out.scale[u] = s8;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                word |= e2m1_code(__fmul_rn(f[8 * w + c], r), f[8 * w + c]) << (4 * c);
-            out.codes[u][w] = word;
-        }
+        out.codes[u][0] = e2m1_word(f, r);
+        out.codes[u][1] = e2m1_word(f + 8, r);
     }
 }
 
