@@ -22,6 +22,13 @@ with R_own expert rows) leaves the reduce and enters the fused unpack:
   reduce_peers (dest r)   (R - R_own)*Hb + (S - S_own)*(slots*8 + Hb)
   unpack_fused (source s) (U - S_own)*Hb + R_own*Hb + S_own*slots*8 + T*Hb
 
+Besides the contract fields the line carries: per-call times (a separate
+pass with HIP events around each call), the time per rank share, the
+critical-path rate (T over the slowest rank's share, which sets the pace
+under skewed routing), the dispatch and combine split, and the same calls
+timed cold (each after a 1 GiB device write that evicts the 256 MB
+last-level cache).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
 import argparse
@@ -332,25 +339,58 @@ def main():
              + [k_unp] * w.W)
     red_call = ep.reduce_peers if fused else ep.reduce
     unp_call = ep.unpack_fused if fused else ep.unpack
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in kinds] for _ in range(args.steps)]
-    for k in range(args.steps):
-        i = 0
-        for s in range(w.W):
-            ev[k][i][0].record(stream); ep.pack(s); ev[k][i][1].record(stream); i += 1
-        for r in range(w.W):
-            ev[k][i][0].record(stream); ep.batch_plan(r); ev[k][i][1].record(stream); i += 1
-            ev[k][i][0].record(stream); ep.batch_copy(r); ev[k][i][1].record(stream); i += 1
-            ev[k][i][0].record(stream); red_call(r); ev[k][i][1].record(stream); i += 1
-        for s in range(w.W):
-            ev[k][i][0].record(stream); unp_call(s); ev[k][i][1].record(stream); i += 1
-    torch.cuda.synchronize()
+    # rank each call belongs to (source for pack/unpack, destination else)
+    rank_of = list(range(w.W)) + [r for r in range(w.W) for _ in range(3)] + list(range(w.W))
 
+    def timed_pass(flush=None):
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in kinds] for _ in range(args.steps)]
+
+        def one(k, i, fn, x):
+            if flush is not None:
+                flush.fill_(k & 0xFF)          # evict the last-level cache first
+            ev[k][i][0].record(stream); fn(x); ev[k][i][1].record(stream)
+
+        for k in range(args.steps):
+            i = 0
+            for s in range(w.W):
+                one(k, i, ep.pack, s); i += 1
+            for r in range(w.W):
+                one(k, i, ep.batch_plan, r); i += 1
+                one(k, i, ep.batch_copy, r); i += 1
+                one(k, i, red_call, r); i += 1
+            for s in range(w.W):
+                one(k, i, unp_call, s); i += 1
+        torch.cuda.synchronize()
+        return [[ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(len(kinds))]
+                for k in range(args.steps)]
+
+    times = timed_pass()
     calls = ["pack", "batch_plan", "batch_copy", k_red, k_unp]
     per_kind = {k: [] for k in calls}
     for k in range(args.steps):
         for i, kind in enumerate(kinds):
-            per_kind[kind].append(ev[k][i][0].elapsed_time(ev[k][i][1]))
+            per_kind[kind].append(times[k][i])
+    # Under skewed routing the slowest rank share sets the pace of a real
+    # expert-parallel step: per step, the largest per-rank sum of its calls.
+    worst_share_ms = float(np.median([
+        max(sum(t for t, rk in zip(times[k], rank_of) if rk == r) for r in range(w.W))
+        for k in range(args.steps)]))
+    dispatch_ms = float(np.mean([sum(t for t, kd in zip(times[k], kinds)
+                                      if kd in ("pack", "batch_plan", "batch_copy"))
+                                  for k in range(args.steps)]))
+    combine_ms = float(np.mean([sum(t for t, kd in zip(times[k], kinds)
+                                     if kd in (k_red, k_unp))
+                                 for k in range(args.steps)]))
+    # The same calls with the 256 MB last-level cache flushed before each
+    # one (a 1 GiB device write), so no call finds its inputs cached.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = timed_pass(flush)
+    del flush
+    cold_avg_us = {kd: float(np.mean([cold[k][i] for k in range(args.steps)
+                                      for i, x in enumerate(kinds) if x == kd])) * 1e3
+                   for kd in calls}
+    cold_step_ms = float(np.mean([sum(c) for c in cold]))
 
     send_cnt = ep.send_cnt.cpu().numpy().astype(np.int64)
     ent = ep.expert_num_tokens.cpu().numpy().astype(np.int64)
@@ -417,6 +457,14 @@ def main():
         "per_call_gbps": {k: round(float(np.sum(bm[k])) / (total_ms[k] / args.steps / 1e3) / 1e9, 1)
                           for k in calls},
         "per_call_note": "per-call times come from a separate pass with HIP events around each call",
+        "per_rank_share_us": round(ms_per_step * 1e3 / w.W, 2),
+        "critical_path_tokens_per_s": round(w.T / (worst_share_ms / 1e3), 1),
+        "dispatch_ms_per_step": round(dispatch_ms, 4),
+        "combine_ms_per_step": round(combine_ms, 4),
+        "cold": {"note": "each call timed after a 1 GiB device write that evicts the last-level cache",
+                 "per_call_avg_us": {k: round(v, 2) for k, v in cold_avg_us.items()},
+                 "tokens_per_s": round(tokens / (cold_step_ms / 1e3), 1),
+                 "effective_gbps": round(step_bytes / (cold_step_ms / 1e3) / 1e9, 1)},
         "roofline": roofline,
         "cpu_baseline": None,
     }
