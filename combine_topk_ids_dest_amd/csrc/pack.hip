@@ -11,8 +11,10 @@
 // grid still fills the chip. In every block wave 0 turns the token's in-tile
 // ranks into final slots (adding the offset of its tile, summed here from
 // the tile counts when there are few tiles) and leaves the destination list
-// in LDS; the block of part 0 also writes the final token_slot context and
-// the pick metadata.
+// in LDS; the block of part 0 also writes the final token_slot context and,
+// after its share of the copy, the pick metadata. With at most one tile of
+// tokens (T <= 256) no routing kernel runs: every block derives the in-tile
+// ranks of its token from the destination masks of all T tokens.
 #include "common.h"
 
 namespace moe_ep {
