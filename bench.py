@@ -243,6 +243,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2,
                     help="1 tiny, 2 dsv3_prefill, 3 mixtral_zipf, 4 decode, 5 multi_payload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the pass with the last-level cache evicted before each call "
+                         "(profiles then see the warm calls only)")
     ap.add_argument("--cpu-shares", type=int, default=8,
                     help="logical-rank shares the CPU oracle is timed on")
     ap.add_argument("--probe", choices=["copy"], default=None)
@@ -384,13 +387,15 @@ def main():
                                  for k in range(args.steps)]))
     # The same calls with the 256 MB last-level cache flushed before each
     # one (a 1 GiB device write), so no call finds its inputs cached.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cold = timed_pass(flush)
-    del flush
-    cold_avg_us = {kd: float(np.mean([cold[k][i] for k in range(args.steps)
-                                      for i, x in enumerate(kinds) if x == kd])) * 1e3
-                   for kd in calls}
-    cold_step_ms = float(np.mean([sum(c) for c in cold]))
+    cold_info = None
+    if not args.no_cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = timed_pass(flush)
+        del flush
+        cold_avg_us = {kd: float(np.mean([cold[k][i] for k in range(args.steps)
+                                          for i, x in enumerate(kinds) if x == kd])) * 1e3
+                       for kd in calls}
+        cold_step_ms = float(np.mean([sum(c) for c in cold]))
 
     send_cnt = ep.send_cnt.cpu().numpy().astype(np.int64)
     ent = ep.expert_num_tokens.cpu().numpy().astype(np.int64)
@@ -405,6 +410,13 @@ def main():
     gbps = step_bytes / (ms_per_step / 1e3) / 1e9
     tokens = w.W * w.T
     value = tokens / (ms_per_step / 1e3)
+
+    if not args.no_cold:
+        cold_info = {
+            "note": "each call timed after a 1 GiB device write that evicts the last-level cache",
+            "per_call_avg_us": {k: round(v, 2) for k, v in cold_avg_us.items()},
+            "tokens_per_s": round(tokens / (cold_step_ms / 1e3), 1),
+            "effective_gbps": round(step_bytes / (cold_step_ms / 1e3) / 1e9, 1)}
 
     avg_us = {k: float(np.mean(v)) * 1e3 for k, v in per_kind.items()}
     total_ms = {k: float(np.sum(v)) for k, v in per_kind.items()}
@@ -461,10 +473,7 @@ def main():
         "critical_path_tokens_per_s": round(w.T / (worst_share_ms / 1e3), 1),
         "dispatch_ms_per_step": round(dispatch_ms, 4),
         "combine_ms_per_step": round(combine_ms, 4),
-        "cold": {"note": "each call timed after a 1 GiB device write that evicts the last-level cache",
-                 "per_call_avg_us": {k: round(v, 2) for k, v in cold_avg_us.items()},
-                 "tokens_per_s": round(tokens / (cold_step_ms / 1e3), 1),
-                 "effective_gbps": round(step_bytes / (cold_step_ms / 1e3) / 1e9, 1)},
+        "cold": cold_info,
         "roofline": roofline,
         "cpu_baseline": None,
     }
