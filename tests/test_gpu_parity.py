@@ -37,6 +37,12 @@ CASES = {
     "all_padding": W1.scaled(T=40, cap=40, pad_frac=1.0),
     # no tokens at all
     "empty": W1.scaled(T=0, cap=16),
+    # the limits: 64 pick columns per slot (K = e_local = 64) ...
+    "max_slots": W1.scaled(W=2, E=128, K=64, T=50, cap=50, H=64),
+    # ... 1024 local experts on one rank ...
+    "max_e_local": W1.scaled(W=1, E=1024, K=8, T=300, cap=300, H=64),
+    # ... and a wide row (32 KiB of bf16) through every pass of every kernel
+    "wide_row": W1.scaled(W=4, E=16, K=4, T=40, cap=48, H=16384),
 }
 
 
