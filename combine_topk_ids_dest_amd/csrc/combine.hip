@@ -168,6 +168,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_reduce_kernel(
     const int64_t nvec = (H * ELEM_BYTES) >> 4;
     const int64_t expert_cap = (int64_t)W * cap;
 
+    // Valid slots of all sources, numbered densely through the prefix of the
+    // (clamped) counts; the skipped source counts as empty.
     if (tid < 64) load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre, nullptr, skip_src);
     __syncthreads();
     const int32_t S = pre[W];
@@ -180,14 +182,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_reduce_kernel(
             bool ok = false;
             int64_t base = 0;
             float w = 0.0f;
+            // the slot's metadata loads are issued together
             if (j < slots) {
                 const int64_t m = s * meta_stride + (int64_t)slot * slots + j;
                 const int32_t row = recv_row[((int64_t)s * cap + slot) * slots + j];
                 const int32_t e = recv_eloc[m];
+                w = recv_w[m];
                 if (row >= 0 && row < expert_cap && e >= 0 && e < e_local) {
                     ok = true;
                     base = (e * y_expert_stride + (int64_t)row * H) * ELEM_BYTES;
-                    w = recv_w[m];
                 }
             }
             const uint64_t act = __ballot(ok);
@@ -324,10 +327,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_unpack_fused_kernel(
                 const int64_t m = (int64_t)lslot * slots + lane;
                 const int32_t row = self_row[m];
                 const int32_t e = self_eloc[m];
+                w = self_w[m];
                 if (row >= 0 && row < expert_cap && e >= 0 && e < e_local) {
                     ok = true;
                     yrow = Y + (e * y_expert_stride + (int64_t)row * H) * ELEM_BYTES;
-                    w = self_w[m];
                 }
             }
             const uint64_t pk = __ballot(ok);
