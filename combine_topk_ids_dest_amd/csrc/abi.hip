@@ -337,11 +337,12 @@ int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
     Q.src_stride = hidden_stride;
     Q.q = static_cast<uint8_t*>(send_q);
     Q.q_stride = q_rank_stride;
-    Q.s = send_scale;
-    Q.s_stride = scale_rank_stride;
+    Q.s = reinterpret_cast<uint8_t*>(send_scale);
+    Q.s_stride = scale_rank_stride * 4;                  // floats -> bytes
     Q.H = H;
     Q.group = group;
-    Q.s_pitch = group > 0 ? (H / group + 3) / 4 * 4 : 0;
+    Q.n_scales = group > 0 ? H / group : 0;
+    Q.s_pitch = (Q.n_scales + 3) / 4 * 4 * 4;
     Q.mode = 1;
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
                     n_payloads, &Q, send_cnt, send_eloc, send_w, token_slot,
@@ -364,11 +365,12 @@ int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
     Q.src_stride = hidden_stride;
     Q.q = static_cast<uint8_t*>(send_q);
     Q.q_stride = q_rank_stride;
-    Q.s = static_cast<float*>(send_scale);
+    Q.s = static_cast<uint8_t*>(send_scale);
     Q.s_stride = scale_rank_stride;
     Q.H = H;
     Q.group = 16;
-    Q.s_pitch = (H / 16 + 15) / 16 * 16;
+    Q.n_scales = H / 16;
+    Q.s_pitch = (Q.n_scales + 15) / 16 * 16;
     Q.mode = 2;
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
                     n_payloads, &Q, send_cnt, send_eloc, send_w, token_slot,

@@ -61,21 +61,22 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Quantize-on-pack arguments: bf16 rows in, OCP fp8 e4m3 codes and one fp32
 // scale per `group` columns out, for every destination of the token.
-// mode 1, fp8: codes [W, cap, H] bytes, fp32 scales [W, cap, s_pitch]
-// (s_stride, s_pitch in floats). mode 2, fp4: two E2M1 codes per byte
-// [W, cap, H/2], E4M3 scale codes [W, cap, s_pitch] bytes (s_stride,
-// s_pitch in bytes; group 16).
+// Quantize-on-pack arguments: bf16 rows in; codes and per-group scale rows
+// out, for every destination of the token. mode 1, fp8: codes [W, cap, H]
+// (one byte per column), fp32 scales. mode 2, fp4: codes [W, cap, H/2]
+// (two E2M1 codes per byte), E4M3 scale codes (one byte per 16 columns).
+// Scale rows are padded to a multiple of 16 bytes with zero bytes (+0.0).
 struct QuantArgs {
     const uint8_t* src;   // bf16 rows [T, H]
     int64_t src_stride;   // bytes between tokens
     uint8_t* q;           // codes
     int64_t q_stride;     // bytes between destination blocks
-    float* s;             // scales (fp4: the bytes of the scale codes)
-    int64_t s_stride;     // between destination blocks (see above)
+    uint8_t* s;           // scale rows [W, cap, s_pitch bytes]
+    int64_t s_stride;     // bytes between destination blocks
+    int64_t s_pitch;      // bytes per scale row
+    int64_t n_scales;     // scales per row: H / group
     int64_t H;
     int group;            // fp8: 32, 64 or 128 columns; fp4: 16
-    int64_t s_pitch;      // fp8: H / group rounded up to 4; fp4: H / 16
-                          // rounded up to 16 (16-byte scale rows)
     int mode;             // 1 fp8, 2 fp4
 };
 

@@ -249,10 +249,9 @@ __device__ __forceinline__ void store_quant_pass_fp4(const QuantArgs& Q, int64_t
                                                      int64_t hi, const Fp4Pass& qp,
                                                      int n, const int32_t* s_dest,
                                                      const int32_t* s_slot) {
-    uint8_t* sbase = reinterpret_cast<uint8_t*>(Q.s);
     for (int a = 0; a < n; ++a) {
         uint8_t* qrow = Q.q + s_dest[a] * Q.q_stride + (int64_t)s_slot[a] * (Q.H >> 1);
-        uint8_t* srow = sbase + s_dest[a] * Q.s_stride + (int64_t)s_slot[a] * Q.s_pitch;
+        uint8_t* srow = Q.s + s_dest[a] * Q.s_stride + (int64_t)s_slot[a] * Q.s_pitch;
 #pragma unroll
         for (int u = 0; u < kQU; ++u) {
             const int64_t i = base + u * kPackThreads + threadIdx.x;
@@ -271,7 +270,8 @@ __device__ __forceinline__ void store_quant_pass(const QuantArgs& Q, int64_t bas
                                                  const int32_t* s_slot) {
     for (int a = 0; a < n; ++a) {
         uint8_t* qrow = Q.q + s_dest[a] * Q.q_stride + (int64_t)s_slot[a] * Q.H;
-        float* srow = Q.s + s_dest[a] * Q.s_stride + (int64_t)s_slot[a] * Q.s_pitch;
+        float* srow = reinterpret_cast<float*>(Q.s + s_dest[a] * Q.s_stride +
+                                               (int64_t)s_slot[a] * Q.s_pitch);
 #pragma unroll
         for (int u = 0; u < kQU; ++u) {
             const int64_t i = base + u * kPackThreads + threadIdx.x;
@@ -432,10 +432,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
                 store_quant_pass(Q, base, top, gv, more, n, s_dest, s_slot);
             }
             // the padding of each scale row is +0.0
-            const int64_t G = Q.H / Q.group;
-            if (part == 0 && tid < n)
-                for (int64_t g = G; g < Q.s_pitch; ++g)
-                    Q.s[s_dest[tid] * Q.s_stride + (int64_t)s_slot[tid] * Q.s_pitch + g] = 0.0f;
+            if (part == 0 && tid < n) {
+                float* srow = reinterpret_cast<float*>(Q.s + s_dest[tid] * Q.s_stride +
+                                                       (int64_t)s_slot[tid] * Q.s_pitch);
+                for (int64_t g = Q.n_scales; g < Q.s_pitch / 4; ++g) srow[g] = 0.0f;
+            }
         } else if (QMODE == 2) {
             if (q_lo < q_hi) store_quant_pass_fp4(Q, q_lo, q_mid, qp4, n, s_dest, s_slot);
             const uint8_t* src = Q.src + t * Q.src_stride;
@@ -447,10 +448,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
                 store_quant_pass_fp4(Q, base, top, more, n, s_dest, s_slot);
             }
             // the padding of each scale row is 0x00 (e4m3 +0.0)
-            uint8_t* sbase = reinterpret_cast<uint8_t*>(Q.s);
-            if (part == 0 && tid < n)
-                for (int64_t g = Q.H >> 4; g < Q.s_pitch; ++g)
-                    sbase[s_dest[tid] * Q.s_stride + (int64_t)s_slot[tid] * Q.s_pitch + g] = 0;
+            if (part == 0 && tid < n) {
+                uint8_t* srow = Q.s + s_dest[tid] * Q.s_stride + (int64_t)s_slot[tid] * Q.s_pitch;
+                for (int64_t g = Q.n_scales; g < Q.s_pitch; ++g) srow[g] = 0;
+            }
         } else if (MOE_EP_PACK_PREFETCH && P.n > 0) {
             const int64_t rb = P.row_bytes[0];
             for (int a = 0; a < n; ++a) {
