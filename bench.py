@@ -27,7 +27,8 @@ pass with HIP events around each call), the time per rank share, the
 critical-path rate (T over the slowest rank's share, which sets the pace
 under skewed routing), the dispatch and combine split, and the same calls
 timed cold (each after a 1 GiB device write that evicts the 256 MB
-last-level cache).
+last-level cache), and the rate of the runtime's own 1 GiB device copy in
+the same session as a second roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -217,22 +218,31 @@ def cpu_baseline(w, srcs, pls, shares: int):
     }
 
 
-def probe_copy(steps: int):
-    """A plain device copy of known size, for scaling HBM counters."""
+def copy_rate(steps: int) -> float:
+    """GB/s (read + write) of the runtime's plain device copy of 1 GiB."""
     import torch
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
     a.fill_(1)
+    b.copy_(a)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         b.copy_(a)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
+    del a, b
+    return 2 * n / dt / 1e9
+
+
+def probe_copy(steps: int):
+    """A plain device copy of known size, for scaling HBM counters."""
+    n = 1 << 30
+    gbps = copy_rate(steps)
     print(json.dumps({"probe": "copy", "bytes_read_per_launch": n,
-                      "bytes_written_per_launch": n, "ms": dt * 1e3,
-                      "gbps": 2 * n / dt / 1e9}), flush=True)
+                      "bytes_written_per_launch": n, "ms": 2 * n / gbps / 1e6,
+                      "gbps": gbps}), flush=True)
 
 
 def main():
@@ -411,6 +421,8 @@ def main():
     tokens = w.W * w.T
     value = tokens / (ms_per_step / 1e3)
 
+    # the runtime's own 1 GiB device copy in this session, as a second roofline
+    copy_gbps = copy_rate(10)
     if not args.no_cold:
         cold_info = {
             "note": "each call timed after a 1 GiB device write that evicts the last-level cache",
@@ -464,6 +476,8 @@ def main():
         },
         "effective_gbps": round(gbps, 1),
         "frac_of_peak_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+        "copy_reference_gbps": round(copy_gbps, 1),
+        "frac_of_copy_reference": round(gbps / copy_gbps, 4),
         "algorithmic_bytes_per_step": int(step_bytes),
         "per_call_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
         "per_call_gbps": {k: round(float(np.sum(bm[k])) / (total_ms[k] / args.steps / 1e3) / 1e9, 1)
