@@ -115,6 +115,7 @@ FP8_CASES = {
     "multi_small": W5.scaled(T=300, cap=300, H=1024),
     "decode": W4,
     "w64": W1.scaled(W=64, E=128, K=4, T=90, cap=96, H=128),
+    "empty": W1.scaled(T=0, cap=16),
 }
 
 
