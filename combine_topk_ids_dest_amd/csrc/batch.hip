@@ -142,6 +142,8 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
             const int64_t rb = P.row_bytes[0];
             const int64_t nvec = rb >> 4;
             const uint8_t* src = P.src[0] + s * P.src_stride[0] + (int64_t)slot * rb;
+            // (guarded loads: the compiler issues them one after another,
+            // which measured faster here than clamped loads all in flight)
 #pragma unroll
             for (int u = 0; u < kBatchUnroll; ++u) {
                 const int64_t i = tid + u * kBatchThreads;
@@ -156,11 +158,14 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
             uint32_t bad = 0;
             if (j < slots) {
                 const int64_t at = ((int64_t)s * cap + slot) * slots + j;
+                // the provisional row is loaded with the id, not after it
                 e = recv_eloc[s * eloc_stride + (int64_t)slot * slots + j];
-                if (e >= 0 && e < e_local) {
-                    const int32_t q = v * slots + j;
-                    const int64_t r = (int64_t)recv_row[at] +
-                                      tile_off[(int64_t)(q / kBatchTile) * e_local + e];
+                const int32_t prov = recv_row[at];
+                const bool ok = e >= 0 && e < e_local;
+                const int32_t q = v * slots + j;
+                const int32_t off = tile_off[(int64_t)(q / kBatchTile) * e_local + (ok ? e : 0)];
+                if (ok) {
+                    const int64_t r = (int64_t)prov + off;
                     if (r < expert_cap) row = (int32_t)r;
                     else bad |= MOE_EP_ERR_ROWCAP;
                 }

@@ -59,8 +59,6 @@ __device__ __forceinline__ void st_row(uint8_t* p, const u32x4& v) {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Quantize-on-pack arguments: bf16 rows in, OCP fp8 e4m3 codes and one fp32
-// scale per `group` columns out, for every destination of the token.
 // Quantize-on-pack arguments: bf16 rows in; codes and per-group scale rows
 // out, for every destination of the token. mode 1, fp8: codes [W, cap, H]
 // (one byte per column), fp32 scales. mode 2, fp4: codes [W, cap, H/2]
@@ -99,6 +97,28 @@ __device__ __forceinline__ int rank_below(uint64_t mask) {
 
 __device__ __forceinline__ void report(uint32_t* err, uint32_t bits) {
     if (bits && err) atomicOr(err, bits);
+}
+
+// Destination mask of one token: bit d is set when some routed pick of the
+// token lives on rank d = id / e_local. Negative ids are padding; ids >= E
+// are dropped and flagged. The ids are read 8 at a time with all 8 loads in
+// flight before the first is used (a load per pick followed by its use
+// would cost one memory latency per pick).
+__device__ __forceinline__ uint64_t token_dest_mask(const int32_t* __restrict__ row, int K,
+                                                    int E, int e_local, uint32_t& bad) {
+    uint64_t mask = 0;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = k0 + u < K ? row[k0 + u] : -1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int32_t id = v[u];
+            if (id >= E) bad |= MOE_EP_ERR_ID_RANGE;
+            if (id >= 0 && id < E) mask |= 1ull << ((uint32_t)id / (uint32_t)e_local);
+        }
+    }
+    return mask;
 }
 
 // Largest s in [0, W) with pre[s] <= v, for an ascending prefix array

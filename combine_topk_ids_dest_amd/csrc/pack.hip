@@ -60,12 +60,6 @@ __device__ __forceinline__ float group_max(float m, int lanes) {
     return m;
 }
 
-// Load the first pass of a plain (unquantised) leading row before the
-// destinations are known (1) or after (0).
-#ifndef MOE_EP_PACK_PREFETCH
-#define MOE_EP_PACK_PREFETCH 0
-#endif
-
 #ifndef MOE_EP_QUANT_UNROLL
 #define MOE_EP_QUANT_UNROLL 1
 #endif
@@ -283,8 +277,65 @@ __device__ __forceinline__ void store_quant_pass(const QuantArgs& Q, int64_t bas
     }
 }
 
+// The first pass (kPackThreads * kPackUnroll vectors) of block item b's
+// column part of the leading payload row, into registers.
+__device__ __forceinline__ void load_first_pass(const PayloadSet& P, int64_t b, int nsplit,
+                                                u32x4 (&pre)[kPackUnroll], int64_t& p_mid) {
+    const int64_t t = b / nsplit;
+    const int part = (int)(b - t * nsplit);
+    const int64_t nvec = P.row_bytes[0] >> 4;
+    const int64_t per = (nvec + nsplit - 1) / nsplit;
+    const int64_t p_lo = part * per;
+    const int64_t p_hi = p_lo + per < nvec ? p_lo + per : nvec;
+    p_mid = p_lo + kPackThreads * kPackUnroll < p_hi ? p_lo + kPackThreads * kPackUnroll : p_hi;
+    const uint8_t* src = P.src[0] + t * P.src_stride[0];
+#pragma unroll
+    for (int u = 0; u < kPackUnroll; ++u) {
+        const int64_t i = p_lo + u * kPackThreads + (int64_t)threadIdx.x;
+        if (i < p_mid) pre[u] = ld_row<MOE_EP_PACK_NT>(src + i * 16);
+    }
+}
+
+// Pick metadata of token t for destination d: the local id and weight of
+// each of its picks on d in router order, then -1 / +0.0 up to `slots`.
+// Ids and weights are read 8 picks at a time, all 16 loads in flight before
+// the first is used.
+__device__ __forceinline__ uint32_t write_pick_meta(const int32_t* __restrict__ ids,
+                                                    const float* __restrict__ wts, int64_t t,
+                                                    int K, int E, int e_local, int d, int slots,
+                                                    int32_t* eloc, float* w) {
+    uint32_t bad = 0;
+    int j = 0;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        int32_t id8[8];
+        float w8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            id8[u] = k0 + u < K ? ids[t * K + k0 + u] : -1;
+            w8[u] = k0 + u < K ? wts[t * K + k0 + u] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int32_t id = id8[u];
+            if (id < 0 || id >= E || (uint32_t)id / (uint32_t)e_local != (uint32_t)d) continue;
+            if (j >= slots) { bad |= MOE_EP_ERR_PICKS; continue; }
+            eloc[j] = id - d * e_local;
+            w[j] = w8[u];
+            ++j;
+        }
+    }
+    for (; j < slots; ++j) {
+        eloc[j] = -1;
+        w[j] = 0.0f;
+    }
+    return bad;
+}
+
 // QMODE 0: plain rows; 1: payload 0 quantised to fp8; 2: to fp4.
-template <int QMODE>
+// PF (plain rows with own routing only): the first pass of the leading row
+// of the block's first item is loaded before the routing, so its latency
+// overlaps it.
+template <int QMODE, bool PF>
 __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t T,
     int K, int E, int e_local, int W, int slots, int64_t cap, int nsplit,
@@ -297,14 +348,17 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     __shared__ int32_t s_slot[MOE_EP_MAX_WORLD];
     __shared__ int s_n;
     // Own routing (rank == nullptr, at most one tile of tokens): every
-    // block derives the destination masks of all T tokens and counts, per
-    // destination, the tokens before its own with one ballot per wave.
-    __shared__ uint64_t s_mask[kPackThreads];
-    __shared__ int32_t s_wcnt[kPackThreads / 64][MOE_EP_MAX_WORLD];
+    // block derives the destination masks of all T tokens; wave w keeps, per
+    // destination d, the ballot of its 64 tokens that go to d.
+    __shared__ uint64_t s_bits[kPackThreads / 64][MOE_EP_MAX_WORLD];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const bool own_route = rank == nullptr;
+
+    u32x4 pre[kPackUnroll];
+    int64_t p_mid = 0;
+    if (PF && blockIdx.x < T * nsplit) load_first_pass(P, blockIdx.x, nsplit, pre, p_mid);
 
     if (tile_cnt && blockIdx.x == 0 && tid < W)
         send_cnt[tid] = sum_tiles(tile_cnt, (T + kRouteTile - 1) / kRouteTile, W, tid);
@@ -312,31 +366,24 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     if (own_route) {
         uint64_t mask = 0;
         uint32_t bad = 0;
-        if (tid < T) {
-            const int32_t* row = ids + (int64_t)tid * K;
-#pragma unroll 8
-            for (int k = 0; k < K; ++k) {
-                const int32_t id = row[k];
-                if (id < 0) continue;
-                if (id >= E) { bad |= MOE_EP_ERR_ID_RANGE; continue; }
-                mask |= 1ull << (id / e_local);
-            }
-        }
-        s_mask[tid] = mask;
-        if (blockIdx.x == 0) {
-            report(err, bad);
+        if (tid < T) mask = token_dest_mask(ids + (int64_t)tid * K, K, E, e_local, bad);
+        if (blockIdx.x == 0) report(err, bad);
+        if (wave * 64 < T) {   // the waves that hold tokens
+            uint64_t mine = 0;
             for (int d = 0; d < W; ++d) {
                 const uint64_t bl = __ballot((mask >> d) & 1ull);
-                if (lane == 0) s_wcnt[wave][d] = __popcll(bl);
+                if (lane == d) mine = bl;
             }
+            if (lane < W) s_bits[wave][lane] = mine;
         }
         __syncthreads();
         if (blockIdx.x == 0 && tid < W) {
             int32_t c = 0;
-#pragma unroll
-            for (int w = 0; w < kPackThreads / 64; ++w) c += s_wcnt[w][tid];
+            for (int w = 0; w * 64 < T; ++w) c += __popcll(s_bits[w][tid]);
             send_cnt[tid] = c;
         }
+        // (a barrier here also keeps the compiler from carrying prologue
+        // values into the token loop, which costs registers)
         __syncthreads();
     }
 
@@ -347,13 +394,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
         // The first pass over the leading row does not depend on where the
         // token goes: its loads (and, for the quantised row, its codes) are
         // issued before the destinations are known, so their latency
-        // overlaps wave 0's slot and metadata work.
+        // overlaps wave 0's slot work. (PF: the first item's loads were
+        // issued before the routing.)
         int64_t q_lo = 0, q_hi = 0, q_mid = 0;
         int gv = 0;
         QuantPass qp;
         Fp4Pass qp4;
-        int64_t p_lo = 0, p_hi = 0, p_mid = 0;
-        u32x4 pre[kPackUnroll];
         if (QMODE != 0) {
             gv = QMODE == 2 ? 1 : Q.group >> 4;   // 16-column units per group
             const int64_t nvq = Q.H >> 4;
@@ -366,29 +412,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
                 if (QMODE == 2) quantize_pass_fp4(Q.src + t * Q.src_stride, q_lo, q_mid, qp4);
                 else quantize_pass(Q.src + t * Q.src_stride, q_lo, q_mid, gv, qp);
             }
-        } else if (MOE_EP_PACK_PREFETCH && P.n > 0) {
-            const int64_t nvec = P.row_bytes[0] >> 4;
-            const int64_t per = (nvec + nsplit - 1) / nsplit;
-            p_lo = part * per;
-            p_hi = p_lo + per < nvec ? p_lo + per : nvec;
-            p_mid = p_lo + kPackThreads * kPackUnroll < p_hi ? p_lo + kPackThreads * kPackUnroll
-                                                            : p_hi;
-            const uint8_t* src = P.src[0] + t * P.src_stride[0];
-#pragma unroll
-            for (int u = 0; u < kPackUnroll; ++u) {
-                const int64_t i = p_lo + u * kPackThreads + tid;
-                if (i < p_mid) pre[u] = ld_row<MOE_EP_PACK_NT>(src + i * 16);
-            }
         }
-
-        if (own_route) {
-            const uint64_t before = tid < t ? s_mask[tid] : 0;
-            for (int d = 0; d < W; ++d) {
-                const uint64_t bl = __ballot((before >> d) & 1ull);
-                if (lane == 0) s_wcnt[wave][d] = __popcll(bl);
-            }
-            __syncthreads();
-        }
+        // PF: the block's first item has its first pass in registers (with
+        // own routing every block has a single item)
+        const bool pf_item = PF && b == blockIdx.x;
 
         // Wave 0: the token's final slot per destination (lane d), and the
         // list of its destinations in LDS for the copy.
@@ -397,16 +424,22 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             const int d = tid;
             if (d < W) {
                 if (own_route) {
-                    if ((s_mask[t] >> d) & 1ull) {
-                        slot = 0;
-#pragma unroll
-                        for (int w = 0; w < kPackThreads / 64; ++w) slot += s_wcnt[w][d];
+                    // tokens before t that go to d: whole waves, then the
+                    // lanes below t's in its own wave
+                    const int tw = (int)(t >> 6);
+                    const int tb = (int)(t & 63);
+                    const uint64_t bits = s_bits[tw][d];
+                    if ((bits >> tb) & 1ull) {
+                        slot = __popcll(bits & ((1ull << tb) - 1ull));
+                        for (int w = 0; w < tw; ++w) slot += __popcll(s_bits[w][d]);
                     }
                 } else {
-                    slot = rank[d * T + t];
-                    if (slot >= 0)
-                        slot += tile_cnt ? sum_tiles(tile_cnt, t / kRouteTile, W, d)
-                                         : tile_off[(t / kRouteTile) * W + d];
+                    // the tile offset does not depend on the rank: both
+                    // loads are in flight together
+                    const int32_t r = rank[d * T + t];
+                    const int32_t off = tile_cnt ? sum_tiles(tile_cnt, t / kRouteTile, W, d)
+                                                 : tile_off[(t / kRouteTile) * W + d];
+                    slot = r >= 0 ? r + off : -1;
                 }
                 if (part == 0) token_slot[t * W + d] = slot;
             }
@@ -420,6 +453,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
         }
         __syncthreads();
         const int n = s_n;
+
 
         if (QMODE == 1) {
             if (q_lo < q_hi) store_quant_pass(Q, q_lo, q_mid, gv, qp, n, s_dest, s_slot);
@@ -452,8 +486,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
                 uint8_t* srow = Q.s + s_dest[tid] * Q.s_stride + (int64_t)s_slot[tid] * Q.s_pitch;
                 for (int64_t g = Q.n_scales; g < Q.s_pitch; ++g) srow[g] = 0;
             }
-        } else if (MOE_EP_PACK_PREFETCH && P.n > 0) {
+        } else if (pf_item) {
             const int64_t rb = P.row_bytes[0];
+            const int64_t nvec = rb >> 4;
+            const int64_t p_lo = part * ((nvec + nsplit - 1) / nsplit);
             for (int a = 0; a < n; ++a) {
                 uint8_t* dst = P.dst[0] + s_dest[a] * P.dst_stride[0] + (int64_t)s_slot[a] * rb;
 #pragma unroll
@@ -471,7 +507,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             const int64_t per = (nvec + nsplit - 1) / nsplit;
             int64_t v_lo = part * per;
             const int64_t v_hi = v_lo + per < nvec ? v_lo + per : nvec;
-            if (QMODE == 0 && MOE_EP_PACK_PREFETCH && p == 0) v_lo = p_mid;   // first pass done
+            if (pf_item && p == 0) v_lo = p_mid;   // first pass done
             const uint8_t* src = P.src[p] + t * P.src_stride[p];
             for (int64_t i0 = v_lo + tid; i0 < v_hi; i0 += kPackThreads * kPackUnroll) {
                 u32x4 v[kPackUnroll];
@@ -494,24 +530,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
         // Wave 0, after its share of the copy: the pick metadata of each
         // destination slot (block of part 0 only).
         if (tid < W && part == 0) {
-            const int d = tid;
             uint32_t bad = 0;
             if (slot >= 0) {
-                const int64_t meta = ((int64_t)d * cap + slot) * slots;
-                int j = 0;
-#pragma unroll 8
-                for (int k = 0; k < K; ++k) {
-                    const int32_t id = ids[t * K + k];
-                    if (id < 0 || id >= E || id / e_local != d) continue;
-                    if (j >= slots) { bad |= MOE_EP_ERR_PICKS; continue; }
-                    send_eloc[meta + j] = id - d * e_local;
-                    send_w[meta + j] = wts[t * K + k];
-                    ++j;
-                }
-                for (; j < slots; ++j) {
-                    send_eloc[meta + j] = -1;
-                    send_w[meta + j] = 0.0f;
-                }
+                const int64_t meta = ((int64_t)tid * cap + slot) * slots;
+                bad = write_pick_meta(ids, wts, t, K, E, e_local, tid, slots,
+                                      send_eloc + meta, send_w + meta);
             }
             report(err, bad);
         }
@@ -534,16 +557,21 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
     const int nsplit = row_split(T, max_vecs);
     const int64_t blocks = T * nsplit;
     const int64_t grid = blocks < 65536 ? blocks : 65536;
+    const bool pf = rank == nullptr && P.n > 0;
     if (quant && quant->mode == 2)
-        pack_copy_kernel<2><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
+        pack_copy_kernel<2, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
             tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, err);
     else if (quant)
-        pack_copy_kernel<1><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
+        pack_copy_kernel<1, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
             tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, err);
+    else if (pf)
+        pack_copy_kernel<0, true><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
+            ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
+            tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, err);
     else
-        pack_copy_kernel<0><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
+        pack_copy_kernel<0, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
             tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, err);
     return hipGetLastError();

@@ -35,16 +35,7 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
     // token lives on rank d. Negative ids are padding; ids >= E are dropped.
     uint64_t mask = 0;
     uint32_t bad = 0;
-    if (t < T) {
-        const int32_t* row = ids + t * K;
-#pragma unroll 8
-        for (int k = 0; k < K; ++k) {
-            const int32_t id = row[k];
-            if (id < 0) continue;
-            if (id >= E) { bad |= MOE_EP_ERR_ID_RANGE; continue; }
-            mask |= 1ull << (id / e_local);
-        }
-    }
+    if (t < T) mask = token_dest_mask(ids + t * K, K, E, e_local, bad);
     report(err, bad);
 
     for (int d = 0; d < W; ++d) {
