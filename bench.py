@@ -5,7 +5,10 @@ one MI355X.
 A step is one pass of the whole path over W logical ranks with synthetic,
 seeded inputs already resident in HBM: W dispatch packs, then for every
 destination the expert batch and the combine reduce, then W combine
-unpacks. `value` is tokens/s over all W*T tokens of a step; effective GB/s
+unpacks. The ranks are spread over --lanes HIP streams (default 4), so the
+kernels of one rank overlap those of another, as they would on W GPUs; each
+phase waits for the previous one on every stream. `value` is tokens/s over
+all W*T tokens of a step; effective GB/s
 uses the algorithmic byte model (what the method must read and write, from
 the run's actual counts):
 
@@ -147,6 +150,23 @@ def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None,
     return out
 
 
+# Device memory the lanes' expert-batch buffers may take together.
+LANE_MEMORY_BYTES = 96 << 30
+
+
+def lanes_that_fit(w, row_bytes, fp8_group, fp4, want: int) -> int:
+    """Lanes to use: at most `want` and W, and no more than fit their
+    [e_local, W*cap, row] expert-batch buffers in LANE_MEMORY_BYTES."""
+    from combine_topk_ids_dest_amd import binding
+    rows = list(row_bytes)
+    if fp4:
+        rows = [w.H // 2, binding.fp4_scale_pitch(w.H)] + rows[1:]
+    elif fp8_group:
+        rows = [w.H, 4 * binding.scale_pitch(w.H, fp8_group)] + rows[1:]
+    per_lane = w.e_local * w.W * w.cap * sum(rows)
+    return max(1, min(want, w.W, LANE_MEMORY_BYTES // max(per_lane, 1)))
+
+
 def cpu_baseline(w, srcs, pls, shares: int):
     """The CPU oracle, as it stands, timed on this host: `shares` logical-rank
     shares (pack of a source, batch and reduce of a destination, unpack of a
@@ -267,6 +287,11 @@ def main():
     ap.add_argument("--fp4", action="store_true",
                     help="quantize-on-pack: send the bf16 hidden row as 4-bit e2m1 "
                          "codes with one e4m3 scale per 16 columns")
+    ap.add_argument("--lanes", type=int, default=4,
+                    help="HIP streams the logical ranks are spread over, so one rank's "
+                         "kernels overlap another's (each lane holds its own workspace and "
+                         "expert-batch buffer; capped by LANE_MEMORY_BYTES; 1 with --graph); "
+                         "1 runs the ranks one after another")
     ap.add_argument("--fp8-group", type=int, default=None,
                     help="quantize-on-pack: send the bf16 hidden row as fp8 e4m3 "
                          "with one scale per this many columns")
@@ -302,8 +327,14 @@ def main():
     if args.fp4 and args.fp8_group:
         print("--fp4 and --fp8-group exclude each other", file=sys.stderr)
         sys.exit(2)
+    lanes = lanes_that_fit(w, row_bytes, args.fp8_group, args.fp4, args.lanes)
+    if args.graph and lanes > 1:
+        # the emulation captures one-lane steps only
+        log("[bench] --graph: the captured step runs on one lane")
+        lanes = 1
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
-                   quant_group=args.fp8_group, quant_fp4=args.fp4)
+                   quant_group=args.fp8_group, quant_fp4=args.fp4, lanes=lanes)
+    streams = [torch.cuda.Stream() for _ in range(lanes)] if lanes > 1 else None
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
     wl.expert_outputs_device(ep.Y, seed=1000 + w.wid)
@@ -313,24 +344,24 @@ def main():
 
     fused = args.fused_local
     for _ in range(args.warmup):
-        ep.step(fused_local=fused)
+        ep.step(fused_local=fused, streams=streams)
     torch.cuda.synchronize()
 
     # Timed region: K whole steps, nothing else enqueued between them.
     stream = torch.cuda.current_stream()
     def run_step():
-        ep.step(fused_local=fused)
+        ep.step(fused_local=fused, streams=streams)
 
     if args.graph:
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            ep.step(fused_local=fused)
+            ep.step(fused_local=fused, streams=streams)
         stream.wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph):
-            ep.step(fused_local=fused)
+            ep.step(fused_local=fused, streams=streams)
         torch.cuda.synchronize()
         graph.replay()
         run_step = graph.replay
@@ -344,9 +375,10 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # Per-call durations: K more steps with a pair of HIP events around every
-    # call, on the stream the library launches on (torch's current stream).
-    # The events add a few microseconds between calls, so these steps are
-    # timed separately from the region above.
+    # call, all on one stream, the one the library launches on (torch's
+    # current stream), one call after another whatever the lanes. The events
+    # add a few microseconds between calls, so these steps are timed
+    # separately from the region above.
     k_red, k_unp = ("reduce_peers", "unpack_fused") if fused else ("reduce", "unpack")
     kinds = (["pack"] * w.W + ["batch_plan", "batch_copy", k_red] * w.W
              + [k_unp] * w.W)
@@ -471,6 +503,7 @@ def main():
                                 else "fp4_e2m1_e4m3_g16" if args.fp4 else "as_given"),
             "combine_accumulation": "fp32",
             "launch": "hip_graph" if args.graph else "eager",
+            "lanes": lanes,
             "local_slice_combine": "fused" if fused else "reduce_then_unpack",
             "parallelism": f"1 GPU, {w.W} logical expert-parallel ranks",
         },

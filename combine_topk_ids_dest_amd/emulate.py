@@ -12,12 +12,20 @@ Device layout (all dense, rank-major):
   send_cnt        [W_src, W_dst]           int32
   send_eloc/_w    [W_src, W_dst, cap, slots]
   token_slot      [W_src, T, W_dst]        int32 (unpack context)
-  b[p]            [e_local, W*cap, row_p]  one buffer, reused per destination
+  b[p]            [e_local, W*cap, row_p]  one buffer per lane, reused by the
+                                           destinations of that lane
   expert_num_tokens [W_dst, e_local]
   recv_row        [W_dst, W_src, cap, slots] (reduce context)
   Y               [e_local, W*cap, H]      expert outputs, reused per destination
   ret             [W_dst, W_src, cap, H]
   out             [W_src, T, H]
+
+Lanes: rank i uses lane i % lanes for the two buffers that ranks share (the
+workspace and b). With several lanes, step(streams=...) runs the ranks of
+each lane on its own HIP stream, so the kernels of different ranks may
+overlap (on W GPUs the ranks run at the same time anyway); the three phases
+(packs, batch + reduce, unpacks) are joined across the streams with events,
+since each phase reads what every rank wrote in the one before.
 """
 from __future__ import annotations
 
@@ -32,7 +40,8 @@ class LogicalEP:
     def __init__(self, T: int, H: int, E: int, K: int, W: int, cap: int,
                  row_bytes: Sequence[int], combine_dtype=torch.bfloat16,
                  device="cuda", fill: Optional[int] = None,
-                 quant_group: Optional[int] = None, quant_fp4: bool = False):
+                 quant_group: Optional[int] = None, quant_fp4: bool = False,
+                 lanes: int = 1):
         """row_bytes: bytes per row of each source payload (payload 0 is the
         bf16 hidden row that the combine returns). fill: byte to pre-fill
         every buffer with (e.g. 0xFF, NaN in bf16/fp32) so unwritten tails
@@ -41,7 +50,11 @@ class LogicalEP:
         quant_group columns (moe_ep_dispatch_pack_fp8), and the codes and
         the scales travel as the first two payloads instead of it.
         quant_fp4: the same with 4-bit E2M1 codes and E4M3 scales per 16
-        columns (moe_ep_dispatch_pack_fp4)."""
+        columns (moe_ep_dispatch_pack_fp4). lanes: copies of the shared
+        workspace and b buffers (see the module docstring)."""
+        if lanes < 1 or lanes > W:
+            raise ValueError("lanes must be in [1, W]")
+        self.lanes = lanes
         self.T, self.H, self.E, self.K, self.W, self.cap = T, H, E, K, W, cap
         self.e_local = E // W
         self.cap_, self.slots, self.expert_cap = B.moe_ep_capacities(K, E, W, cap)
@@ -80,7 +93,9 @@ class LogicalEP:
         self.send_eloc = alloc((W_, W_, cap, sl), torch.int32)
         self.send_w = alloc((W_, W_, cap, sl), torch.float32)
         self.token_slot = alloc((W_, T, W_), torch.int32)
-        self.b = [alloc((el, self.expert_cap, rb), torch.uint8) for rb in self.send_row_bytes]
+        self.b_lanes = [[alloc((el, self.expert_cap, rb), torch.uint8)
+                         for rb in self.send_row_bytes] for _ in range(lanes)]
+        self.b = self.b_lanes[0]
         self.expert_num_tokens = alloc((W_, el), torch.int32)
         self.recv_row = alloc((W_, W_, cap, sl), torch.int32)
         self.Y = alloc((el, self.expert_cap, H), combine_dtype)
@@ -88,7 +103,9 @@ class LogicalEP:
         self.out = alloc((W_, T, H), combine_dtype)
         self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
         ws = B.moe_ep_workspace_bytes(cap, K, E, W, cap)
-        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+        self.workspaces = [torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+                           for _ in range(lanes)]
+        self.workspace = self.workspaces[0]
         self._calls = {}
 
     # -- inputs ---------------------------------------------------------
@@ -118,7 +135,7 @@ class LogicalEP:
                 self.src[0][s].view(torch.bfloat16), self.send[0][s], self.send[1][s],
                 [(self.src[p][s], self.send[p + 1][s]) for p in range(1, len(self.src))],
                 self.send_cnt[s], self.send_eloc[s], self.send_w[s],
-                self.token_slot[s], self.err, self.workspace)
+                self.token_slot[s], self.err, self.workspaces[s % self.lanes])
         if self.quant_group is not None:
             G = B.scale_pitch(self.H, self.quant_group)
             return B.prepare_dispatch_pack_fp8(
@@ -127,33 +144,35 @@ class LogicalEP:
                 self.send[0][s], self.send[1][s].view(torch.float32).view(self.W, self.cap, G),
                 [(self.src[p][s], self.send[p + 1][s]) for p in range(1, len(self.src))],
                 self.send_cnt[s], self.send_eloc[s], self.send_w[s],
-                self.token_slot[s], self.err, self.workspace)
+                self.token_slot[s], self.err, self.workspaces[s % self.lanes])
         return B.prepare_dispatch_pack(
             self.ids[s], self.wts[s], self.E, self.W, self.cap,
             [(self.src[p][s], self.send[p][s]) for p in range(len(self.src))],
             self.send_cnt[s], self.send_eloc[s], self.send_w[s],
-            self.token_slot[s], self.err, self.workspace)
+            self.token_slot[s], self.err, self.workspaces[s % self.lanes])
 
     def _prep_batch(self, r: int):
         return B.prepare_expert_batch(
             self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
             self.K, self.cap,
-            [(self.send[p][:, r], self.b[p]) for p in range(len(self.send))],
+            [(self.send[p][:, r], self.b_lanes[r % self.lanes][p])
+             for p in range(len(self.send))],
             self.expert_num_tokens[r], self.recv_row[r], self.err,
-            self.workspace)
+            self.workspaces[r % self.lanes])
 
     def _prep_batch_plan(self, r: int):
         return B.prepare_expert_batch_plan(
             self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
             self.K, self.cap, self.expert_num_tokens[r], self.recv_row[r],
-            self.err, self.workspace)
+            self.err, self.workspaces[r % self.lanes])
 
     def _prep_batch_copy(self, r: int):
         return B.prepare_expert_batch_copy(
             self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
             self.K, self.cap,
-            [(self.send[p][:, r], self.b[p]) for p in range(len(self.send))],
-            self.recv_row[r], self.err, self.workspace)
+            [(self.send[p][:, r], self.b_lanes[r % self.lanes][p])
+             for p in range(len(self.send))],
+            self.recv_row[r], self.err, self.workspaces[r % self.lanes])
 
     def _prep_reduce(self, r: int):
         return B.prepare_combine_reduce(
@@ -206,22 +225,63 @@ class LogicalEP:
         else:
             self._prep_unpack_fused(s, Y)(stream)
 
-    def step(self, stream=None, fused_local=False):
+    def step(self, stream=None, fused_local=False, streams=None):
         """One pass of the whole path over all W logical ranks: W packs,
         then batch + reduce per destination (reusing b and Y), then W
         unpacks. fused_local: each rank's local slice is combined by the
         fused unpack (the shared Y stands in for every rank's own expert
-        output)."""
+        output). streams: one HIP stream per lane; rank i's calls go to
+        streams[i % lanes], and each phase starts on every stream only
+        after the previous phase has ended on all of them. The step is
+        ordered after the work already on `stream` (default: the current
+        stream), and that stream waits for the whole step. A step over
+        several lanes runs eagerly only (not under HIP graph capture)."""
+        if streams is None:
+            lane_of = [stream] * self.W
+        else:
+            if len(streams) != self.lanes:
+                raise ValueError("one stream per lane")
+            if torch.cuda.is_current_stream_capturing():
+                # capturing the fork and joins ended in a crash of the
+                # process at the end of the capture; not supported
+                raise RuntimeError("a step over several lanes is not captured in a "
+                                   "HIP graph: capture a one-lane step (streams=None)")
+            lane_of = [streams[i % self.lanes] for i in range(self.W)]
+            main = stream if stream is not None else torch.cuda.current_stream()
+            # the lanes start after the work on `main`, which itself follows
+            # the lanes' earlier steps (it waited for them at their end)
+            for st in streams:
+                st.wait_stream(main)
         for s in range(self.W):
-            self.pack(s, stream)
+            self.pack(s, lane_of[s])
+        if streams is not None:
+            self._join(streams)
         for r in range(self.W):
-            self.batch(r, stream)
+            self.batch(r, lane_of[r])
             if fused_local:
-                self.reduce_peers(r, stream)
+                self.reduce_peers(r, lane_of[r])
             else:
-                self.reduce(r, stream)
+                self.reduce(r, lane_of[r])
+        if streams is not None:
+            self._join(streams)
         for s in range(self.W):
             if fused_local:
-                self.unpack_fused(s, stream)
+                self.unpack_fused(s, lane_of[s])
             else:
-                self.unpack(s, stream)
+                self.unpack(s, lane_of[s])
+        if streams is not None:
+            for st in streams:
+                main.wait_stream(st)
+
+    @staticmethod
+    def _join(streams):
+        """Every stream in `streams` waits for the work enqueued so far on
+        all of them."""
+        evs = []
+        for st in streams:
+            ev = torch.cuda.Event()
+            ev.record(st)
+            evs.append(ev)
+        for st in streams:
+            for ev in evs:
+                st.wait_event(ev)
