@@ -5,9 +5,9 @@ one MI355X.
 A step is one pass of the whole path over W logical ranks with synthetic,
 seeded inputs already resident in HBM: W dispatch packs, then for every
 destination the expert batch and the combine reduce, then W combine
-unpacks. The ranks are spread over --lanes HIP streams (default 4), so the
-kernels of one rank overlap those of another, as they would on W GPUs; each
-phase waits for the previous one on every stream. `value` is tokens/s over
+unpacks. The ranks are spread over --lanes HIP streams (4 unless a step is
+tiny), so the kernels of one rank overlap those of another, as they would on
+W GPUs; each phase waits for the previous one on every stream. `value` is tokens/s over
 all W*T tokens of a step; effective GB/s
 uses the algorithmic byte model (what the method must read and write, from
 the run's actual counts):
@@ -152,6 +152,8 @@ def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None,
 
 # Device memory the lanes' expert-batch buffers may take together.
 LANE_MEMORY_BYTES = 96 << 30
+AUTO_LANES = 4
+AUTO_LANES_MIN_BYTES = 16 << 20
 
 
 def lanes_that_fit(w, row_bytes, fp8_group, fp4, want: int) -> int:
@@ -287,11 +289,13 @@ def main():
     ap.add_argument("--fp4", action="store_true",
                     help="quantize-on-pack: send the bf16 hidden row as 4-bit e2m1 "
                          "codes with one e4m3 scale per 16 columns")
-    ap.add_argument("--lanes", type=int, default=4,
+    ap.add_argument("--lanes", default="auto",
                     help="HIP streams the logical ranks are spread over, so one rank's "
                          "kernels overlap another's (each lane holds its own workspace and "
                          "expert-batch buffer; capped by LANE_MEMORY_BYTES; 1 with --graph); "
-                         "1 runs the ranks one after another")
+                         "1 runs the ranks one after another; auto: AUTO_LANES, or 1 when a "
+                         "step's source rows are under AUTO_LANES_MIN_BYTES (the joins "
+                         "between streams then cost more than the overlap gains)")
     ap.add_argument("--fp8-group", type=int, default=None,
                     help="quantize-on-pack: send the bf16 hidden row as fp8 e4m3 "
                          "with one scale per this many columns")
@@ -327,7 +331,11 @@ def main():
     if args.fp4 and args.fp8_group:
         print("--fp4 and --fp8-group exclude each other", file=sys.stderr)
         sys.exit(2)
-    lanes = lanes_that_fit(w, row_bytes, args.fp8_group, args.fp4, args.lanes)
+    if args.lanes == "auto":
+        want = AUTO_LANES if w.W * w.T * sum(row_bytes) >= AUTO_LANES_MIN_BYTES else 1
+    else:
+        want = int(args.lanes)
+    lanes = lanes_that_fit(w, row_bytes, args.fp8_group, args.fp4, want)
     if args.graph and lanes > 1:
         # the emulation captures one-lane steps only
         log("[bench] --graph: the captured step runs on one lane")

@@ -107,6 +107,7 @@ class LogicalEP:
                            for _ in range(lanes)]
         self.workspace = self.workspaces[0]
         self._calls = {}
+        self._events = {}
 
     # -- inputs ---------------------------------------------------------
     def set_source(self, s: int, ids, wts, payload_rows: Sequence):
@@ -250,12 +251,14 @@ class LogicalEP:
             main = stream if stream is not None else torch.cuda.current_stream()
             # the lanes start after the work on `main`, which itself follows
             # the lanes' earlier steps (it waited for them at their end)
+            fork = self._lane_events("fork", 1)[0]
+            fork.record(main)
             for st in streams:
-                st.wait_stream(main)
+                st.wait_event(fork)
         for s in range(self.W):
             self.pack(s, lane_of[s])
         if streams is not None:
-            self._join(streams)
+            self._join(streams, 0)
         for r in range(self.W):
             self.batch(r, lane_of[r])
             if fused_local:
@@ -263,25 +266,31 @@ class LogicalEP:
             else:
                 self.reduce(r, lane_of[r])
         if streams is not None:
-            self._join(streams)
+            self._join(streams, 1)
         for s in range(self.W):
             if fused_local:
                 self.unpack_fused(s, lane_of[s])
             else:
                 self.unpack(s, lane_of[s])
         if streams is not None:
-            for st in streams:
-                main.wait_stream(st)
+            for st, ev in zip(streams, self._lane_events("end", len(streams))):
+                ev.record(st)
+                main.wait_event(ev)
 
-    @staticmethod
-    def _join(streams):
+    def _lane_events(self, key, n: int):
+        evs = self._events.get(key)
+        if evs is None:
+            evs = self._events[key] = [torch.cuda.Event() for _ in range(n)]
+        return evs
+
+    def _join(self, streams, phase: int):
         """Every stream in `streams` waits for the work enqueued so far on
-        all of them."""
-        evs = []
-        for st in streams:
-            ev = torch.cuda.Event()
+        the others (one event per phase and lane, made once and recorded
+        again at every step)."""
+        evs = self._lane_events(phase, len(streams))
+        for st, ev in zip(streams, evs):
             ev.record(st)
-            evs.append(ev)
-        for st in streams:
-            for ev in evs:
-                st.wait_event(ev)
+        for i, st in enumerate(streams):
+            for j, ev in enumerate(evs):
+                if i != j:
+                    st.wait_event(ev)
