@@ -169,6 +169,12 @@ def lanes_that_fit(w, row_bytes, fp8_group, fp4, want: int) -> int:
     return max(1, min(want, w.W, LANE_MEMORY_BYTES // max(per_lane, 1)))
 
 
+def auto_lanes(w, row_bytes, fp8_group=None, fp4=False) -> int:
+    """The lanes of --lanes auto."""
+    want = AUTO_LANES if w.W * w.T * sum(row_bytes) >= AUTO_LANES_MIN_BYTES else 1
+    return lanes_that_fit(w, row_bytes, fp8_group, fp4, want)
+
+
 def cpu_baseline(w, srcs, pls, shares: int):
     """The CPU oracle, as it stands, timed on this host: `shares` logical-rank
     shares (pack of a source, batch and reduce of a destination, unpack of a
@@ -332,10 +338,9 @@ def main():
         print("--fp4 and --fp8-group exclude each other", file=sys.stderr)
         sys.exit(2)
     if args.lanes == "auto":
-        want = AUTO_LANES if w.W * w.T * sum(row_bytes) >= AUTO_LANES_MIN_BYTES else 1
+        lanes = auto_lanes(w, row_bytes, args.fp8_group, args.fp4)
     else:
-        want = int(args.lanes)
-    lanes = lanes_that_fit(w, row_bytes, args.fp8_group, args.fp4, want)
+        lanes = lanes_that_fit(w, row_bytes, args.fp8_group, args.fp4, int(args.lanes))
     if args.graph and lanes > 1:
         # the emulation captures one-lane steps only
         log("[bench] --graph: the captured step runs on one lane")

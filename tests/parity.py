@@ -409,3 +409,46 @@ def run_fullsize(w: wl.Workload, seed: int = 0, fp8_group=None, fp4=False):
     assert int(ep.err.item()) == 0
     say(f"[fullsize] {w.name}: ok")
     return ep
+
+
+STEP_OUTPUTS = ("send_cnt", "token_slot", "send_eloc", "send_w", "expert_num_tokens",
+                "recv_row", "ret", "out")
+
+
+def snapshot_step(ep):
+    """Device copies of every output of a step, and the valid rows of the
+    last destination's expert batch."""
+    snap = {n: getattr(ep, n).clone() for n in STEP_OUTPUTS}
+    snap["send"] = [x.clone() for x in ep.send]
+    r = ep.W - 1
+    ent = ep.expert_num_tokens[r].tolist()
+    snap["b_last"] = [torch.cat([b[e, :ent[e]] for e in range(ep.e_local)])
+                      for b in ep.b_lanes[r % ep.lanes]]
+    return snap
+
+
+def check_lanes_step(w: wl.Workload, ref, lanes: int, seed: int = 0):
+    """The whole step as bench.py times it, with the ranks over `lanes` HIP
+    streams, on the inputs of run_fullsize: every output byte equals the
+    one-stream outputs in `ref` (snapshot_step of the path that run_fullsize
+    checked against the oracle)."""
+    say(f"[fullsize] {w.name}: whole step over {lanes} lanes")
+    srcs = [wl.routing(w, s, seed) for s in range(w.W)]
+    pls = [wl.payloads(w, s, seed, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
+    ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, [p.shape[1] for p in pls[0]],
+                   torch.bfloat16, torch.device("cuda"), fill=SENTINEL, lanes=lanes)
+    for s in range(w.W):
+        ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
+    wl.expert_outputs_device(ep.Y, seed=2000 + w.wid)
+    streams = [torch.cuda.Stream() for _ in range(lanes)]
+    ep.step(streams=streams)
+    torch.cuda.synchronize()
+    got = snapshot_step(ep)
+    for n in STEP_OUTPUTS:
+        assert torch.equal(got[n].view(torch.uint8), ref[n].view(torch.uint8)), f"lanes: {n}"
+    for p, (a, b) in enumerate(zip(got["send"], ref["send"])):
+        assert torch.equal(a, b), f"lanes: send payload {p}"
+    for p, (a, b) in enumerate(zip(got["b_last"], ref["b_last"])):
+        assert torch.equal(a, b), f"lanes: batch of the last destination, payload {p}"
+    assert int(ep.err.item()) == 0
+    say(f"[fullsize] {w.name}: {lanes} lanes ok")

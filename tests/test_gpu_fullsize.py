@@ -1,5 +1,6 @@
 """GPU parity at the full sizes of the five workloads, in the launch
-configuration that bench.py times (LogicalEP calls on W logical ranks).
+configuration that bench.py times (LogicalEP calls on W logical ranks, and
+the whole step over the HIP streams bench.py spreads the ranks over).
 Integer outputs are compared whole; every valid payload byte is compared on
 the device with the source row the oracle's slot and row maps name; the
 combine is compared element by element on column windows the oracle
@@ -7,8 +8,9 @@ computes exactly."""
 import pytest
 import torch
 
+import bench
 import workloads as wl
-from parity import SENTINEL, run_fullsize, say
+from parity import SENTINEL, check_lanes_step, run_fullsize, say, snapshot_step
 
 pytestmark = pytest.mark.gpu
 
@@ -18,7 +20,13 @@ pytestmark = pytest.mark.gpu
 def test_fullsize(wid):
     w = wl.WORKLOADS[wid]
     say(f"[fullsize] start {w.name}")
-    run_fullsize(w)
+    ep = run_fullsize(w)
+    lanes = bench.auto_lanes(w, ep.row_bytes)
+    if lanes > 1:
+        ref = snapshot_step(ep)
+        del ep
+        torch.cuda.empty_cache()
+        check_lanes_step(w, ref, lanes)
 
 
 @pytest.mark.timeout(600)
