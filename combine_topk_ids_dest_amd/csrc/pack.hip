@@ -27,6 +27,8 @@ namespace moe_ep {
 #endif
 constexpr int kPackThreads = MOE_EP_PACK_THREADS;
 constexpr int kPackUnroll = MOE_EP_PACK_UNROLL;
+// Leading rows above this many 16-byte vectors load their first pass early.
+constexpr int64_t kPackPrefetchVecs = 512;
 static_assert(kPackThreads >= kRouteTile, "own routing holds one tile of masks");
 
 // Sum of tile_cnt[j][d] over tiles j < tiles (loads issued 8 at a time).
@@ -332,9 +334,9 @@ __device__ __forceinline__ uint32_t write_pick_meta(const int32_t* __restrict__ 
 }
 
 // QMODE 0: plain rows; 1: payload 0 quantised to fp8; 2: to fp4.
-// PF (plain rows with own routing only): the first pass of the leading row
-// of the block's first item is loaded before the routing, so its latency
-// overlaps it.
+// PF (plain rows): the first pass of the leading row of the block's first
+// item is loaded before the routing and the slot planning, so its latency
+// overlaps them.
 template <int QMODE, bool PF>
 __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t T,
@@ -557,7 +559,9 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
     const int nsplit = row_split(T, max_vecs);
     const int64_t blocks = T * nsplit;
     const int64_t grid = blocks < 65536 ? blocks : 65536;
-    const bool pf = rank == nullptr && P.n > 0;
+    // the early first pass pays with its own routing (short kernels) and
+    // for leading rows wider than 8 KiB; 8 KiB rows measured slower with it
+    const bool pf = P.n > 0 && (rank == nullptr || P.row_bytes[0] / 16 > kPackPrefetchVecs);
     if (quant && quant->mode == 2)
         pack_copy_kernel<2, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
