@@ -1,7 +1,8 @@
 """Host-side logic without a GPU: the binding's layout checks (no library
 call is made; CPU tensors only stand in for shapes and strides), the
-benchmark's algorithmic byte model on a hand-counted case, and the rule
-that a counter summary taken on other kernel sources is not used."""
+benchmark's algorithmic byte model on a hand-counted case, the rule that a
+counter summary taken on other kernel sources is not used, and the lanes
+the benchmark picks per workload."""
 import os
 import shutil
 
@@ -77,3 +78,22 @@ def test_counter_summary_of_other_sources_is_ignored(tmp_path, monkeypatch):
         f.write("\n// changed\n")
     assert bench.read_traffic(kern, "w") is None         # the kernel changed since
     assert bench.read_traffic(kern, "other") is None     # no summary at all
+
+
+def test_auto_lanes_per_workload():
+    """--lanes auto: 4 lanes, 1 for a tiny step, and no more lanes than
+    there are ranks or than fit the lanes' expert-batch buffers in
+    LANE_MEMORY_BYTES (the multi-payload rows are 21,792 B)."""
+    W = wl.WORKLOADS
+    assert bench.auto_lanes(W[1], [2 * W[1].H]) == 1
+    assert bench.auto_lanes(W[2], [2 * W[2].H]) == 4
+    assert bench.auto_lanes(W[3], [2 * W[3].H]) == 4
+    assert bench.auto_lanes(W[4], [2 * W[4].H]) == 4
+    rows5 = [2 * W[5].H, W[5].H, 4 * 56, 32, 32]
+    per_lane = W[5].e_local * W[5].W * W[5].cap * sum(rows5)
+    assert bench.auto_lanes(W[5], rows5) == bench.LANE_MEMORY_BYTES // per_lane == 2
+    # quantised rows are smaller, so more lanes fit
+    assert bench.auto_lanes(W[5], rows5, fp8_group=128) == 3
+    assert bench.auto_lanes(W[5], rows5, fp4=True) == 4
+    # never more lanes than ranks
+    assert bench.lanes_that_fit(W[1], [2 * W[1].H], None, False, 16) == W[1].W
