@@ -43,6 +43,10 @@ CASES = {
     "max_e_local": W1.scaled(W=1, E=1024, K=8, T=300, cap=300, H=64),
     # ... and a wide row (32 KiB of bf16) through every pass of every kernel
     "wide_row": W1.scaled(W=4, E=16, K=4, T=40, cap=48, H=16384),
+    # enough tokens that the unpack covers whole rows in one block: rows of
+    # 288 vectors in bf16, 576 in fp32 (above the 512 that switch the
+    # combine kernels to 4 vectors per lane)
+    "whole_row_unpack": W1.scaled(W=4, E=16, K=4, T=2100, cap=2100, H=2304),
 }
 
 
@@ -53,7 +57,8 @@ def test_parity(name):
     run_full_parity(w, salt=3)
 
 
-@pytest.mark.parametrize("name", ["tiny", "dsv3_small", "mixtral_small"])
+@pytest.mark.parametrize("name", ["tiny", "dsv3_small", "mixtral_small", "wide_row",
+                                  "whole_row_unpack"])
 def test_parity_fp32_combine(name):
     w = CASES[name]
     say(f"[parity fp32] {name}")
@@ -168,7 +173,8 @@ def test_parity_fused_local_combine(name):
 
 
 @pytest.mark.parametrize("name,f32", [("dsv3_small", False), ("mixtral_small", False),
-                                      ("tiny", True)])
+                                      ("tiny", True), ("wide_row", True),
+                                      ("whole_row_unpack", True)])
 def test_fused_local_combine_is_bit_identical_to_unfused(name, f32):
     say(f"[fused == unfused] {name} f32={f32}")
     ep1, _ = run_full_parity(CASES[name], salt=29, f32=f32)
