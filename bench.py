@@ -288,7 +288,8 @@ def main():
                     help="logical-rank shares the CPU oracle is timed on")
     ap.add_argument("--probe", choices=["copy"], default=None)
     ap.add_argument("--graph", action="store_true",
-                    help="capture one step in a HIP graph and time its replays")
+                    help="capture the step in HIP graphs (one per phase and lane when the "
+                         "ranks are spread over several lanes) and time their replays")
     ap.add_argument("--fused-local", action="store_true",
                     help="combine each rank's local slice with the fused unpack "
                          "(moe_ep_combine_reduce_peers + moe_ep_combine_unpack_fused)")
@@ -298,7 +299,8 @@ def main():
     ap.add_argument("--lanes", default="auto",
                     help="HIP streams the logical ranks are spread over, so one rank's "
                          "kernels overlap another's (each lane holds its own workspace and "
-                         "expert-batch buffer; capped by LANE_MEMORY_BYTES; 1 with --graph); "
+                         "expert-batch buffer; capped by LANE_MEMORY_BYTES; with --graph one "
+                         "graph per phase and lane); "
                          "1 runs the ranks one after another; auto: AUTO_LANES, or 1 when a "
                          "step's source rows are under AUTO_LANES_MIN_BYTES (the joins "
                          "between streams then cost more than the overlap gains)")
@@ -341,10 +343,6 @@ def main():
         lanes = auto_lanes(w, row_bytes, args.fp8_group, args.fp4)
     else:
         lanes = lanes_that_fit(w, row_bytes, args.fp8_group, args.fp4, int(args.lanes))
-    if args.graph and lanes > 1:
-        # the emulation captures one-lane steps only
-        log("[bench] --graph: the captured step runs on one lane")
-        lanes = 1
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
                    quant_group=args.fp8_group, quant_fp4=args.fp4, lanes=lanes)
     streams = [torch.cuda.Stream() for _ in range(lanes)] if lanes > 1 else None
@@ -365,7 +363,12 @@ def main():
     def run_step():
         ep.step(fused_local=fused, streams=streams)
 
-    if args.graph:
+    if args.graph and lanes > 1:
+        # one graph per (phase, lane), replayed on the lanes' streams
+        ep.capture_lane_graphs(fused_local=fused)
+        ep.step_graphs(streams)
+        run_step = lambda: ep.step_graphs(streams)
+    elif args.graph:
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)

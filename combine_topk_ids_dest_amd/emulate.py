@@ -277,6 +277,67 @@ class LogicalEP:
                 ev.record(st)
                 main.wait_event(ev)
 
+    # -- the step as one HIP graph per (phase, lane) -------------------------
+    # Every lane's calls of a phase are captured on one stream (a plain
+    # single-stream capture); a step then replays the graphs on the lanes'
+    # streams with the same event joins as step(streams=...), so the host
+    # enqueues 3 x lanes graph launches instead of one launch per call.
+    _PHASES = 3
+
+    def _phase_calls(self, phase: int, lane: int, fused_local: bool):
+        for i in range(lane, self.W, self.lanes):
+            if phase == 0:
+                self.pack(i)
+            elif phase == 1:
+                self.batch(i)
+                if fused_local:
+                    self.reduce_peers(i)
+                else:
+                    self.reduce(i)
+            elif fused_local:
+                self.unpack_fused(i)
+            else:
+                self.unpack(i)
+
+    def capture_lane_graphs(self, fused_local=False):
+        """Captures the lane graphs (after one eager step, so that every call
+        is marshalled). Replay them with step_graphs."""
+        self.step(fused_local=fused_local)
+        torch.cuda.synchronize()
+        graphs = []
+        for phase in range(self._PHASES):
+            row = []
+            for lane in range(self.lanes):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    self._phase_calls(phase, lane, fused_local)
+                row.append(g)
+            graphs.append(row)
+        torch.cuda.synchronize()
+        self._lane_graphs = graphs
+
+    def step_graphs(self, streams, stream=None):
+        """One step from the lane graphs: graph (phase, lane) replays on
+        streams[lane]; the phases are joined across the streams as in step.
+        Ordered after the work on `stream` (default: the current stream),
+        which waits for the whole step."""
+        if len(streams) != self.lanes:
+            raise ValueError("one stream per lane")
+        main = stream if stream is not None else torch.cuda.current_stream()
+        fork = self._lane_events("fork", 1)[0]
+        fork.record(main)
+        for st in streams:
+            st.wait_event(fork)
+        for phase, row in enumerate(self._lane_graphs):
+            if phase > 0:
+                self._join(streams, phase - 1)
+            for st, g in zip(streams, row):
+                with torch.cuda.stream(st):
+                    g.replay()
+        for st, ev in zip(streams, self._lane_events("end", len(streams))):
+            ev.record(st)
+            main.wait_event(ev)
+
     def _lane_events(self, key, n: int):
         evs = self._events.get(key)
         if evs is None:

@@ -1,8 +1,10 @@
 """The emulated step with the logical ranks spread over several HIP streams
 (lanes, each with its own workspace and expert-batch buffer) writes the same
-bytes as the one-stream step. Capturing such a step in a HIP graph crashed
-the process when the capture ended; that case is switched off (the step
-raises under capture) and its test is skipped."""
+bytes as the one-stream step, eagerly and from one HIP graph per phase and
+lane (each captured on a single stream) replayed on the lanes' streams.
+Capturing a whole step over several streams in one graph crashed the
+process when the capture ended; that case is switched off (the step raises
+under capture) and its test is skipped."""
 import pytest
 import torch
 
@@ -73,6 +75,38 @@ def test_lanes_match_one_stream(wid, scale, lanes, mode, fused):
     torch.cuda.synchronize()
     _same(ref, _outputs(ep), "eager")
     _same(ref_b, _last_batch(ep), "eager batch")
+    assert int(ep.err.item()) == 0
+
+
+@pytest.mark.parametrize("wid,scale,lanes,mode,fused", CASES)
+def test_lane_graphs_match_one_stream(wid, scale, lanes, mode, fused):
+    w = wl.WORKLOADS[wid] if scale is None else wl.WORKLOADS[wid].scaled(**scale)
+    say(f"[lane graphs] {w.name} T={w.T} W={w.W} lanes={lanes} {mode} fused={fused}")
+    one = _setup(w, 3, 1, **mode)
+    one.step(fused_local=fused)
+    torch.cuda.synchronize()
+    ref, ref_b = _outputs(one), _last_batch(one)
+    del one
+
+    ep = _setup(w, 3, lanes, **mode)
+    streams = [torch.cuda.Stream() for _ in range(lanes)]
+    ep.capture_lane_graphs(fused_local=fused)
+    for rep in range(3):
+        # eager work between replays: scribble over what the step writes
+        ep.out.view(torch.uint8).fill_(0xAB)
+        ep.ret.view(torch.uint8).fill_(0xCD)
+        ep.token_slot.fill_(-9)
+        ep.send_cnt.fill_(-9)
+        ep.expert_num_tokens.fill_(-9)
+        torch.cuda.synchronize()
+        ep.step_graphs(streams)
+        torch.cuda.synchronize()
+        got = _outputs(ep)
+        _same([x for i, x in enumerate(ref) if i != 6],
+              [x for i, x in enumerate(got) if i != 6], f"replay {rep}")
+        valid = _valid_ret_rows(ep, fused)
+        assert torch.equal(ref[6].view(torch.uint8)[valid], got[6].view(torch.uint8)[valid])
+        _same(ref_b, _last_batch(ep), f"replay {rep} batch")
     assert int(ep.err.item()) == 0
 
 
