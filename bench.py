@@ -36,6 +36,7 @@ the same session as a second roofline.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -304,6 +305,9 @@ def main():
                          "1 runs the ranks one after another; auto: AUTO_LANES, or 1 when a "
                          "step's source rows are under AUTO_LANES_MIN_BYTES (the joins "
                          "between streams then cost more than the overlap gains)")
+    ap.add_argument("--no-contiguous", action="store_true",
+                    help="allocate every buffer from torch's caching allocator instead of "
+                         "physically contiguous blocks for the large ones")
     ap.add_argument("--fp8-group", type=int, default=None,
                     help="quantize-on-pack: send the bf16 hidden row as fp8 e4m3 "
                          "with one scale per this many columns")
@@ -344,7 +348,8 @@ def main():
     else:
         lanes = lanes_that_fit(w, row_bytes, args.fp8_group, args.fp4, int(args.lanes))
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
-                   quant_group=args.fp8_group, quant_fp4=args.fp4, lanes=lanes)
+                   quant_group=args.fp8_group, quant_fp4=args.fp4, lanes=lanes,
+                   contiguous=not args.no_contiguous)
     streams = [torch.cuda.Stream() for _ in range(lanes)] if lanes > 1 else None
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
@@ -520,6 +525,8 @@ def main():
             "combine_accumulation": "fp32",
             "launch": "hip_graph" if args.graph else "eager",
             "lanes": lanes,
+            "large_buffers": ("physically_contiguous" if ep.contiguous_bytes
+                              else "caching_allocator"),
             "local_slice_combine": "fused" if fused else "reduce_then_unpack",
             "parallelism": f"1 GPU, {w.W} logical expert-parallel ranks",
         },
@@ -546,6 +553,7 @@ def main():
 
     if not args.no_cpu_baseline:
         del ep
+        gc.collect()
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(w, srcs, pls, args.cpu_shares)
     print(json.dumps(result), flush=True)

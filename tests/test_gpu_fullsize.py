@@ -5,6 +5,8 @@ Integer outputs are compared whole; every valid payload byte is compared on
 the device with the source row the oracle's slot and row maps name; the
 combine is compared element by element on column windows the oracle
 computes exactly."""
+import gc
+
 import pytest
 import torch
 
@@ -25,6 +27,7 @@ def test_fullsize(wid):
     if lanes > 1:
         ref = snapshot_step(ep)
         del ep
+        gc.collect()                 # contiguous blocks go with their last reference
         torch.cuda.empty_cache()
         check_lanes_step(w, ref, lanes)
 

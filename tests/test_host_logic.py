@@ -97,3 +97,23 @@ def test_auto_lanes_per_workload():
     assert bench.auto_lanes(W[5], rows5, fp4=True) == 4
     # never more lanes than ranks
     assert bench.lanes_that_fit(W[1], [2 * W[1].H], None, False, 16) == W[1].W
+
+
+def test_emulation_is_freed_by_reference_count():
+    """Contiguous device blocks are returned when their last tensor goes, so
+    the emulation object must hold no reference cycle that would keep its
+    buffers until a garbage collection; the block allocator declines
+    non-GPU devices (the caller then allocates from torch)."""
+    import weakref
+
+    import torch
+
+    from combine_topk_ids_dest_amd import devmem
+    from combine_topk_ids_dest_amd.emulate import LogicalEP
+    w = wl.WORKLOADS[1]
+    ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, [2 * w.H], torch.bfloat16, "cpu")
+    assert ep.contiguous_bytes == 0
+    ref = weakref.ref(ep)
+    del ep
+    assert ref() is None
+    assert devmem.empty_contiguous((4, 4), torch.uint8, "cpu") is None
