@@ -62,3 +62,19 @@ def test_no_contiguous_when_switched_off():
     del ep
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_refused_block_falls_back_and_leaves_no_error():
+    """A block the device cannot grant (1 PiB) gives None, and the runtime's
+    last error is cleared, so the library's next launches do not report it;
+    the emulation then takes its buffers from torch."""
+    assert devmem.empty_contiguous((1 << 50,), torch.uint8, "cuda") is None
+    w = wl.WORKLOADS[1]
+    ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, [2 * w.H], torch.bfloat16, "cuda")
+    for s in range(w.W):
+        ids, wts = wl.routing(w, s)
+        ep.set_source(s, ids, wts, wl.payloads(w, s, ids=ids, wts=wts))
+    ep.step()                          # raises MoeEpError on a stale launch error
+    torch.cuda.synchronize()
+    assert int(ep.err.item()) == 0
+    assert int(ep.send_cnt.sum().item()) > 0
