@@ -150,8 +150,8 @@ int launch_copy(const int32_t* recv_cnt, int64_t cnt_rank_stride,
     const int32_t* tile_off = reinterpret_cast<const int32_t*>(wsb + ws.off_off);
     return hip_status(launch_batch_copy(recv_cnt, cnt_rank_stride, recv_eloc,
                                         eloc_rank_stride, sh.W, sh.e_local,
-                                        sh.slots, sh.cap, tile_off, recv_row, P,
-                                        err_flags, st));
+                                        sh.slots, sh.cap, tile_off, nullptr, 0, nullptr,
+                                        0, recv_row, P, err_flags, st));
 }
 
 }  // namespace
@@ -437,6 +437,23 @@ int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_stride,
     rc = check_payloads(payloads, n_payloads, sh.cap, sh.expert_cap, true, &P);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // Few tiles: no column_scan; the copy sums the tile offsets and writes
+    // expert_num_tokens (the result is the same as plan + copy).
+    if (ws.ntiles > 0 && ws.ntiles <= kBatchFuseTiles) {
+        uint8_t* wsb = static_cast<uint8_t*>(workspace);
+        int32_t* tile_cnt = reinterpret_cast<int32_t*>(wsb + ws.cnt_off);
+        const int32_t clamp = sh.expert_cap < kI32Max ? (int32_t)sh.expert_cap : INT_MAX;
+        rc = hip_status(launch_batch_local(recv_cnt, cnt_rank_stride, recv_eloc,
+                                           eloc_rank_stride, sh.W, sh.e_local, sh.slots,
+                                           sh.cap, (int)ws.ntiles, recv_row, tile_cnt,
+                                           err_flags, st));
+        if (rc) return rc;
+        return hip_status(launch_batch_copy(recv_cnt, cnt_rank_stride, recv_eloc,
+                                            eloc_rank_stride, sh.W, sh.e_local, sh.slots,
+                                            sh.cap, nullptr, tile_cnt, (int)ws.ntiles,
+                                            expert_num_tokens, clamp, recv_row, P,
+                                            err_flags, st));
+    }
     rc = launch_plan(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride, sh, ws,
                      expert_num_tokens, recv_row, err_flags, workspace, st);
     if (rc) return rc;

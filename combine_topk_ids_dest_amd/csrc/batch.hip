@@ -16,6 +16,9 @@
 //   column_scan: tile offsets per expert and expert_num_tokens.
 //   batch_copy: one slot row per block; final row = provisional + tile
 //     offset; the row is read once and stored to each of its experts' rows.
+// With few tiles (moe_ep_expert_batch, at most kBatchFuseTiles) there is no
+// column_scan: batch_copy sums the tile offset of each pick from the tile
+// counts itself and its block 0 writes expert_num_tokens.
 #include "common.h"
 
 namespace moe_ep {
@@ -104,6 +107,22 @@ __global__ __launch_bounds__(256) void batch_local_kernel(
 }
 
 constexpr int kBatchThreads = 256;
+
+// Sum of tile_cnt[j][key] over tiles j < tiles of a [tiles][nkeys] table
+// (loads issued 8 at a time).
+__device__ __forceinline__ int32_t sum_tile_column(const int32_t* __restrict__ tile_cnt,
+                                                   int32_t tiles, int nkeys, int key) {
+    int32_t s = 0;
+    for (int32_t j0 = 0; j0 < tiles; j0 += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = j0 + u < tiles ? tile_cnt[(int64_t)(j0 + u) * nkeys + key] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    return s;
+}
 constexpr int kBatchUnroll = 4;
 // Rows of the leading payload above this many 16-byte vectors have their
 // first pass loaded before the slot's expert rows are known (the loads
@@ -113,11 +132,16 @@ constexpr int kBatchUnroll = 4;
 #define MOE_EP_BATCH_PREFETCH_VECS 512
 #endif
 
-template <bool PREFETCH>
+// FUSED: tile offsets summed here from tile_cnt (fused_tiles tiles), and
+// block 0 writes expert_num_tokens (clamped to clamp_max); otherwise they
+// come from column_scan (tile_off).
+template <bool PREFETCH, bool FUSED>
 __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
     const int32_t* __restrict__ recv_cnt, int64_t cnt_stride,
     const int32_t* __restrict__ recv_eloc, int64_t eloc_stride, int W,
     int e_local, int slots, int64_t cap, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ tile_cnt, int32_t fused_tiles,
+    int32_t* __restrict__ expert_num_tokens, int32_t clamp_max,
     int32_t* __restrict__ recv_row, const PayloadSet P,
     uint32_t* __restrict__ err) {
     __shared__ int32_t pre[MOE_EP_MAX_WORLD + 1];
@@ -128,6 +152,12 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
     const int64_t expert_cap = (int64_t)W * cap;
 
     if (tid < 64) load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre, nullptr);
+    if (FUSED && blockIdx.x == 0) {
+        for (int e = tid; e < e_local; e += kBatchThreads) {
+            const int32_t tot = sum_tile_column(tile_cnt, fused_tiles, e_local, e);
+            expert_num_tokens[e] = tot < clamp_max ? tot : clamp_max;
+        }
+    }
     __syncthreads();
     const int32_t S = pre[W];
 
@@ -163,7 +193,9 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
                 const int32_t prov = recv_row[at];
                 const bool ok = e >= 0 && e < e_local;
                 const int32_t q = v * slots + j;
-                const int32_t off = tile_off[(int64_t)(q / kBatchTile) * e_local + (ok ? e : 0)];
+                const int32_t off =
+                    FUSED ? sum_tile_column(tile_cnt, q / kBatchTile, e_local, ok ? e : 0)
+                          : tile_off[(int64_t)(q / kBatchTile) * e_local + (ok ? e : 0)];
                 if (ok) {
                     const int64_t r = (int64_t)prov + off;
                     if (r < expert_cap) row = (int32_t)r;
@@ -288,20 +320,27 @@ hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
 hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
                              const int32_t* recv_eloc, int64_t eloc_stride,
                              int W, int e_local, int slots, int64_t cap,
-                             const int32_t* tile_off, int32_t* recv_row,
+                             const int32_t* tile_off, const int32_t* tile_cnt,
+                             int fused_tiles, int32_t* expert_num_tokens,
+                             int32_t clamp_max, int32_t* recv_row,
                              const PayloadSet& P, uint32_t* err,
                              hipStream_t stream) {
     const int64_t max_rows = (int64_t)W * cap;
     if (max_rows == 0) return hipSuccess;
     const int64_t grid = max_rows < MOE_EP_ROW_GRID ? max_rows : MOE_EP_ROW_GRID;
-    if (P.n > 0 && P.row_bytes[0] / 16 > MOE_EP_BATCH_PREFETCH_VECS)
-        batch_copy_kernel<true><<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>(
-            recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
-            tile_off, recv_row, P, err);
-    else
-        batch_copy_kernel<false><<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>(
-            recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap,
-            tile_off, recv_row, P, err);
+    const bool pf = P.n > 0 && P.row_bytes[0] / 16 > MOE_EP_BATCH_PREFETCH_VECS;
+#define MOE_EP_BATCH_COPY_LAUNCH(PFV, FUSEDV)                                              \
+    batch_copy_kernel<PFV, FUSEDV><<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>( \
+        recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap, tile_off,     \
+        tile_cnt, fused_tiles, expert_num_tokens, clamp_max, recv_row, P, err)
+    if (tile_cnt) {
+        if (pf) MOE_EP_BATCH_COPY_LAUNCH(true, true);
+        else MOE_EP_BATCH_COPY_LAUNCH(false, true);
+    } else {
+        if (pf) MOE_EP_BATCH_COPY_LAUNCH(true, false);
+        else MOE_EP_BATCH_COPY_LAUNCH(false, false);
+    }
+#undef MOE_EP_BATCH_COPY_LAUNCH
     return hipGetLastError();
 }
 

@@ -20,6 +20,12 @@ constexpr int kPackFuseTiles = MOE_EP_PACK_FUSE_TILES;
 constexpr int kBatchTile = 1024;
 constexpr int kBatchRounds = kBatchTile / 256;
 constexpr int kBatchChunks = kBatchTile / 64;   // wave-sized chunks per tile
+// Up to this many pick tiles, moe_ep_expert_batch runs no column_scan: the
+// copy kernel sums tile offsets itself and writes expert_num_tokens.
+#ifndef MOE_EP_BATCH_FUSE_TILES
+#define MOE_EP_BATCH_FUSE_TILES 64
+#endif
+constexpr int kBatchFuseTiles = MOE_EP_BATCH_FUSE_TILES;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -223,10 +229,16 @@ hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
                               int ntiles, int32_t* recv_row, int32_t* tile_cnt,
                               uint32_t* err, hipStream_t stream);
 
+// tile_cnt != nullptr selects the fused tile offsets (fused_tiles <=
+// kBatchFuseTiles): offsets are summed from tile_cnt and block 0 writes
+// expert_num_tokens (clamped to clamp_max); otherwise tile_off holds the
+// offsets from column_scan.
 hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
                              const int32_t* recv_eloc, int64_t eloc_stride,
                              int W, int e_local, int slots, int64_t cap,
-                             const int32_t* tile_off, int32_t* recv_row,
+                             const int32_t* tile_off, const int32_t* tile_cnt,
+                             int fused_tiles, int32_t* expert_num_tokens,
+                             int32_t clamp_max, int32_t* recv_row,
                              const PayloadSet& P, uint32_t* err,
                              hipStream_t stream);
 
