@@ -152,21 +152,22 @@ def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None,
 
 
 # Device memory the lanes' expert-batch buffers may take together.
-LANE_MEMORY_BYTES = 96 << 30
+LANE_MEMORY_BYTES = 160 << 30
 AUTO_LANES = 4
 AUTO_LANES_MIN_BYTES = 16 << 20
 
 
 def lanes_that_fit(w, row_bytes, fp8_group, fp4, want: int) -> int:
     """Lanes to use: at most `want` and W, and no more than fit their
-    [e_local, W*cap, row] expert-batch buffers in LANE_MEMORY_BYTES."""
+    [e_local, W*cap, row] expert-batch and [e_local, W*cap, H] bf16
+    expert-output buffers in LANE_MEMORY_BYTES."""
     from combine_topk_ids_dest_amd import binding
     rows = list(row_bytes)
     if fp4:
         rows = [w.H // 2, binding.fp4_scale_pitch(w.H)] + rows[1:]
     elif fp8_group:
         rows = [w.H, 4 * binding.scale_pitch(w.H, fp8_group)] + rows[1:]
-    per_lane = w.e_local * w.W * w.cap * sum(rows)
+    per_lane = w.e_local * w.W * w.cap * (sum(rows) + 2 * w.H)
     return max(1, min(want, w.W, LANE_MEMORY_BYTES // max(per_lane, 1)))
 
 
@@ -299,8 +300,8 @@ def main():
                          "codes with one e4m3 scale per 16 columns")
     ap.add_argument("--lanes", default="auto",
                     help="HIP streams the logical ranks are spread over, so one rank's "
-                         "kernels overlap another's (each lane holds its own workspace and "
-                         "expert-batch buffer; capped by LANE_MEMORY_BYTES; with --graph one "
+                         "kernels overlap another's (each lane holds its own workspace, "
+                         "expert-batch and expert-output buffers; capped by LANE_MEMORY_BYTES; with --graph one "
                          "graph per phase and lane); "
                          "1 runs the ranks one after another; auto: AUTO_LANES, or 1 when a "
                          "step's source rows are under AUTO_LANES_MIN_BYTES (the joins "
@@ -354,6 +355,7 @@ def main():
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
     wl.expert_outputs_device(ep.Y, seed=1000 + w.wid)
+    ep.share_expert_outputs()
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs generated and resident in "
         f"{time.perf_counter() - t_gen:.1f} s")

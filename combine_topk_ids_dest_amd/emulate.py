@@ -16,12 +16,13 @@ Device layout (all dense, rank-major):
                                            destinations of that lane
   expert_num_tokens [W_dst, e_local]
   recv_row        [W_dst, W_src, cap, slots] (reduce context)
-  Y               [e_local, W*cap, H]      expert outputs, reused per destination
+  Y               [e_local, W*cap, H]      expert outputs, one buffer per lane,
+                                           reused by the destinations of that lane
   ret             [W_dst, W_src, cap, H]
   out             [W_src, T, H]
 
-Lanes: rank i uses lane i % lanes for the two buffers that ranks share (the
-workspace and b). With several lanes, step(streams=...) runs the ranks of
+Lanes: rank i uses lane i % lanes for the buffers that ranks share (the
+workspace, b and Y), so no two lanes read or write the same expert rows. With several lanes, step(streams=...) runs the ranks of
 each lane on its own HIP stream, so the kernels of different ranks may
 overlap (on W GPUs the ranks run at the same time anyway); the three phases
 (packs, batch + reduce, unpacks) are joined across the streams with events,
@@ -124,7 +125,9 @@ class LogicalEP:
         self.b = self.b_lanes[0]
         self.expert_num_tokens = alloc((W_, el), torch.int32)
         self.recv_row = alloc((W_, W_, cap, sl), torch.int32)
-        self.Y = alloc((el, self.expert_cap, H), combine_dtype)
+        # self.Y is lane 0's; share_expert_outputs() copies it to the others
+        self.Y_lanes = [alloc((el, self.expert_cap, H), combine_dtype) for _ in range(lanes)]
+        self.Y = self.Y_lanes[0]
         self.ret = alloc((W_, W_, cap, H), combine_dtype)
         self.out = alloc((W_, T, H), combine_dtype)
         self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
@@ -144,6 +147,13 @@ class LogicalEP:
         for p, rows in enumerate(payload_rows):
             t = torch.as_tensor(rows).view(torch.uint8)
             self.src[p][s].copy_(t.reshape(self.T, self.row_bytes[p]))
+
+    def share_expert_outputs(self):
+        """Copies lane 0's expert outputs (self.Y) to the other lanes' Y
+        buffers, for callers that draw one set of expert outputs for every
+        destination."""
+        for y in self.Y_lanes[1:]:
+            y.copy_(self.Y)
 
     # -- the four calls for one logical rank ----------------------------
     # Each call is marshalled once (binding.prepare_*) and replayed; the
@@ -203,7 +213,7 @@ class LogicalEP:
 
     def _prep_reduce(self, r: int):
         return B.prepare_combine_reduce(
-            self.Y, self.send_cnt[:, r], self.send_eloc[:, r], self.send_w[:, r],
+            self.Y_lanes[r % self.lanes], self.send_cnt[:, r], self.send_eloc[:, r], self.send_w[:, r],
             self.recv_row[r], self.W, self.e_local, self.K, self.cap,
             self.ret[r])
 
@@ -213,7 +223,7 @@ class LogicalEP:
 
     def _prep_reduce_peers(self, r: int):
         return B.prepare_combine_reduce(
-            self.Y, self.send_cnt[:, r], self.send_eloc[:, r], self.send_w[:, r],
+            self.Y_lanes[r % self.lanes], self.send_cnt[:, r], self.send_eloc[:, r], self.send_w[:, r],
             self.recv_row[r], self.W, self.e_local, self.K, self.cap,
             self.ret[r], self_src=r)
 
@@ -221,7 +231,8 @@ class LogicalEP:
         # rank s's own source block as rank s receives it: send[s][s]
         return B.prepare_combine_unpack_fused(
             self.ret[:, s], self.token_slot[s], self.cap, s,
-            self.Y if Y is None else Y, self.send_eloc[s, s], self.send_w[s, s],
+            self.Y_lanes[s % self.lanes] if Y is None else Y, self.send_eloc[s, s],
+            self.send_w[s, s],
             self.recv_row[s, s], self.e_local, self.K, self.out[s])
 
     def pack(self, s: int, stream=None):

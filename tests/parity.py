@@ -440,6 +440,7 @@ def check_lanes_step(w: wl.Workload, ref, lanes: int, seed: int = 0):
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
     wl.expert_outputs_device(ep.Y, seed=2000 + w.wid)
+    ep.share_expert_outputs()
     streams = [torch.cuda.Stream() for _ in range(lanes)]
     ep.step(streams=streams)
     torch.cuda.synchronize()
