@@ -265,9 +265,9 @@ class LogicalEP:
 
     def step(self, stream=None, fused_local=False, streams=None):
         """One pass of the whole path over all W logical ranks: W packs,
-        then batch + reduce per destination (reusing b and Y), then W
-        unpacks. fused_local: each rank's local slice is combined by the
-        fused unpack (the shared Y stands in for every rank's own expert
+        then batch + reduce per destination (reusing its lane's b and Y),
+        then W unpacks. fused_local: each rank's local slice is combined by
+        the fused unpack (its lane's Y stands in for the rank's own expert
         output). streams: one HIP stream per lane; rank i's calls go to
         streams[i % lanes], and each phase starts on every stream only
         after the previous phase has ended on all of them. The step is
