@@ -242,3 +242,47 @@ def test_fp8_every_bf16_bit_pattern():
     say(f"[fp8 sweep] all bf16 patterns in {T} rows")
     run_full_parity(w, srcs=[(ids, wts)],
                     pls=[[hidden.view(np.uint8).reshape(T, 2 * H)]], fp8_group=128)
+
+
+def _batch_outputs(w, split: bool):
+    """Per destination: expert_num_tokens, recv_row and the valid expert rows
+    of a step's batch half, through the one call or through plan + copy."""
+    from combine_topk_ids_dest_amd.emulate import LogicalEP
+    srcs = [wl.routing(w, s, 23) for s in range(w.W)]
+    pls = [wl.payloads(w, s, 23, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
+    ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, [p.shape[1] for p in pls[0]],
+                   torch.bfloat16, "cuda", fill=0xFF)
+    for s in range(w.W):
+        ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
+        ep.pack(s)
+    out = []
+    for r in range(w.W):
+        if split:
+            ep.batch_plan(r)
+            ep.batch_copy(r)
+        else:
+            ep.batch(r)
+        ent = ep.expert_num_tokens[r].clone()
+        rows = [torch.cat([b[e, :int(ent[e])] for e in range(ep.e_local)]).clone()
+                for b in ep.b]
+        out.append((ent, ep.recv_row[r].clone(), rows))
+    torch.cuda.synchronize()
+    assert int(ep.err.item()) == 0
+    return out, ep.slots
+
+
+@pytest.mark.parametrize("cap,tiles", [(64, 2), (2048, 64), (2080, 65)])
+def test_combined_batch_is_bit_identical_to_plan_then_copy(cap, tiles):
+    """moe_ep_expert_batch skips the column scan for at most 64 pick tiles
+    (the copy sums the tile offsets itself); plan + copy always runs it.
+    At 2, exactly 64 and 65 tiles both give the same bytes."""
+    w = W1.scaled(W=8, E=32, K=4, T=cap, cap=cap, H=64, pad_frac=0.05)
+    one, slots = _batch_outputs(w, split=False)
+    two, _ = _batch_outputs(w, split=True)
+    assert -(-w.W * w.cap * slots // 1024) == tiles
+    say(f"[batch one call vs plan + copy] cap={cap}: {tiles} pick tiles")
+    for r, ((e1, r1, b1), (e2, r2, b2)) in enumerate(zip(one, two)):
+        assert torch.equal(e1, e2), f"expert_num_tokens of destination {r}"
+        assert torch.equal(r1, r2), f"recv_row of destination {r}"
+        for p, (x, y) in enumerate(zip(b1, b2)):
+            assert torch.equal(x, y), f"expert rows of destination {r}, payload {p}"
