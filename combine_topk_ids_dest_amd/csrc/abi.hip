@@ -26,8 +26,11 @@ struct Shape {
 
 int check_shape(int32_t K, int32_t e_local, int32_t W, int64_t max_num_tokens,
                 Shape* sh) {
+    // cap <= INT_MAX first (W * cap * slots < 2^31 needs it anyway), so the
+    // products below cannot overflow
     if (K <= 0 || W <= 0 || W > MOE_EP_MAX_WORLD || e_local <= 0 ||
-        e_local > MOE_EP_MAX_LOCAL_EXPERTS || max_num_tokens < 0)
+        e_local > MOE_EP_MAX_LOCAL_EXPERTS || max_num_tokens < 0 ||
+        max_num_tokens > kI32Max)
         return MOE_EP_EINVAL;
     sh->W = W;
     sh->e_local = e_local;
@@ -161,7 +164,8 @@ extern "C" {
 int moe_ep_capacities(int32_t K, int32_t E, int32_t W, int64_t max_num_tokens,
                       int64_t* cap, int32_t* slots, int64_t* expert_cap) {
     if (!cap || !slots || !expert_cap) return MOE_EP_EINVAL;
-    if (K <= 0 || E <= 0 || W <= 0 || E % W != 0 || max_num_tokens < 0)
+    if (K <= 0 || E <= 0 || W <= 0 || E % W != 0 || max_num_tokens < 0 ||
+        max_num_tokens > INT64_MAX / W)   // expert_cap would overflow
         return MOE_EP_EINVAL;
     const int32_t e_local = E / W;
     *cap = max_num_tokens;

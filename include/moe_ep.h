@@ -39,7 +39,8 @@
  *     OR-ing MOE_EP_ERR_* bits into *err_flags (if non-NULL; the caller
  *     clears it) and have the defined behaviour given with each bit.
  *   - Limits: 1 <= W <= 64, e_local <= 1024, slots <= 64,
- *     n_payloads <= 8, and W * cap * slots, T * K, T * W < 2^31.
+ *     n_payloads <= 8, cap <= INT_MAX, and W * cap * slots, T * K,
+ *     T * W < 2^31 (EINVAL otherwise).
  */
 #ifndef MOE_EP_H
 #define MOE_EP_H
@@ -100,7 +101,8 @@ typedef struct moe_ep_payload {
 /*
  * capacities() of the vLLM page: cap = max_num_tokens,
  * slots = min(K, E / W), expert_cap = max_num_tokens * W. Host only.
- * EINVAL if K <= 0, E <= 0, W <= 0, E % W != 0 or max_num_tokens < 0.
+ * EINVAL if K <= 0, E <= 0, W <= 0, E % W != 0, max_num_tokens < 0 or
+ * max_num_tokens * W does not fit in int64_t.
  */
 MOE_EP_API int moe_ep_capacities(int32_t K, int32_t E, int32_t W, int64_t max_num_tokens,
                       int64_t* cap, int32_t* slots, int64_t* expert_cap);

@@ -80,6 +80,19 @@ def test_capacities_and_workspace():
     with pytest.raises(B.MoeEpError) as e:
         B.moe_ep_workspace_bytes(10, 8, 256, 128, 4096)    # W > 64
     assert e.value.status == B.EINVAL
+    # huge max_num_tokens: rejected before any product can overflow (the
+    # sanitizer run of these tests would report a signed overflow)
+    big = 1 << 62
+    assert B.moe_ep_capacities(8, 256, 1, big) == (big, 8, big)
+    for bad in [(8, 256, 8, big), (8, 256, 8, (1 << 63) - 1)]:
+        with pytest.raises(B.MoeEpError) as e:
+            B.moe_ep_capacities(*bad)
+        assert e.value.status == B.EINVAL
+    for mnt in (big, (1 << 31)):
+        with pytest.raises(B.MoeEpError) as e:
+            B.moe_ep_workspace_bytes(0, 8, 256, 8, mnt)
+        assert e.value.status == B.EINVAL
+    assert B.moe_ep_workspace_bytes(0, 1, 64, 64, (1 << 31) - 1 >> 6) > 0
 
 
 def test_status_strings():
