@@ -18,6 +18,17 @@ inline bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// stride >= rows * width (rows, width >= 0), compared without forming the
+// product: caller-given sizes may be large enough to overflow it.
+inline bool covers(int64_t stride, int64_t rows, int64_t width) {
+    if (rows <= 0 || width <= 0) return stride >= 0;
+    return stride / width >= rows;
+}
+
+// An element stride (eb = 2 or 4 bytes per element) that spans a multiple
+// of 16 bytes.
+inline bool stride16(int64_t stride, int eb) { return stride % (16 / eb) == 0; }
+
 // Shapes common to every call; fills e_local, cap, slots, expert_cap.
 struct Shape {
     int32_t W = 0, e_local = 0, slots = 0;
@@ -87,8 +98,8 @@ int check_payloads(const moe_ep_payload* payloads, int32_t n_payloads,
         if (d.row_bytes % 16 || d.src_stride % 16 || d.dst_stride % 16 ||
             !aligned16(d.src) || !aligned16(d.dst))
             return MOE_EP_EALIGN;
-        if (d.src_stride < min_src_rows * d.row_bytes ||
-            d.dst_stride < min_dst_rows * d.row_bytes)
+        if (!covers(d.src_stride, min_src_rows, d.row_bytes) ||
+            !covers(d.dst_stride, min_dst_rows, d.row_bytes))
             return MOE_EP_EINVAL;
         P->src[p] = static_cast<const uint8_t*>(d.src);
         P->dst[p] = static_cast<uint8_t*>(d.dst);
@@ -210,7 +221,8 @@ int moe_ep_combine_unpack_fused(const void* back, int64_t back_rank_stride,
     Shape sh;
     int rc = check_shape(K, e_local, W, max_num_tokens, &sh);
     if (rc) return rc;
-    if (T < 0 || H <= 0 || self_rank < 0 || self_rank >= W) return MOE_EP_EINVAL;
+    if (T < 0 || H <= 0 || H > kI32Max || self_rank < 0 || self_rank >= W)
+        return MOE_EP_EINVAL;
     const int eb = elem_bytes(dtype);
     if (eb == 0) return MOE_EP_EDTYPE;
     if (T > max_num_tokens) return MOE_EP_ECAP;
@@ -218,9 +230,10 @@ int moe_ep_combine_unpack_fused(const void* back, int64_t back_rank_stride,
     if (T > 0 && (!back || !token_slot || !out || !expert_out || !self_eloc ||
                   !self_w || !self_row))
         return MOE_EP_EINVAL;
-    if (back_rank_stride < max_num_tokens * H || expert_stride < sh.expert_cap * H)
+    if (!covers(back_rank_stride, max_num_tokens, H) ||
+        !covers(expert_stride, sh.expert_cap, H))
         return MOE_EP_EINVAL;
-    if ((H * eb) % 16 || (back_rank_stride * eb) % 16 || (expert_stride * eb) % 16 ||
+    if ((H * eb) % 16 || !stride16(back_rank_stride, eb) || !stride16(expert_stride, eb) ||
         !aligned16(back) || !aligned16(out) || !aligned16(expert_out))
         return MOE_EP_EALIGN;
     return hip_status(launch_combine_unpack_fused(
@@ -253,20 +266,20 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
     if (quant && quant->mode == 1) {
         const QuantArgs& Q = *quant;
         if (Q.group != 32 && Q.group != 64 && Q.group != 128) return MOE_EP_EINVAL;
-        if (Q.H <= 0 || Q.H % Q.group) return MOE_EP_EINVAL;
+        if (Q.H <= 0 || Q.H > kI32Max || Q.H % Q.group) return MOE_EP_EINVAL;
         if (T > 0 && (!Q.src || !Q.q || !Q.s)) return MOE_EP_EINVAL;
-        if (Q.src_stride < 2 * Q.H || Q.q_stride < sh.cap * Q.H ||
-            Q.s_stride < sh.cap * Q.s_pitch)
+        if (!covers(Q.src_stride, 2, Q.H) || !covers(Q.q_stride, sh.cap, Q.H) ||
+            !covers(Q.s_stride, sh.cap, Q.s_pitch))
             return MOE_EP_EINVAL;
         if (!aligned16(Q.src) || Q.src_stride % 16 || (reinterpret_cast<uintptr_t>(Q.q) & 15) ||
             Q.q_stride % 16 || (reinterpret_cast<uintptr_t>(Q.s) & 3))
             return MOE_EP_EALIGN;
     } else if (quant) {
         const QuantArgs& Q = *quant;
-        if (Q.H <= 0) return MOE_EP_EINVAL;
+        if (Q.H <= 0 || Q.H > kI32Max) return MOE_EP_EINVAL;
         if (T > 0 && (!Q.src || !Q.q || !Q.s)) return MOE_EP_EINVAL;
-        if (Q.src_stride < 2 * Q.H || Q.q_stride < sh.cap * (Q.H / 2) ||
-            Q.s_stride < sh.cap * Q.s_pitch)
+        if (!covers(Q.src_stride, 2, Q.H) || !covers(Q.q_stride, sh.cap, Q.H / 2) ||
+            !covers(Q.s_stride, sh.cap, Q.s_pitch))
             return MOE_EP_EINVAL;
         // code rows of H/2 bytes, like every travelling row, are 16-byte multiples
         if (Q.H % 32 || !aligned16(Q.src) || Q.src_stride % 16 || !aligned16(Q.q) ||
@@ -342,7 +355,10 @@ int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
     Q.q = static_cast<uint8_t*>(send_q);
     Q.q_stride = q_rank_stride;
     Q.s = reinterpret_cast<uint8_t*>(send_scale);
-    Q.s_stride = scale_rank_stride * 4;                  // floats -> bytes
+    // floats -> bytes; a stride whose byte count overflows becomes -1,
+    // which the stride check rejects
+    Q.s_stride = scale_rank_stride < 0 || scale_rank_stride > INT64_MAX / 4
+                     ? -1 : scale_rank_stride * 4;
     Q.H = H;
     Q.group = group;
     Q.n_scales = group > 0 ? H / group : 0;
@@ -498,13 +514,13 @@ static int combine_reduce(const void* expert_out, int64_t expert_stride,
     if (rc) return rc;
     const int eb = elem_bytes(dtype);
     if (eb == 0) return MOE_EP_EDTYPE;
-    if (H <= 0) return MOE_EP_EINVAL;
+    if (H <= 0 || H > kI32Max) return MOE_EP_EINVAL;
     if (!expert_out || !recv_cnt || !recv_eloc || !recv_w || !recv_row || !ret)
         return MOE_EP_EINVAL;
     if (cnt_rank_stride < 1 || meta_rank_stride < sh.cap * sh.slots ||
-        expert_stride < sh.expert_cap * H || ret_rank_stride < sh.cap * H)
+        !covers(expert_stride, sh.expert_cap, H) || !covers(ret_rank_stride, sh.cap, H))
         return MOE_EP_EINVAL;
-    if ((H * eb) % 16 || (expert_stride * eb) % 16 || (ret_rank_stride * eb) % 16 ||
+    if ((H * eb) % 16 || !stride16(expert_stride, eb) || !stride16(ret_rank_stride, eb) ||
         !aligned16(expert_out) || !aligned16(ret))
         return MOE_EP_EALIGN;
     return hip_status(launch_combine_reduce(
@@ -546,15 +562,16 @@ int moe_ep_combine_unpack(const void* back, int64_t back_rank_stride,
                           int32_t dtype, int64_t H, const int32_t* token_slot,
                           int64_t T, int32_t W, int64_t max_num_tokens,
                           void* out, void* stream) {
-    if (W <= 0 || W > MOE_EP_MAX_WORLD || T < 0 || max_num_tokens < 0 || H <= 0)
+    if (W <= 0 || W > MOE_EP_MAX_WORLD || T < 0 || max_num_tokens < 0 ||
+        max_num_tokens > kI32Max || H <= 0 || H > kI32Max)
         return MOE_EP_EINVAL;
     const int eb = elem_bytes(dtype);
     if (eb == 0) return MOE_EP_EDTYPE;
     if (T > max_num_tokens) return MOE_EP_ECAP;
     if (T * W > kI32Max) return MOE_EP_EINVAL;
     if (T > 0 && (!back || !token_slot || !out)) return MOE_EP_EINVAL;
-    if (back_rank_stride < max_num_tokens * H) return MOE_EP_EINVAL;
-    if ((H * eb) % 16 || (back_rank_stride * eb) % 16 || !aligned16(back) ||
+    if (!covers(back_rank_stride, max_num_tokens, H)) return MOE_EP_EINVAL;
+    if ((H * eb) % 16 || !stride16(back_rank_stride, eb) || !aligned16(back) ||
         !aligned16(out))
         return MOE_EP_EALIGN;
     return hip_status(launch_combine_unpack(back, back_rank_stride, dtype, H,

@@ -39,8 +39,8 @@
  *     OR-ing MOE_EP_ERR_* bits into *err_flags (if non-NULL; the caller
  *     clears it) and have the defined behaviour given with each bit.
  *   - Limits: 1 <= W <= 64, e_local <= 1024, slots <= 64,
- *     n_payloads <= 8, cap <= INT_MAX, and W * cap * slots, T * K,
- *     T * W < 2^31 (EINVAL otherwise).
+ *     n_payloads <= 8, cap <= INT_MAX, H <= INT_MAX, and
+ *     W * cap * slots, T * K, T * W < 2^31 (EINVAL otherwise).
  */
 #ifndef MOE_EP_H
 #define MOE_EP_H

@@ -257,6 +257,12 @@ def test_combine_argument_checks():
     assert reduce(rstride=16 * 256 - 8) == B.EINVAL
     assert reduce(y=None) == B.EINVAL
     assert reduce(y=FAKE + 2) == B.EALIGN
+    # sizes and strides large enough to overflow a product are rejected,
+    # not multiplied (the sanitizer run of these tests checks the latter)
+    huge = 1 << 62
+    assert reduce(H=huge) == B.EINVAL
+    assert reduce(H=1 << 40, estride=huge, rstride=huge) == B.EINVAL
+    assert reduce(estride=(1 << 63) - 4, rstride=(1 << 63) - 4) == B.EALIGN
 
     def unpack(dtype=B.BF16, H=256, T=8, W=4, cap=16, bstride=None, out=FAKE):
         if bstride is None:
@@ -270,6 +276,9 @@ def test_combine_argument_checks():
     assert unpack(bstride=16 * 256 - 8) == B.EINVAL
     assert unpack(out=None) == B.EINVAL
     assert unpack(H=12) == B.EALIGN
+    assert unpack(H=1 << 62, bstride=1 << 62) == B.EINVAL
+    assert unpack(cap=1 << 62, T=8) == B.EINVAL
+    assert unpack(bstride=(1 << 63) - 4) == B.EALIGN
 
     def peers(self_src=0, W=4, y=FAKE):
         return lib.moe_ep_combine_reduce_peers(y, W * 16 * 256, B.BF16, 256, FAKE, 1,
@@ -295,6 +304,7 @@ def test_combine_argument_checks():
     assert fused(estride=4 * 16 * 256 - 8) == B.EINVAL
     assert fused(y=FAKE + 2) == B.EALIGN
     assert fused(H=12, estride=4 * 16 * 16) == B.EALIGN
+    assert fused(H=1 << 62, estride=1 << 62) == B.EINVAL
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
