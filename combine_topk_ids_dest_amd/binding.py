@@ -200,18 +200,40 @@ def _payload_array(pairs, src_row_dim: int, dst_row_dim: int):
     return arr
 
 
+def _tensors(x):
+    """The tensors in a nest of tuples and lists."""
+    if isinstance(x, torch.Tensor):
+        yield x
+    elif isinstance(x, (tuple, list)):
+        for y in x:
+            yield from _tensors(y)
+
+
 class PreparedCall:
     """One call of the library with its arguments marshalled once; calling
     it passes them unchanged with the stream of the moment. It keeps the
-    tensors (and the payload descriptor array) it points into alive."""
+    tensors (and the payload descriptor array) it points into alive. Every
+    tensor must be on one GPU (the library takes device pointers only), and
+    the stream of a call must belong to that GPU."""
 
     def __init__(self, name: str, args: tuple, keep: tuple):
+        devices = {t.device for t in _tensors(keep)}
+        if any(d.type != "cuda" for d in devices) or len(devices) > 1:
+            raise ValueError(f"{name}: every tensor must be on one GPU, got "
+                             f"{sorted(str(d) for d in devices)}")
+        self.device = devices.pop().index if devices else None
         self.name = name
         self.fn = getattr(load(), name)
         self.args = args
         self.keep = keep
 
     def __call__(self, stream=None) -> None:
+        if self.device is not None and not isinstance(stream, int):
+            dev = (torch.cuda.current_device() if stream is None
+                   else stream.device.index)
+            if dev != self.device:
+                raise ValueError(f"{self.name}: the stream is on cuda:{dev}, the "
+                                 f"tensors on cuda:{self.device}")
         _check(self.name, self.fn(*self.args, _stream(stream)))
 
 

@@ -118,3 +118,17 @@ def test_emulation_is_freed_by_reference_count():
     del ep
     assert ref() is None
     assert devmem.empty_contiguous((4, 4), torch.uint8, "cpu") is None
+
+
+def test_prepared_calls_take_gpu_tensors_only():
+    """The library takes device pointers only: a call prepared on host
+    tensors is refused before any pointer reaches it."""
+    import torch
+    back = torch.zeros(4, 16, 256, dtype=torch.bfloat16)
+    token_slot = torch.zeros(8, 4, dtype=torch.int32)
+    out = torch.zeros(8, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="one GPU"):
+        B.prepare_combine_unpack(back, token_slot, 16, out)
+    with pytest.raises(ValueError, match="one GPU"):
+        B.moe_ep_combine_unpack(back, token_slot, 16, out)
+    assert list(B._tensors((1, [back, (None, out)], token_slot))) == [back, out, token_slot]
