@@ -124,10 +124,14 @@ __device__ __forceinline__ int32_t sum_tile_column(const int32_t* __restrict__ t
     return s;
 }
 constexpr int kBatchUnroll = 4;
-// Rows of the leading payload above this many 16-byte vectors have their
-// first pass loaded before the slot's expert rows are known (the loads
-// overlap wave 0's planning; it costs registers, which narrower rows, with
-// less to overlap, need more).
+// A row of one payload above this many 16-byte vectors has its first pass
+// loaded before the slot's expert rows are known (the loads overlap wave 0's
+// planning). It costs registers (6 waves per SIMD instead of 8), which
+// narrower rows, with less to overlap, and rows of several payloads, whose
+// later payloads are not prefetched, need more: at the DS-V3 shape (one
+// 14 KiB payload) the early pass took the copy from 152-155 to 148 us, at
+// the multi-payload shape (14 KiB + four more payloads) it made it slower,
+// 365 against 345 us.
 #ifndef MOE_EP_BATCH_PREFETCH_VECS
 #define MOE_EP_BATCH_PREFETCH_VECS 512
 #endif
@@ -328,7 +332,7 @@ hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
     const int64_t max_rows = (int64_t)W * cap;
     if (max_rows == 0) return hipSuccess;
     const int64_t grid = max_rows < MOE_EP_ROW_GRID ? max_rows : MOE_EP_ROW_GRID;
-    const bool pf = P.n > 0 && P.row_bytes[0] / 16 > MOE_EP_BATCH_PREFETCH_VECS;
+    const bool pf = P.n == 1 && P.row_bytes[0] / 16 > MOE_EP_BATCH_PREFETCH_VECS;
 #define MOE_EP_BATCH_COPY_LAUNCH(PFV, FUSEDV)                                              \
     batch_copy_kernel<PFV, FUSEDV><<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>( \
         recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap, tile_off,     \
