@@ -151,9 +151,14 @@ def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None,
     return out
 
 
-# Device memory the lanes' expert-batch buffers may take together.
+# Device memory the lanes' expert-batch and expert-output buffers may take
+# together.
 LANE_MEMORY_BYTES = 160 << 30
-AUTO_LANES = 4
+# Two lanes measured fastest at every shape with more than one lane's worth
+# of work: with the ranks over 1, 2, 3 and 4 streams the DS-V3 step took
+# 3.30, 3.24, 3.40 and 3.38 ms, Mixtral 1.39, 1.35, - and 1.38 ms, decode
+# 1.40, 0.98, 0.99 and 1.12 ms.
+AUTO_LANES = 2
 AUTO_LANES_MIN_BYTES = 16 << 20
 
 

@@ -81,21 +81,22 @@ def test_counter_summary_of_other_sources_is_ignored(tmp_path, monkeypatch):
 
 
 def test_auto_lanes_per_workload():
-    """--lanes auto: 4 lanes, 1 for a tiny step, and no more lanes than
+    """--lanes auto: 2 lanes, 1 for a tiny step, and no more lanes than
     there are ranks or than fit the lanes' expert-batch and bf16
     expert-output buffers in LANE_MEMORY_BYTES (the multi-payload rows are
     21,792 B)."""
     W = wl.WORKLOADS
     assert bench.auto_lanes(W[1], [2 * W[1].H]) == 1
-    assert bench.auto_lanes(W[2], [2 * W[2].H]) == 4
-    assert bench.auto_lanes(W[3], [2 * W[3].H]) == 4
-    assert bench.auto_lanes(W[4], [2 * W[4].H]) == 4
+    assert bench.auto_lanes(W[2], [2 * W[2].H]) == 2
+    assert bench.auto_lanes(W[3], [2 * W[3].H]) == 2
+    assert bench.auto_lanes(W[4], [2 * W[4].H]) == 2
     rows5 = [2 * W[5].H, W[5].H, 4 * 56, 32, 32]
     per_lane = W[5].e_local * W[5].W * W[5].cap * (sum(rows5) + 2 * W[5].H)
     assert bench.auto_lanes(W[5], rows5) == bench.LANE_MEMORY_BYTES // per_lane == 2
-    # quantised rows are smaller, so more lanes fit
+    # quantised rows are smaller, so more lanes would fit
     assert bench.auto_lanes(W[5], rows5, fp8_group=128) == 2
-    assert bench.auto_lanes(W[5], rows5, fp4=True) == 3
+    assert bench.auto_lanes(W[5], rows5, fp4=True) == 2
+    assert bench.lanes_that_fit(W[5], rows5, None, True, 4) == 3
     # never more lanes than ranks
     assert bench.lanes_that_fit(W[1], [2 * W[1].H], None, False, 16) == W[1].W
 
