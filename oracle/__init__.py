@@ -46,7 +46,8 @@ def load(rebuild: bool = False):
     global _lib
     if _lib is not None and not rebuild:
         return _lib
-    if rebuild or not os.path.exists(_build.LIB):
+    if (rebuild or not os.path.exists(_build.LIB)
+            or os.path.getmtime(_build.SRC) > os.path.getmtime(_build.LIB)):
         _build.build()
     _lib = _open(_build.LIB)
     return _lib
@@ -94,6 +95,8 @@ def _open(path: str):
     lib.oracle_combine_unpack.restype = None
     lib.oracle_round_bf16.argtypes = [ctypes.c_float]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_bf16_bits.argtypes = [ctypes.c_uint32]
+    lib.oracle_round_bf16_bits.restype = ctypes.c_uint16
     lib.oracle_sanitize_expert_ids.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _I32, _P, _I64]
     lib.oracle_sanitize_expert_ids.restype = ctypes.c_uint32
@@ -148,6 +151,12 @@ def capacities(K: int, E: int, W: int, max_num_tokens: int):
 
 def round_bf16(x: float) -> int:
     return int(load().oracle_round_bf16(ctypes.c_float(x)))
+
+
+def round_bf16_bits(u: int) -> int:
+    """bf16 bits of the binary32 word u (passed as an integer, so NaN
+    payloads and signaling NaNs arrive unchanged)."""
+    return int(load().oracle_round_bf16_bits(ctypes.c_uint32(u)))
 
 
 def f32_to_e4m3(x: float) -> int:

@@ -65,7 +65,10 @@ static float oracle_bf16_to_f32(uint16_t b)
 /* binary32 -> bf16, round to nearest, ties to even. The 16 discarded bits
  * are compared with the halfway point 0x8000: above it rounds up, below it
  * truncates, and exactly at it rounds to the neighbour whose last kept bit
- * is zero. A NaN stays a quiet NaN with its sign. */
+ * is zero. A NaN is not rounded: it keeps its sign and the upper 7 bits
+ * of its fraction, with the quiet bit (the leading fraction bit) set, since
+ * IEEE 754 asks that a NaN result carry what of an input NaN's payload the
+ * format can hold and that a signaling NaN come out quiet. */
 static uint16_t oracle_f32_to_bf16(float f)
 {
     uint32_t u;
@@ -381,8 +384,17 @@ void oracle_combine_unpack(
     }
 }
 
-/* Exposed for the pins on the number format. */
+/* Exposed for the pins on the number format. The _bits form takes the
+ * binary32 word as an integer, so that a signaling NaN reaches the rounding
+ * unchanged (a float argument may be quieted on the way in). */
 uint16_t oracle_round_bf16(float f) { return oracle_f32_to_bf16(f); }
+
+uint16_t oracle_round_bf16_bits(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return oracle_f32_to_bf16(f);
+}
 
 /* ------------------------------------------------------------------ */
 /* Quantize-on-pack (the fp8 dispatch that the FlashInfer one-sided    */
@@ -422,12 +434,13 @@ uint8_t oracle_f32_to_e4m3(float f)
 
 /* Per-row, per-group fp8 quantisation of bf16 rows. For every group of
  * `group` consecutive columns: amax = max |x| over the non-NaN entries;
- * the stored scale is amax / 448 and the codes are q = e4m3(x * r) with
- * r = 448 / amax (both fp32 divisions and the product rounded to nearest);
- * scale = r = 1 when amax = 0. Each code carries the sign bit of its input
- * x (IEEE 754 leaves the sign of a NaN product open: a NaN input, or an
- * infinite one times r = 0, gives the NaN code with x's sign).
- * Dequantisation is q * scale. Row t of x at x + t*x_row_stride
+ * the scale is s = amax / 448 and each code is q = e4m3(x / s), both fp32
+ * divisions rounded to nearest and the quotient then encoded to nearest
+ * even (the plain scaled cast: divide by the scale in fp32, then convert);
+ * s = 1 when amax = 0. Each code carries the sign bit of its input x
+ * (IEEE 754 leaves the sign of a NaN quotient open: a NaN input, or an
+ * infinite one divided by an infinite scale, gives the NaN code with x's
+ * sign). Dequantisation is q * s. Row t of x at x + t*x_row_stride
  * (elements); codes of row t at q + t*q_row_stride (bytes); scales of row t
  * at scale + t*scale_row_stride (elements). */
 void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
@@ -444,11 +457,11 @@ void oracle_quantize_fp8(const uint16_t* x, int64_t T, int64_t H,
                     amax = v;
             }
             const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-            const float r = amax > 0.0f ? 448.0f / amax : 1.0f;
             scale[t * scale_row_stride + g] = s;
             for (int64_t h = g * group; h < (g + 1) * group && h < H; ++h) {
                 const float v = oracle_bf16_to_f32(x[t * x_row_stride + h]);
-                const uint8_t c = oracle_f32_to_e4m3(v * r);
+                const float y = v / s;
+                const uint8_t c = oracle_f32_to_e4m3(y);
                 q[t * q_row_stride + h] = (uint8_t)((c & 0x7Fu) | (signbit(v) ? 0x80u : 0u));
             }
         }
@@ -504,7 +517,8 @@ uint8_t oracle_f32_to_e2m1(float f)
  * bytes plus H/16 scale bytes per token). For every block: amax = max |x|;
  * the stored scale is the E4M3 code of amax / 6 (fp32 division, then
  * rounded to nearest even, saturating at 448); with s its value, the codes
- * are q = e2m1(x * r), r = 1 / s (fp32 division) or r = 0 when s = 0.
+ * are q = e2m1(x / s) (fp32 division rounded to nearest, then the E2M1
+ * encoding), or zeros when s = 0.
  * NaN entries do not take part in amax, and each code carries the sign
  * bit of its input x (a NaN input gives a zero of its sign).
  * Dequantisation is value(q) * s. Two codes per byte: the even column in
@@ -525,14 +539,15 @@ void oracle_quantize_fp4(const uint16_t* x, int64_t T, int64_t H,
             }
             const uint8_t s8 = oracle_f32_to_e4m3(amax / 6.0f);
             const float s = oracle_e4m3_to_f32(s8);
-            const float r = s > 0.0f ? 1.0f / s : 0.0f;
             scale[t * scale_row_stride + b] = s8;
             for (int64_t h = b * 16; h < b * 16 + 16; h += 2) {
                 const float v0 = oracle_bf16_to_f32(x[t * x_row_stride + h]);
                 const float v1 = oracle_bf16_to_f32(x[t * x_row_stride + h + 1]);
-                const uint8_t c0 = (uint8_t)((oracle_f32_to_e2m1(v0 * r) & 7u) |
+                const float y0 = s > 0.0f ? v0 / s : 0.0f;
+                const float y1 = s > 0.0f ? v1 / s : 0.0f;
+                const uint8_t c0 = (uint8_t)((oracle_f32_to_e2m1(y0) & 7u) |
                                              (signbit(v0) ? 8u : 0u));
-                const uint8_t c1 = (uint8_t)((oracle_f32_to_e2m1(v1 * r) & 7u) |
+                const uint8_t c1 = (uint8_t)((oracle_f32_to_e2m1(y1) & 7u) |
                                              (signbit(v1) ? 8u : 0u));
                 q[t * q_row_stride + h / 2] = (uint8_t)(c0 | (c1 << 4));
             }

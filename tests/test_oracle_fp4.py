@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import workloads as wl
-from test_oracle_fp8 import e4m3_value
+from test_oracle_fp8 import e4m3_nearest_even, e4m3_value, rn_f32
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 MAGS = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
@@ -81,6 +81,44 @@ def test_golden_fp4_rows():
         assert sc[0].tobytes().hex().upper() == row["scales_hex"]
 
 
+def e2m1_nearest_even(y: Fraction, negative: bool) -> int:
+    """E2M1 code of an exact value: nearest magnitude, ties to the even code,
+    saturating at 6; the sign bit as given."""
+    a = abs(y)
+    best = min(range(8), key=lambda c: (abs(a - Fraction(MAGS[c])), c & 1))
+    return (8 if negative else 0) | best
+
+
+def _codes_hex(codes):
+    return bytes(c0 | (c1 << 4) for c0, c1 in zip(codes[0::2], codes[1::2])).hex().upper()
+
+
+def test_golden_fp4_rows_rederived_in_exact_arithmetic():
+    """s = value(e4m3(fp32(amax / 6))) and code = e2m1(fp32(x / s)), every
+    rounding done on exact rationals here, give the golden codes and scale
+    codes; where a row lists the codes of x * fp32(1 / s), those differ."""
+    with open(os.path.join(GOLD, "fp4_quant.json")) as fh:
+        g = json.load(fh)
+    for row in g["rows"]:
+        vals = np.array(row["values"], np.float32)
+        codes, recip, scales = [], [], []
+        for b0 in range(0, len(vals), 16):
+            xs = [Fraction(float(v)) for v in vals[b0:b0 + 16]]
+            amax = max(abs(x) for x in xs)
+            s8 = e4m3_nearest_even(rn_f32(amax / 6)) if amax > 0 else 0
+            s = Fraction(e4m3_value(s8))
+            scales.append(s8)
+            r = rn_f32(1 / s) if s > 0 else Fraction(0)
+            for x, v in zip(xs, vals[b0:b0 + 16]):
+                neg = bool(np.signbit(v))
+                codes.append(e2m1_nearest_even(rn_f32(x / s) if s > 0 else Fraction(0), neg))
+                recip.append(e2m1_nearest_even(rn_f32(x * r), neg))
+        assert _codes_hex(codes) == row["codes_hex"]
+        assert bytes(scales).hex().upper() == row["scales_hex"]
+        if "times_reciprocal_codes_hex" in row:
+            assert _codes_hex(recip) == row["times_reciprocal_codes_hex"] != row["codes_hex"]
+
+
 def _rows(wid=2, T=64):
     w = wl.WORKLOADS[wid].scaled(T=T, cap=T)
     return w, wl.hidden_bf16(w, 0, 9)
@@ -97,7 +135,7 @@ def test_fp4_scales_are_e4m3_of_amax_over_6():
 
 
 def test_fp4_dequantisation_error_bound():
-    """|x - value(q) * s| <= half the E2M1 spacing at |x * r| (0.25, 0.5, 1
+    """|x - value(q) * s| <= half the E2M1 spacing at |x / s| (0.25, 0.5, 1
     below 2, 4, 6) times s; above 6 (the scale rounded down) the
     saturation error, at most 6 * 2^-4 / (1 - 2^-4) times s."""
     w, x = _rows(T=128)
@@ -144,10 +182,10 @@ def test_fp4_nonfinite_inputs():
     smaller values; an infinite amax saturates the scale at 448; every code
     carries its input's sign bit (a NaN gives a zero of its sign)."""
     row = np.zeros(32, np.uint16)
-    # block 0: -sNaN, +inf, 1.0, -2.0: amax = inf, scale 0x7E (448), r = 1/448
+    # block 0: -sNaN, +inf, 1.0, -2.0: amax = inf, scale 0x7E (s = 448)
     row[0:4] = [0xFFBC, 0x7F80, 0x3F80, 0xC000]
-    # block 1: 1.0, +sNaN, 0.5: amax = 1, 1/6 -> e4m3 0.171875 (0x23),
-    # r = 5.818: 1.0 -> 5.82 -> 7; 0.5 -> 2.91 -> 3 (code 5); NaN -> +0
+    # block 1: 1.0, +sNaN, 0.5: amax = 1, 1/6 -> e4m3 0.171875 (0x23):
+    # 1.0 / s = 5.82 -> 7; 0.5 / s = 2.91 -> 3 (code 5); NaN -> +0
     row[16:19] = [0x3F80, 0x7FA0, 0x3F00]
     q, sc = oracle.quantize_fp4(row[None, :])
     assert sc[0].tolist() == [0x7E, 0x23]

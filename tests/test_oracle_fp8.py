@@ -4,10 +4,13 @@ Independent references: the OCP E4M3 definition decoded code by code here
 (exponent bias 7, 3 fraction bits, subnormals, 448 the largest finite
 value), exact midpoints between neighbouring codes, torch's
 float8_e4m3fn conversion (a library routine) on random in-range values,
-and a hand-derived quantised row (tests/golden/fp8_quant.json).
+hand-derived quantised rows (tests/golden/fp8_quant.json), and the rule
+(s = fp32(amax / 448), code = e4m3(fp32(x / s))) re-derived in exact
+rational arithmetic.
 """
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -75,21 +78,82 @@ def test_matches_torch_conversion_in_range():
     assert np.array_equal(got, ref)
 
 
-def test_golden_quantized_row():
+def _golden_rows():
     with open(os.path.join(GOLD, "fp8_quant.json")) as fh:
         g = json.load(fh)
     H, group = g["H"], g["group"]
-    row = np.zeros(H, np.float32)
-    for k, v in g["row_values"].items():
-        row[int(k)] = v
-    bits = wl.f32_to_bf16_bits(row.reshape(1, H))
-    assert np.array_equal(wl.bf16_bits_to_f32(bits)[0], row)   # exact in bf16
-    q, sc = oracle.quantize_fp8(bits, group)
-    assert sc[0].tolist() == g["scales"]
-    exp = np.zeros(H, np.uint8)
-    for k, v in g["codes"].items():
-        exp[int(k)] = int(v, 16)
-    assert q[0].tolist() == exp.tolist()
+    for r in g["rows"]:
+        row = np.zeros(H, np.float32)
+        for k, v in r["row_values"].items():
+            row[int(k)] = v
+        bits = wl.f32_to_bf16_bits(row.reshape(1, H))
+        assert np.array_equal(wl.bf16_bits_to_f32(bits)[0], row)   # exact in bf16
+        exp = np.zeros(H, np.uint8)
+        for k, v in r["codes"].items():
+            exp[int(k)] = int(v, 16)
+        yield H, group, r, row, bits, exp
+
+
+def test_golden_quantized_row():
+    for H, group, r, row, bits, exp in _golden_rows():
+        q, sc = oracle.quantize_fp8(bits, group)
+        assert [hex(v) for v in sc[0].view(np.uint32)] == \
+            [hex(int(h, 16)) for h in r["scales_f32_hex"]]
+        assert q[0].tolist() == exp.tolist()
+
+
+def rn_f32(q: Fraction) -> Fraction:
+    """q rounded to binary32, nearest, ties to even (normal range only)."""
+    if q == 0:
+        return q
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                   # 2^e <= a < 2^(e+1)
+    assert -126 <= e <= 127
+    unit = Fraction(2) ** (e - 23)
+    n, rem = divmod(a, unit)
+    if rem * 2 > unit or (rem * 2 == unit and n % 2 == 1):
+        n += 1
+    return (n * unit) * (1 if q > 0 else -1)
+
+
+E4M3_POS = [(Fraction(e4m3_value(c)), c) for c in range(0x7F)]
+
+
+def e4m3_nearest_even(y: Fraction) -> int:
+    """The E4M3 code nearest to y, ties to the even code, magnitudes past
+    448 saturating to 448 (the sign taken from y)."""
+    a = min(abs(y), Fraction(448))
+    _, c = min(E4M3_POS, key=lambda vc: (abs(a - vc[0]), vc[1] & 1))
+    return c | (0x80 if y < 0 else 0)
+
+
+def test_golden_rows_rederived_in_exact_arithmetic():
+    """s = fp32(amax / 448) and code = e4m3(fp32(x / s)), both roundings done
+    on exact rationals here, give every code and scale of the golden rows;
+    the alternative rules listed with the rows give other codes."""
+    for H, group, r, row, bits, exp in _golden_rows():
+        for g0 in range(0, H, group):
+            xs = [Fraction(float(v)) for v in row[g0:g0 + group]]
+            amax = max(abs(v) for v in xs)
+            s = rn_f32(amax / 448) if amax > 0 else Fraction(1)
+            assert float(s) == float(np.uint32(int(r["scales_f32_hex"][g0 // group], 16))
+                                      .view(np.float32))
+            r448 = rn_f32(Fraction(448) / amax) if amax > 0 else Fraction(1)
+            for h, x in enumerate(xs):
+                col = g0 + h
+                code = e4m3_nearest_even(rn_f32(x / s)) if x != 0 else \
+                    (0x80 if np.signbit(row[col]) else 0)
+                assert code == exp[col], (col, hex(code), hex(exp[col]))
+                if str(col) in r.get("times_448_over_amax_codes", {}):
+                    other = e4m3_nearest_even(rn_f32(x * r448))
+                    assert other == int(r["times_448_over_amax_codes"][str(col)], 16)
+                    assert other != code
+                if str(col) in r.get("exact_quotient_codes", {}):
+                    other = e4m3_nearest_even(x / s)
+                    assert other == int(r["exact_quotient_codes"][str(col)], 16)
+                    assert other != code
 
 
 def test_quantize_dequantize_error_bound():

@@ -61,12 +61,15 @@ MUTANTS = {
     "quant_scale_wrong_divisor": (
         "const float s = amax > 0.0f ? amax / 448.0f : 1.0f;",
         "const float s = amax > 0.0f ? amax / 447.0f : 1.0f;"),
-    "quant_codes_wrong_multiplier": (
-        "const float r = amax > 0.0f ? 448.0f / amax : 1.0f;",
-        "const float r = amax > 0.0f ? 447.0f / amax : 1.0f;"),
     "quant_multiplies_by_scale": (
-        "const uint8_t c = oracle_f32_to_e4m3(v * r);",
-        "const uint8_t c = oracle_f32_to_e4m3(v * s);"),
+        "const float y = v / s;",
+        "const float y = v * s;"),
+    "quant_times_448_over_amax": (
+        "const float y = v / s;",
+        "const float y = v * (amax > 0.0f ? 448.0f / amax : 1.0f);"),
+    "quant_times_reciprocal_of_scale": (
+        "const float y = v / s;",
+        "const float y = v * (1.0f / s);"),
     "quant_sign_from_product": (
         "(uint8_t)((c & 0x7Fu) | (signbit(v) ? 0x80u : 0u));",
         "c;"),
@@ -110,8 +113,20 @@ MUTANTS = {
         "oracle_f32_to_e4m3(amax / 6.0f)",
         "oracle_f32_to_e4m3(amax / 4.0f)"),
     "fp4_codes_from_unrounded_scale": (
-        "const float r = s > 0.0f ? 1.0f / s : 0.0f;",
-        "const float r = amax > 0.0f ? 6.0f / amax : 0.0f;"),
+        "            const float s = oracle_e4m3_to_f32(s8);",
+        "            const float s = amax / 6.0f;"),
+    "fp4_times_reciprocal_of_scale": (
+        "const float y0 = s > 0.0f ? v0 / s : 0.0f;\n                const float y1 = s > 0.0f ? v1 / s : 0.0f;",
+        "const float y0 = s > 0.0f ? v0 * (1.0f / s) : 0.0f;\n                const float y1 = s > 0.0f ? v1 * (1.0f / s) : 0.0f;"),
+    "bf16_nan_drops_quiet_bit": (
+        "return (uint16_t)(kept | 0x0040u);",
+        "return (uint16_t)kept;"),
+    "bf16_nan_rounded_like_numbers": (
+        "    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)\n        return (uint16_t)(kept | 0x0040u);\n",
+        ""),
+    "bf16_nan_canonical": (
+        "return (uint16_t)(kept | 0x0040u);",
+        "return (uint16_t)0x7FC0u;"),
     "e4m3_decode_wrong_bias": (
         "v = ldexp(8.0 + f, e - 10);",
         "v = ldexp(8.0 + f, e - 9);"),
@@ -127,6 +142,7 @@ def _pin_battery():
         lambda: pins.test_golden_reduce("f32"),
         lambda: pins.test_golden_unpack("bf16"),
         pins.test_golden_bf16_rounding,
+        pins.test_golden_bf16_nan,
         lambda: pins.test_golden_products_rounded_before_add("bf16"),
         lambda: pins.test_pack_exhaustive_micro(2, 2),
         pins.test_combine_dense_brute_force_tiny,

@@ -138,6 +138,13 @@ def test_golden_bf16_rounding():
     g = _gold("rounding.json")["bf16_rne"]
     for fx, bx in g["cases_f32_hex_to_bf16_hex"]:
         assert oracle.round_bf16(float(_f32_from_hex(fx))) == _hex(bx), fx
+        assert oracle.round_bf16_bits(_hex(fx)) == _hex(bx), fx
+
+
+def test_golden_bf16_nan():
+    g = _gold("rounding.json")["bf16_nan"]
+    for fx, bx in g["cases_f32_hex_to_bf16_hex"]:
+        assert oracle.round_bf16_bits(_hex(fx)) == _hex(bx), fx
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
