@@ -67,13 +67,23 @@ __device__ __forceinline__ float group_max(float m, int lanes) {
 #endif
 constexpr int kQU = MOE_EP_QUANT_UNROLL;
 
+// fp32(x / s) for the reciprocal rd = 1 / s rounded to fp64. x * rd in
+// fp64 is within 2^-52 (relative) of x / s, while the quotient of two
+// binary32 numbers is never a binary32 midpoint and lies at least 2^-49
+// (relative) away from every midpoint; so rounding the fp64 product to
+// binary32 gives the correctly rounded quotient, for one fp64 multiply per
+// element instead of a division.
+__device__ __forceinline__ float div_by(float x, double rd) {
+    return (float)((double)x * rd);
+}
+
 // One pass of the quantiser over a bf16 row. A lane unit i covers the 16
 // columns 16i .. 16i+15 (two 16-byte loads of bf16, one 16-byte store of
 // codes); the lane's units are i = base + u*kPackThreads + tid, u < kQU,
-// below hi. For a group with amax > 0 the scale is amax / 448 and each code
-// is e4m3(x * r) with r = 448 / amax (correctly rounded divisions, the
-// product rounded to nearest, the hardware conversion to nearest even);
-// scale = r = 1 when amax = 0. base and hi are multiples of the group's
+// below hi. For a group with amax > 0 the scale is s = amax / 448 and each
+// code is e4m3(x / s) (the division correctly rounded to fp32, div_by,
+// then the hardware conversion to nearest even); s = 1 when amax = 0.
+// base and hi are multiples of the group's
 // units, so a group's units sit in consecutive, aligned lanes and its amax
 // is a reduction within a DPP row. The row's loads are all issued first.
 // NaN entries never become the amax (a compare-and-select, not fmaxf,
@@ -119,14 +129,17 @@ __device__ __forceinline__ void quantize_pass(const uint8_t* __restrict__ src,
             for (int c = 0; c < 16; ++c) m = abs_max(m, f[c]);
         }
         m = group_max(m, gu);
-        out.scale[u] = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
-        const float r = m > 0.0f ? __fdiv_rn(448.0f, m) : 1.0f;
+        const float s = m > 0.0f ? __fdiv_rn(m, 448.0f) : 1.0f;
+        out.scale[u] = s;
+        // an infinite amax gives rd = 0: finite x -> 0, infinite x -> NaN,
+        // as x / s would
+        const double rd = 1.0 / (double)s;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const int lo16 = __builtin_amdgcn_cvt_pk_fp8_f32(
-                __fmul_rn(f[4 * w], r), __fmul_rn(f[4 * w + 1], r), 0, false);
+                div_by(f[4 * w], rd), div_by(f[4 * w + 1], rd), 0, false);
             const uint32_t codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-                __fmul_rn(f[4 * w + 2], r), __fmul_rn(f[4 * w + 3], r), lo16, true);
+                div_by(f[4 * w + 2], rd), div_by(f[4 * w + 3], rd), lo16, true);
             const uint32_t signs = ((__float_as_uint(f[4 * w]) >> 24) & 0x80u) |
                                    ((__float_as_uint(f[4 * w + 1]) >> 16) & 0x8000u) |
                                    ((__float_as_uint(f[4 * w + 2]) >> 8) & 0x800000u) |
@@ -137,10 +150,11 @@ __device__ __forceinline__ void quantize_pass(const uint8_t* __restrict__ src,
 }
 
 // 4-bit pass: a lane unit i covers columns 16i .. 16i+15, which are one
-// scale block. amax is lane-local (NaN entries skipped, as above); the scale code is the hardware OCP e4m3
-// conversion of amax / 6 (correctly rounded division, then nearest even,
-// saturating at 448); with s its value, r = 1 / s (0 when s = 0) and each
-// code is the E2M1 code of x * r (product rounded to nearest).
+// scale block. amax is lane-local (NaN entries skipped, as above); the
+// scale code is the hardware OCP e4m3 conversion of amax / 6 (correctly
+// rounded division, then nearest even, saturating at 448); with s its
+// value each code is the E2M1 code of fp32(x / s) (div_by with
+// rd = 1 / s), or a zero of x's sign when s = 0 (rd = 0).
 struct Fp4Pass {
     u32x2 codes[kQU];
     uint32_t scale[kQU];
@@ -166,38 +180,38 @@ __device__ __forceinline__ uint32_t e2m1_code(float y, float x) {
     return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
-// The E2M1 codes of x[c] * r for 8 values, two per byte (x[0] in the low
-// nibble of byte 0). gfx950's pair conversion (v_cvt_scalef32_pk_fp4_f32,
+// The E2M1 codes of fp32(x[c] / s) for 8 values, two per byte (x[0] in the
+// low nibble of byte 0). gfx950's pair conversion (v_cvt_scalef32_pk_fp4_f32,
 // scale 1) rounds to nearest even and saturates at 6 like e2m1_code, but
-// turns a NaN into the largest code; a NaN product is therefore replaced by
-// a zero with x's sign first, which gives e2m1_code's result on every input.
-// (0: e2m1_code for each value.)
+// turns a NaN into the largest code; a NaN quotient is therefore replaced
+// by a zero with x's sign first, which gives e2m1_code's result on every
+// input. (0: e2m1_code for each value.)
 #ifndef MOE_EP_HW_FP4
 #define MOE_EP_HW_FP4 1
 #endif
-// x * r, or a zero with x's sign when that is NaN
-__device__ __forceinline__ float scaled_or_zero(float x, float r) {
-    const float y = __fmul_rn(x, r);
+// fp32(x / s) (x * 0 when s = 0), or a zero with x's sign when that is NaN
+__device__ __forceinline__ float scaled_or_zero(float x, double rd) {
+    const float y = div_by(x, rd);
     return y == y ? y : __uint_as_float(__float_as_uint(x) & 0x80000000u);
 }
 
 // byte SEL of word <- the codes of the pair (x[2*SEL], x[2*SEL+1])
 template <int SEL>
-__device__ __forceinline__ uint32_t e2m1_pair(uint32_t word, const float* x, float r) {
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t word, const float* x, double rd) {
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-        word, scaled_or_zero(x[2 * SEL], r), scaled_or_zero(x[2 * SEL + 1], r), 1.0f, SEL);
+        word, scaled_or_zero(x[2 * SEL], rd), scaled_or_zero(x[2 * SEL + 1], rd), 1.0f, SEL);
 }
 
-__device__ __forceinline__ uint32_t e2m1_word(const float* x, float r) {
+__device__ __forceinline__ uint32_t e2m1_word(const float* x, double rd) {
     uint32_t word = 0;
     if (MOE_EP_HW_FP4) {
-        word = e2m1_pair<0>(word, x, r);
-        word = e2m1_pair<1>(word, x, r);
-        word = e2m1_pair<2>(word, x, r);
-        word = e2m1_pair<3>(word, x, r);
+        word = e2m1_pair<0>(word, x, rd);
+        word = e2m1_pair<1>(word, x, rd);
+        word = e2m1_pair<2>(word, x, rd);
+        word = e2m1_pair<3>(word, x, rd);
     } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) word |= e2m1_code(__fmul_rn(x[c], r), x[c]) << (4 * c);
+        for (int c = 0; c < 8; ++c) word |= e2m1_code(div_by(x[c], rd), x[c]) << (4 * c);
     }
     return word;
 }
@@ -234,10 +248,10 @@ __device__ __forceinline__ void quantize_pass_fp4(const uint8_t* __restrict__ sr
         const uint32_t s8 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
                                 fminf(__fdiv_rn(m, 6.0f), 448.0f), 0.0f, 0, false) & 0xFFu;
         const float sv = e4m3_value(s8);
-        const float r = sv > 0.0f ? __fdiv_rn(1.0f, sv) : 0.0f;
+        const double rd = sv > 0.0f ? 1.0 / (double)sv : 0.0;
         out.scale[u] = s8;
-        out.codes[u][0] = e2m1_word(f, r);
-        out.codes[u][1] = e2m1_word(f + 8, r);
+        out.codes[u][0] = e2m1_word(f, rd);
+        out.codes[u][1] = e2m1_word(f + 8, rd);
     }
 }
 

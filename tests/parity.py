@@ -245,9 +245,14 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
 # ---------------------------------------------------------------------------
 
 def column_windows(nbytes: int, width: int = 64):
-    """Byte windows of a row: the start, the 4 KiB boundary of one pass of
-    256 lanes x 16 B, the middle and the end (16-byte aligned)."""
-    starts = {0, 4096 - width // 2, (nbytes // 2) // 16 * 16, nbytes - width}
+    """Byte windows of a row: the start, the middle, the end, and in every
+    4 KiB pass of 256 lanes x 16 B one window across its start and one in
+    its middle (16-byte aligned), so each vector pass of every kernel is
+    compared."""
+    starts = {0, (nbytes // 2) // 16 * 16, nbytes - width}
+    for k in range(0, nbytes, 4096):
+        starts.add(max(0, k - width // 2))
+        starts.add(k + 2048)
     out = []
     for s in sorted(starts):
         s = max(0, min(s, nbytes - width)) // 16 * 16

@@ -47,6 +47,9 @@ CASES = {
     # 288 vectors in bf16, 576 in fp32 (above the 512 that switch the
     # combine kernels to 4 vectors per lane)
     "whole_row_unpack": W1.scaled(W=4, E=16, K=4, T=2100, cap=2100, H=2304),
+    # more than 64 routing tiles of 256 tokens (67): the send side takes the
+    # column scan for send_cnt and the tile offsets it writes
+    "many_route_tiles": W1.scaled(W=4, E=16, K=4, T=17000, cap=17000, H=128),
 }
 
 
@@ -121,6 +124,7 @@ FP8_CASES = {
     "decode": W4,
     "w64": W1.scaled(W=64, E=128, K=4, T=90, cap=96, H=128),
     "empty": W1.scaled(T=0, cap=16),
+    "many_route_tiles": CASES["many_route_tiles"],
 }
 
 
@@ -226,11 +230,84 @@ def test_fp4_every_bf16_bit_pattern():
         raise
 
 
+def _e4m3_positive_values():
+    vals = []
+    for c in range(0x7F):
+        e, f = c >> 3, c & 7
+        vals.append((f / 8) * 2.0 ** -6 if e == 0 else (1 + f / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def _bf16_nearest(v: np.ndarray) -> np.ndarray:
+    return wl.f32_to_bf16_bits(np.asarray(v, np.float32))
+
+
+def test_fp8_quotients_near_midpoints():
+    """Groups whose scale is not a power of two and whose entries make x / s
+    land on or next to every E4M3 midpoint: for each amax (every bf16
+    significand in [1, 2) at three exponents) the group holds amax and, per
+    midpoint m between neighbouring codes, the bf16 value nearest to
+    m * amax / 448. Here x / s and x * (448 / amax) often round to different
+    codes; the kernel's codes must be the oracle's (fp32 quotient, then
+    nearest even)."""
+    vals = _e4m3_positive_values()
+    mids = (vals[:-1] + vals[1:]) / 2                     # 126 midpoints
+    group, groups = 128, []
+    for ex in (-3, 0, 5):
+        for m7 in range(128):
+            amax = (1 + m7 / 128) * 2.0 ** ex
+            g = np.zeros(group, np.uint16)
+            g[0] = _bf16_nearest(np.array([amax]))[0]
+            x = _bf16_nearest(mids * amax / 448.0)
+            g[1:1 + len(x)] = x
+            g[1 + len(x)] = x[len(x) // 2] | 0x8000          # one negative
+            groups.append(g)
+    H = 1024
+    rows = np.stack(groups).reshape(-1, H)
+    T = rows.shape[0]
+    w = W1.scaled(W=1, E=2, K=1, T=T, cap=T, H=H, pad_frac=0.0)
+    ids = np.zeros((T, 1), np.int32)
+    wts = np.ones((T, 1), np.float32)
+    say(f"[fp8 midpoints] {len(groups)} groups in {T} rows")
+    run_full_parity(w, srcs=[(ids, wts)],
+                    pls=[[rows.view(np.uint8).reshape(T, 2 * H)]], fp8_group=group)
+
+
+def test_fp4_quotients_at_midpoints():
+    """Blocks of 16 whose scale s = value(e4m3(amax / 6)) runs over every
+    E4M3 code reachable from a bf16 amax = 6 s, holding amax and, per E2M1
+    midpoint m (0.25 .. 5) and sign, the bf16 value nearest to m * s (exactly
+    m * s where that is a bf16 value: a tie that x * fp32(1 / s) would break
+    the wrong way where 1 / s is inexact). Codes bit-exact with the oracle."""
+    vals = _e4m3_positive_values()
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    blocks = []
+    for s in vals[1:]:
+        b = np.zeros(16, np.uint16)
+        b[0] = _bf16_nearest(np.array([6.0 * s]))[0]
+        x = _bf16_nearest(mids * s)
+        b[1:8] = x
+        b[8:15] = x | 0x8000
+        blocks.append(b)
+    H = 512
+    n = -(-len(blocks) // (H // 16)) * (H // 16)
+    blocks += [np.zeros(16, np.uint16)] * (n - len(blocks))
+    rows = np.stack(blocks).reshape(-1, H)
+    T = rows.shape[0]
+    w = W1.scaled(W=1, E=2, K=1, T=T, cap=T, H=H, pad_frac=0.0)
+    ids = np.zeros((T, 1), np.int32)
+    wts = np.ones((T, 1), np.float32)
+    say(f"[fp4 midpoints] {len(vals) - 1} scales in {T} rows")
+    run_full_parity(w, srcs=[(ids, wts)],
+                    pls=[[rows.view(np.uint8).reshape(T, 2 * H)]], fp4=True)
+
+
 def test_fp8_every_bf16_bit_pattern():
     """All 65,536 bf16 bit patterns through the fp8 quantiser (groups of
     128): NaN entries never set a group's amax; groups with an infinite
-    amax get scale inf and r = 0; codes carry their input's sign. Codes and
-    scales bit-exact with the oracle."""
+    amax get scale inf (finite entries give zero codes, infinite ones the
+    NaN code); codes carry their input's sign. Codes and scales bit-exact
+    with the oracle."""
     rng = np.random.default_rng(43)
     vals = rng.permutation(np.arange(0x10000, dtype=np.uint32)).astype(np.uint16)
     H = 1024
