@@ -76,10 +76,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_ep_status_string.restype = ctypes.c_char_p
     lib.moe_ep_dispatch_pack.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
-        _P, _P, _P, _P, _P, _P, _SZ, _P]
+        _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
     lib.moe_ep_dispatch_pack_fp8.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I64, _I64, _I32,
-        _P, _I64, _P, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        _P, _I64, _P, _I64, _P, _I32, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
     lib.moe_ep_expert_batch.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
         _P, _P, _P, _P, _SZ, _P]
@@ -89,7 +89,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32, _P, _P, _P, _SZ, _P]
     lib.moe_ep_dispatch_pack_fp4.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I64, _I64, _P, _I64, _P, _I64,
-        _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        _P, _I32, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
     lib.moe_ep_sanitize_expert_ids.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _I32, _P, _I64, _P, _P]
     lib.moe_ep_combine_reduce.argtypes = [
@@ -179,16 +179,21 @@ def moe_ep_workspace_bytes(T: int, K: int, E: int, W: int, max_num_tokens: int) 
 # The four calls of the path
 # ---------------------------------------------------------------------------
 
-def _payload_array(pairs, src_row_dim: int, dst_row_dim: int):
+def _payload_array(pairs, src_row_dim: int, dst_row_dim: int,
+                   src_lead: Sequence[int] = (), dst_lead: Sequence[int] = ()):
     """Descriptors for (src, dst) pairs whose dim 0 is the strided leading
     dim and whose dims from 1 on are dense; a row spans the dims from
-    src_row_dim (dst_row_dim) on."""
+    src_row_dim (dst_row_dim) on. src_lead / dst_lead: least sizes of the
+    dims before the row (the leading dim and, for [W, cap, row] blocks, the
+    rows per block)."""
     if len(pairs) > MAX_PAYLOADS:
         raise ValueError("too many payloads")
     arr = (MoeEpPayload * MAX_PAYLOADS)()
     for i, (src, dst) in enumerate(pairs):
         _dense_from(src, 1, "payload src")
         _dense_from(dst, 1, "payload dst")
+        _lead_at_least(src, src_lead, f"payload {i} src")
+        _lead_at_least(dst, dst_lead, f"payload {i} dst")
         rb = _row_bytes(src, src_row_dim)
         if _row_bytes(dst, dst_row_dim) != rb:
             raise ValueError("payload src and dst rows differ in size")
@@ -200,13 +205,101 @@ def _payload_array(pairs, src_row_dim: int, dst_row_dim: int):
     return arr
 
 
-def _tensors(x):
-    """The tensors in a nest of tuples and lists."""
-    if isinstance(x, torch.Tensor):
-        yield x
-    elif isinstance(x, (tuple, list)):
-        for y in x:
-            yield from _tensors(y)
+# ---------------------------------------------------------------------------
+# Shape checks. The C ABI sees pointers and strides only, so a tensor of the
+# wrong size would be read or written out of bounds on the device; every
+# prepare_* function checks sizes here first and raises ValueError (before
+# the one-GPU check, so that host tensors can stand in for the shapes).
+# ---------------------------------------------------------------------------
+
+def _lead_at_least(t: torch.Tensor, mins: Sequence[int], name: str):
+    if t.dim() < len(mins) or any(t.size(i) < m for i, m in enumerate(mins)):
+        raise ValueError(f"{name}: leading dims {tuple(t.shape[:len(mins)])} "
+                         f"must be at least {tuple(mins)}")
+
+
+def _shape(t: Optional[torch.Tensor], shape: Sequence[int], name: str, dtypes=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+
+
+def _blocks(t: torch.Tensor, n: int, block_elems: int, name: str, dtypes=None):
+    """n blocks along dim 0 (any stride), each a dense run of block_elems
+    elements."""
+    if t.dim() < 1 or t.size(0) != n:
+        raise ValueError(f"{name}: {n} blocks along dim 0 expected, shape {tuple(t.shape)}")
+    per = 1
+    for x in t.shape[1:]:
+        per *= x
+    if per != block_elems:
+        raise ValueError(f"{name}: blocks of {per} elements, expected {block_elems}")
+    _dense_from(t, 1, name)
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+
+
+def _vector(t: torch.Tensor, n: int, name: str, dtypes=None):
+    """At least n elements along one dim (any stride)."""
+    if t.dim() != 1 or t.size(0) < n:
+        raise ValueError(f"{name}: a vector of at least {n} elements expected, "
+                         f"shape {tuple(t.shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+
+
+def _err(err_flags: Optional[torch.Tensor]):
+    if err_flags is not None:
+        _vector(err_flags, 1, "err_flags", _I32T)
+
+
+_I32T = (torch.int32,)
+_F32T = (torch.float32,)
+
+
+def _sizes(K: int, E: int, W: int, max_num_tokens: int):
+    """e_local, slots, cap, expert_cap as capacities() forms them."""
+    if K <= 0 or E <= 0 or W <= 0 or E % W or max_num_tokens < 0:
+        raise ValueError(f"bad sizes K={K} E={E} W={W} max_num_tokens={max_num_tokens}")
+    e_local = E // W
+    return e_local, min(K, e_local), max_num_tokens, max_num_tokens * W
+
+
+def _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt, send_eloc,
+               send_w, token_slot, err_flags):
+    """Checks the routing inputs and metadata outputs of a pack call;
+    returns (T, K, cap, slots). send_eloc / send_w: [W, cap, slots] with a
+    free rank stride, shared by both."""
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, K]")
+    T, K = topk_ids.shape
+    _, slots, cap, _ = _sizes(K, E, W, max_num_tokens)
+    _shape(topk_ids, (T, K), "topk_ids", _I32T)
+    _shape(topk_weights, (T, K), "topk_weights", _F32T)
+    _dense_from(topk_ids, 0, "topk_ids")
+    _dense_from(topk_weights, 0, "topk_weights")
+    _vector(send_cnt, W, "send_cnt", _I32T)
+    _dense_from(send_cnt, 0, "send_cnt")
+    _blocks(send_eloc, W, cap * slots, "send_eloc", _I32T)
+    _blocks(send_w, W, cap * slots, "send_w", _F32T)
+    if send_eloc.stride(0) != send_w.stride(0):
+        raise ValueError("send_eloc and send_w must share a rank stride")
+    _shape(token_slot, (T, W), "token_slot", _I32T)
+    _dense_from(token_slot, 0, "token_slot")
+    _err(err_flags)
+    return T, K, cap, slots
+
+
+def _receive_side(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens):
+    """Checks the received counts and local ids; returns (slots, cap,
+    expert_cap)."""
+    _, slots, cap, ecap = _sizes(K, e_local * W, W, max_num_tokens)
+    _vector(recv_cnt, W, "recv_cnt", _I32T)
+    _blocks(recv_eloc, W, cap * slots, "recv_eloc", _I32T)
+    return slots, cap, ecap
 
 
 class PreparedCall:
@@ -237,6 +330,19 @@ class PreparedCall:
         _check(self.name, self.fn(*self.args, _stream(stream)))
 
 
+def _tensors(x):
+    """The tensors in a nest of tuples and lists."""
+    if isinstance(x, torch.Tensor):
+        yield x
+    elif isinstance(x, (tuple, list)):
+        for y in x:
+            yield from _tensors(y)
+
+
+def _ws_bytes(workspace: torch.Tensor) -> int:
+    return workspace.numel() * workspace.element_size()
+
+
 def prepare_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                           E: int, W: int, max_num_tokens: int,
                           payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
@@ -244,18 +350,16 @@ def prepare_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                           send_w: torch.Tensor, token_slot: torch.Tensor,
                           err_flags: Optional[torch.Tensor],
                           workspace: torch.Tensor) -> PreparedCall:
-    """payloads: (src [T, ...], dst [W, cap, ...]) pairs; the rank stride of
-    dst is free, everything below it dense."""
-    T, K = topk_ids.shape
-    for t, n in ((topk_ids, "topk_ids"), (topk_weights, "topk_weights"),
-                 (send_eloc, "send_eloc"), (send_w, "send_w"),
-                 (token_slot, "token_slot"), (send_cnt, "send_cnt")):
-        _dense_from(t, 0, n)
-    arr = _payload_array(payloads, 1, 2)
+    """payloads: (src [T, ...], dst [W, cap, ...]) pairs; send_eloc /
+    send_w: [W, cap, slots] with one free rank stride (meta_rank_stride);
+    the rank stride of each dst is free, everything below it dense."""
+    T, K, cap, _ = _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt,
+                              send_eloc, send_w, token_slot, err_flags)
+    arr = _payload_array(payloads, 1, 2, (T,), (W, cap))
     args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
             ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
-            _ptr(send_w), _ptr(token_slot), _ptr(err_flags), _ptr(workspace),
-            workspace.numel() * workspace.element_size())
+            _ptr(send_w), send_eloc.stride(0), _ptr(token_slot), _ptr(err_flags),
+            _ptr(workspace), _ws_bytes(workspace))
     return PreparedCall("moe_ep_dispatch_pack", args,
                         (arr, topk_ids, topk_weights, payloads, send_cnt, send_eloc,
                          send_w, token_slot, err_flags, workspace))
@@ -278,27 +382,30 @@ def prepare_dispatch_pack_fp8(topk_ids: torch.Tensor, topk_weights: torch.Tensor
     """hidden: bf16 [T, H] (token stride free, rows dense); send_q: fp8 codes
     [W, cap, H] (uint8 or float8, rank stride free); send_scale: fp32
     [W, cap, Gp], Gp = H/group rounded up to 4 (rank stride free)."""
-    T, K = topk_ids.shape
+    T, K, cap, _ = _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt,
+                              send_eloc, send_w, token_slot, err_flags)
     if hidden.dtype != torch.bfloat16:
         raise ValueError("hidden must be bfloat16")
-    for t, n in ((topk_ids, "topk_ids"), (topk_weights, "topk_weights"),
-                 (send_eloc, "send_eloc"), (send_w, "send_w"),
-                 (token_slot, "token_slot"), (send_cnt, "send_cnt")):
-        _dense_from(t, 0, n)
+    if hidden.dim() != 2 or hidden.size(0) < T:
+        raise ValueError("hidden must be [T, H]")
     _dense_from(hidden, 1, "hidden")
+    H = hidden.size(1)
+    if group <= 0:
+        raise ValueError("group must be positive")
+    if send_q.element_size() != 1:
+        raise ValueError("send_q must hold one byte per code")
+    _shape(send_q, (W, cap, H), "send_q")
+    _shape(send_scale, (W, cap, scale_pitch(H, group)), "send_scale", _F32T)
     _dense_from(send_q, 1, "send_q")
     _dense_from(send_scale, 1, "send_scale")
-    H = hidden.size(1)
-    if send_scale.size(-1) != scale_pitch(H, group):
-        raise ValueError("send_scale rows must hold scale_pitch(H, group) floats")
-    arr = _payload_array(payloads, 1, 2)
+    arr = _payload_array(payloads, 1, 2, (T,), (W, cap))
     args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
             _ptr(hidden), hidden.stride(0) * 2, H, group,
             _ptr(send_q), send_q.stride(0) * send_q.element_size(),
             _ptr(send_scale), send_scale.stride(0),
             ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
-            _ptr(send_w), _ptr(token_slot), _ptr(err_flags), _ptr(workspace),
-            workspace.numel() * workspace.element_size())
+            _ptr(send_w), send_eloc.stride(0), _ptr(token_slot), _ptr(err_flags),
+            _ptr(workspace), _ws_bytes(workspace))
     return PreparedCall("moe_ep_dispatch_pack_fp8", args,
                         (arr, topk_ids, topk_weights, hidden, send_q, send_scale,
                          payloads, send_cnt, send_eloc, send_w, token_slot,
@@ -332,28 +439,31 @@ def prepare_dispatch_pack_fp4(topk_ids: torch.Tensor, topk_weights: torch.Tensor
     """hidden: bf16 [T, H] (token stride free, rows dense); send_q: codes
     [W, cap, H/2] bytes; send_scale: e4m3 scale codes [W, cap, Sp] bytes,
     Sp = fp4_scale_pitch(H) (rank strides free)."""
-    T, K = topk_ids.shape
+    T, K, cap, _ = _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt,
+                              send_eloc, send_w, token_slot, err_flags)
     if hidden.dtype != torch.bfloat16:
         raise ValueError("hidden must be bfloat16")
-    for t, n in ((topk_ids, "topk_ids"), (topk_weights, "topk_weights"),
-                 (send_eloc, "send_eloc"), (send_w, "send_w"),
-                 (token_slot, "token_slot"), (send_cnt, "send_cnt")):
-        _dense_from(t, 0, n)
+    if hidden.dim() != 2 or hidden.size(0) < T:
+        raise ValueError("hidden must be [T, H]")
     for t, n in ((hidden, "hidden"), (send_q, "send_q"), (send_scale, "send_scale")):
         _dense_from(t, 1, n)
     H = hidden.size(1)
+    if send_q.dim() != 3 or send_scale.dim() != 3:
+        raise ValueError("send_q and send_scale must be [W, cap, bytes]")
+    if tuple(send_q.shape[:2]) != (W, cap) or tuple(send_scale.shape[:2]) != (W, cap):
+        raise ValueError("send_q and send_scale must have W x cap rows")
     if send_q.size(-1) * send_q.element_size() != H // 2:
         raise ValueError("send_q rows must hold H/2 bytes")
     if send_scale.size(-1) * send_scale.element_size() != fp4_scale_pitch(H):
         raise ValueError("send_scale rows must hold fp4_scale_pitch(H) bytes")
-    arr = _payload_array(payloads, 1, 2)
+    arr = _payload_array(payloads, 1, 2, (T,), (W, cap))
     args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
             _ptr(hidden), hidden.stride(0) * 2, H,
             _ptr(send_q), send_q.stride(0) * send_q.element_size(),
             _ptr(send_scale), send_scale.stride(0) * send_scale.element_size(),
             ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
-            _ptr(send_w), _ptr(token_slot), _ptr(err_flags), _ptr(workspace),
-            workspace.numel() * workspace.element_size())
+            _ptr(send_w), send_eloc.stride(0), _ptr(token_slot), _ptr(err_flags),
+            _ptr(workspace), _ws_bytes(workspace))
     return PreparedCall("moe_ep_dispatch_pack_fp4", args,
                         (arr, topk_ids, topk_weights, hidden, send_q, send_scale,
                          payloads, send_cnt, send_eloc, send_w, token_slot,
@@ -385,14 +495,17 @@ def prepare_expert_batch(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
                          workspace: torch.Tensor) -> PreparedCall:
     """recv_cnt: [W] view (any stride); recv_eloc: [W, cap, slots] view (rank
     stride free); payloads: (src [W, cap, ...], dst [e_local, W*cap, ...])."""
-    _dense_from(recv_eloc, 1, "recv_eloc")
+    slots, cap, ecap = _receive_side(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens)
+    _shape(recv_row, (W, cap, slots), "recv_row", _I32T)
     _dense_from(recv_row, 0, "recv_row")
+    _shape(expert_num_tokens, (e_local,), "expert_num_tokens", _I32T)
     _dense_from(expert_num_tokens, 0, "expert_num_tokens")
-    arr = _payload_array(payloads, 2, 2)
+    _err(err_flags)
+    arr = _payload_array(payloads, 2, 2, (W, cap), (e_local, ecap))
     args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
             W, e_local, K, max_num_tokens, ctypes.addressof(arr), len(payloads),
             _ptr(expert_num_tokens), _ptr(recv_row), _ptr(err_flags), _ptr(workspace),
-            workspace.numel() * workspace.element_size())
+            _ws_bytes(workspace))
     return PreparedCall("moe_ep_expert_batch", args,
                         (arr, recv_cnt, recv_eloc, payloads, expert_num_tokens,
                          recv_row, err_flags, workspace))
@@ -412,13 +525,15 @@ def prepare_expert_batch_plan(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
                               err_flags: Optional[torch.Tensor],
                               workspace: torch.Tensor) -> PreparedCall:
     """The receive scan half of moe_ep_expert_batch."""
-    _dense_from(recv_eloc, 1, "recv_eloc")
+    slots, cap, _ = _receive_side(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens)
+    _shape(recv_row, (W, cap, slots), "recv_row", _I32T)
     _dense_from(recv_row, 0, "recv_row")
+    _shape(expert_num_tokens, (e_local,), "expert_num_tokens", _I32T)
     _dense_from(expert_num_tokens, 0, "expert_num_tokens")
+    _err(err_flags)
     args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
             W, e_local, K, max_num_tokens, _ptr(expert_num_tokens), _ptr(recv_row),
-            _ptr(err_flags), _ptr(workspace),
-            workspace.numel() * workspace.element_size())
+            _ptr(err_flags), _ptr(workspace), _ws_bytes(workspace))
     return PreparedCall("moe_ep_expert_batch_plan", args,
                         (recv_cnt, recv_eloc, expert_num_tokens, recv_row,
                          err_flags, workspace))
@@ -431,13 +546,14 @@ def prepare_expert_batch_copy(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
                               err_flags: Optional[torch.Tensor],
                               workspace: torch.Tensor) -> PreparedCall:
     """The row copy half of moe_ep_expert_batch (after the plan)."""
-    _dense_from(recv_eloc, 1, "recv_eloc")
+    slots, cap, ecap = _receive_side(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens)
+    _shape(recv_row, (W, cap, slots), "recv_row", _I32T)
     _dense_from(recv_row, 0, "recv_row")
-    arr = _payload_array(payloads, 2, 2)
+    _err(err_flags)
+    arr = _payload_array(payloads, 2, 2, (W, cap), (e_local, ecap))
     args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
             W, e_local, K, max_num_tokens, ctypes.addressof(arr), len(payloads),
-            _ptr(recv_row), _ptr(err_flags), _ptr(workspace),
-            workspace.numel() * workspace.element_size())
+            _ptr(recv_row), _ptr(err_flags), _ptr(workspace), _ws_bytes(workspace))
     return PreparedCall("moe_ep_expert_batch_copy", args,
                         (arr, recv_cnt, recv_eloc, payloads, recv_row, err_flags,
                          workspace))
@@ -463,8 +579,9 @@ def prepare_sanitize_expert_ids(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
                                 err_flags: Optional[torch.Tensor]) -> PreparedCall:
     """recv_eloc / out: [W, cap, slots] views (rank stride free); out may be
     recv_eloc itself."""
-    _dense_from(recv_eloc, 1, "recv_eloc")
-    _dense_from(out, 1, "out")
+    slots, cap, _ = _receive_side(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens)
+    _blocks(out, W, cap * slots, "out", _I32T)
+    _err(err_flags)
     args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), recv_eloc.stride(0),
             W, e_local, K, max_num_tokens, invalid_id, _ptr(out), out.stride(0),
             _ptr(err_flags))
@@ -490,14 +607,19 @@ def prepare_combine_reduce(expert_out: torch.Tensor, recv_cnt: torch.Tensor,
     dt = _dtype_code(expert_out)
     if ret.dtype != expert_out.dtype:
         raise ValueError("ret and expert_out differ in dtype")
-    _dense_from(expert_out, 1, "expert_out")
-    _dense_from(ret, 1, "ret")
-    _dense_from(recv_eloc, 1, "recv_eloc")
-    _dense_from(recv_w, 1, "recv_w")
-    _dense_from(recv_row, 0, "recv_row")
+    slots, cap, ecap = _receive_side(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens)
+    _blocks(recv_w, W, cap * slots, "recv_w", _F32T)
     if recv_eloc.stride(0) != recv_w.stride(0):
         raise ValueError("recv_eloc and recv_w must share a rank stride")
+    _shape(recv_row, (W, cap, slots), "recv_row", _I32T)
+    _dense_from(recv_row, 0, "recv_row")
+    if expert_out.dim() != 3:
+        raise ValueError("expert_out must be [e_local, W*cap, H]")
     H = expert_out.size(2)
+    _lead_at_least(expert_out, (e_local, ecap), "expert_out")
+    _shape(ret, (W, cap, H), "ret")
+    _dense_from(expert_out, 1, "expert_out")
+    _dense_from(ret, 1, "ret")
     head = (_ptr(expert_out), expert_out.stride(0), dt, H, _ptr(recv_cnt),
             recv_cnt.stride(0), _ptr(recv_eloc), _ptr(recv_w), recv_eloc.stride(0),
             _ptr(recv_row), W, e_local, K, max_num_tokens)
@@ -515,6 +637,25 @@ def moe_ep_combine_reduce(expert_out, recv_cnt, recv_eloc, recv_w, recv_row, W,
                            e_local, K, max_num_tokens, ret)(stream)
 
 
+def _unpack_side(back: torch.Tensor, token_slot: torch.Tensor, max_num_tokens: int,
+                 out: torch.Tensor):
+    """Checks the returned partials, the context and the output of an
+    unpack; returns (T, W, H)."""
+    if token_slot.dim() != 2:
+        raise ValueError("token_slot must be [T, W]")
+    T, W = token_slot.shape
+    if back.dim() != 3:
+        raise ValueError("back must be [W, cap, H]")
+    H = back.size(2)
+    _shape(back, (W, max_num_tokens, H), "back")
+    _shape(token_slot, (T, W), "token_slot", _I32T)
+    _shape(out, (T, H), "out")
+    _dense_from(back, 1, "back")
+    _dense_from(token_slot, 0, "token_slot")
+    _dense_from(out, 0, "out")
+    return T, W, H
+
+
 def prepare_combine_unpack(back: torch.Tensor, token_slot: torch.Tensor,
                            max_num_tokens: int, out: torch.Tensor) -> PreparedCall:
     """back: [W, cap, H] view (rank stride free); token_slot: [T, W];
@@ -522,11 +663,7 @@ def prepare_combine_unpack(back: torch.Tensor, token_slot: torch.Tensor,
     dt = _dtype_code(back)
     if out.dtype != back.dtype:
         raise ValueError("out and back differ in dtype")
-    _dense_from(back, 1, "back")
-    _dense_from(token_slot, 0, "token_slot")
-    _dense_from(out, 0, "out")
-    T, W = token_slot.shape
-    H = back.size(2)
+    T, W, H = _unpack_side(back, token_slot, max_num_tokens, out)
     args = (_ptr(back), back.stride(0), dt, H, _ptr(token_slot), T, W,
             max_num_tokens, _ptr(out))
     return PreparedCall("moe_ep_combine_unpack", args, (back, token_slot, out))
@@ -554,14 +691,16 @@ def prepare_combine_unpack_fused(back: torch.Tensor, token_slot: torch.Tensor,
     dt = _dtype_code(back)
     if out.dtype != back.dtype or expert_out.dtype != back.dtype:
         raise ValueError("out, back and expert_out must share a dtype")
-    _dense_from(back, 1, "back")
-    _dense_from(token_slot, 0, "token_slot")
-    _dense_from(out, 0, "out")
+    T, W, H = _unpack_side(back, token_slot, max_num_tokens, out)
+    _, slots, cap, ecap = _sizes(K, e_local * W, W, max_num_tokens)
+    if expert_out.dim() != 3 or expert_out.size(2) != H:
+        raise ValueError("expert_out must be [e_local, W*cap, H]")
+    _lead_at_least(expert_out, (e_local, ecap), "expert_out")
     _dense_from(expert_out, 1, "expert_out")
-    for t, n in ((self_eloc, "self_eloc"), (self_w, "self_w"), (self_row, "self_row")):
+    for t, n, dts in ((self_eloc, "self_eloc", _I32T), (self_w, "self_w", _F32T),
+                      (self_row, "self_row", _I32T)):
+        _shape(t, (cap, slots), n, dts)
         _dense_from(t, 0, n)
-    T, W = token_slot.shape
-    H = back.size(2)
     args = (_ptr(back), back.stride(0), dt, H, _ptr(token_slot), T, W,
             max_num_tokens, self_rank, _ptr(expert_out), expert_out.stride(0),
             _ptr(self_eloc), _ptr(self_w), _ptr(self_row), e_local, K, _ptr(out))

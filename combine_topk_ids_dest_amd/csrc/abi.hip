@@ -250,8 +250,9 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
              int32_t K, int32_t E, int32_t W, int64_t max_num_tokens,
              const moe_ep_payload* payloads, int32_t n_payloads,
              const QuantArgs* quant, int32_t* send_cnt, int32_t* send_eloc,
-             float* send_w, int32_t* token_slot, uint32_t* err_flags,
-             void* workspace, size_t workspace_bytes, void* stream) {
+             float* send_w, int64_t meta_rank_stride, int32_t* token_slot,
+             uint32_t* err_flags, void* workspace, size_t workspace_bytes,
+             void* stream) {
     if (E <= 0 || W <= 0 || E % W != 0 || T < 0) return MOE_EP_EINVAL;
     Shape sh;
     int rc = check_shape(K, E / W, W, max_num_tokens, &sh);
@@ -259,6 +260,10 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
     if (T > max_num_tokens) return MOE_EP_ECAP;
     if (T * K > kI32Max || T * W > kI32Max) return MOE_EP_EINVAL;
     if (!send_cnt || !send_eloc || !send_w) return MOE_EP_EINVAL;
+    // destination blocks of the metadata: at least dense, and the offset of
+    // the last block must fit in int64_t
+    if (meta_rank_stride < sh.cap * sh.slots || meta_rank_stride > INT64_MAX / W)
+        return MOE_EP_EINVAL;
     if (T > 0 && (!topk_ids || !topk_weights || !token_slot)) return MOE_EP_EINVAL;
     PayloadSet P;
     rc = check_payloads(payloads, n_payloads, 1, sh.cap, T > 0, &P);
@@ -287,6 +292,8 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
             return MOE_EP_EALIGN;
     }
     const PackWs ws = pack_ws(T, W);
+    // one tile of tokens needs no workspace (the pack routes by itself)
+    const bool own_route = T > 0 && T <= kRouteTile;
     if (ws.bytes > 0 && (!workspace || workspace_bytes < (size_t)ws.bytes))
         return MOE_EP_EWORKSPACE;
     if (workspace && !aligned16(workspace)) return MOE_EP_EALIGN;
@@ -299,11 +306,12 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
 
     // One tile of tokens (decode-sized batches): pack_copy routes by itself
     // and writes send_cnt; no separate routing launch.
-    if (T > 0 && T <= kRouteTile)
+    if (own_route)
         return hip_status(launch_pack_copy(topk_ids, topk_weights, T, K, E,
                                            sh.e_local, W, sh.slots, sh.cap, nullptr,
                                            token_slot, nullptr, nullptr, send_cnt, P,
-                                           quant, send_eloc, send_w, err_flags, st));
+                                           quant, send_eloc, send_w, meta_rank_stride,
+                                           err_flags, st));
     rc = hip_status(launch_route_local(topk_ids, T, K, E, sh.e_local, W,
                                        rank, tile_cnt, err_flags, st));
     if (rc) return rc;
@@ -319,7 +327,7 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
                                        sh.e_local, W, sh.slots, sh.cap, rank,
                                        token_slot, fused ? tile_cnt : nullptr,
                                        tile_off, send_cnt, P, quant, send_eloc,
-                                       send_w, err_flags, st));
+                                       send_w, meta_rank_stride, err_flags, st));
 }
 
 }  // namespace
@@ -331,11 +339,12 @@ int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
                          int64_t max_num_tokens,
                          const moe_ep_payload* payloads, int32_t n_payloads,
                          int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                         int32_t* token_slot, uint32_t* err_flags,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         int64_t meta_rank_stride, int32_t* token_slot,
+                         uint32_t* err_flags, void* workspace, size_t workspace_bytes,
+                         void* stream) {
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
-                    n_payloads, nullptr, send_cnt, send_eloc, send_w, token_slot,
-                    err_flags, workspace, workspace_bytes, stream);
+                    n_payloads, nullptr, send_cnt, send_eloc, send_w, meta_rank_stride,
+                    token_slot, err_flags, workspace, workspace_bytes, stream);
 }
 
 int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
@@ -346,8 +355,8 @@ int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
                              float* send_scale, int64_t scale_rank_stride,
                              const moe_ep_payload* payloads, int32_t n_payloads,
                              int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                             int32_t* token_slot, uint32_t* err_flags,
-                             void* workspace, size_t workspace_bytes,
+                             int64_t meta_rank_stride, int32_t* token_slot,
+                             uint32_t* err_flags, void* workspace, size_t workspace_bytes,
                              void* stream) {
     QuantArgs Q;
     Q.src = static_cast<const uint8_t*>(hidden);
@@ -365,8 +374,8 @@ int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
     Q.s_pitch = (Q.n_scales + 3) / 4 * 4 * 4;
     Q.mode = 1;
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
-                    n_payloads, &Q, send_cnt, send_eloc, send_w, token_slot,
-                    err_flags, workspace, workspace_bytes, stream);
+                    n_payloads, &Q, send_cnt, send_eloc, send_w, meta_rank_stride,
+                    token_slot, err_flags, workspace, workspace_bytes, stream);
 }
 
 int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
@@ -377,8 +386,8 @@ int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
                              int64_t scale_rank_stride,
                              const moe_ep_payload* payloads, int32_t n_payloads,
                              int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                             int32_t* token_slot, uint32_t* err_flags,
-                             void* workspace, size_t workspace_bytes,
+                             int64_t meta_rank_stride, int32_t* token_slot,
+                             uint32_t* err_flags, void* workspace, size_t workspace_bytes,
                              void* stream) {
     QuantArgs Q;
     Q.src = static_cast<const uint8_t*>(hidden);
@@ -393,8 +402,8 @@ int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
     Q.s_pitch = (Q.n_scales + 15) / 16 * 16;
     Q.mode = 2;
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
-                    n_payloads, &Q, send_cnt, send_eloc, send_w, token_slot,
-                    err_flags, workspace, workspace_bytes, stream);
+                    n_payloads, &Q, send_cnt, send_eloc, send_w, meta_rank_stride,
+                    token_slot, err_flags, workspace, workspace_bytes, stream);
 }
 
 int moe_ep_expert_batch_plan(const int32_t* recv_cnt, int64_t cnt_rank_stride,

@@ -209,7 +209,7 @@ hipError_t launch_column_scan(const int32_t* cnt, int ntiles, int nkeys,
                               int32_t* off, int32_t* total, int32_t clamp_max,
                               hipStream_t stream);
 
-// rank: the in-tile ranks of route_local ([T, W], -1 = no pair).
+// rank: the in-tile ranks of route_local ([W, T], -1 = no pair).
 // tile_cnt != nullptr selects the fused tile offsets (ntiles <=
 // kPackFuseTiles): offsets are summed from tile_cnt and block 0 writes
 // send_cnt; otherwise tile_off holds the offsets from column_scan.
@@ -220,8 +220,8 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             int32_t* token_slot, const int32_t* tile_cnt,
                             const int32_t* tile_off, int32_t* send_cnt,
                             const PayloadSet& P, const QuantArgs* quant,
-                            int32_t* send_eloc, float* send_w, uint32_t* err,
-                            hipStream_t stream);
+                            int32_t* send_eloc, float* send_w, int64_t meta_stride,
+                            uint32_t* err, hipStream_t stream);
 
 hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
                               const int32_t* recv_eloc, int64_t eloc_stride,

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ rank, int32_t* __restrict__ token_slot,
     const int32_t* __restrict__ tile_cnt, const int32_t* __restrict__ tile_off,
     int32_t* __restrict__ send_cnt, const PayloadSet P, const QuantArgs Q,
-    int32_t* __restrict__ send_eloc, float* __restrict__ send_w,
+    int32_t* __restrict__ send_eloc, float* __restrict__ send_w, int64_t meta_stride,
     uint32_t* __restrict__ err) {
     __shared__ int32_t s_dest[MOE_EP_MAX_WORLD];
     __shared__ int32_t s_slot[MOE_EP_MAX_WORLD];
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
         if (tid < W && part == 0) {
             uint32_t bad = 0;
             if (slot >= 0) {
-                const int64_t meta = ((int64_t)tid * cap + slot) * slots;
+                const int64_t meta = (int64_t)tid * meta_stride + (int64_t)slot * slots;
                 bad = write_pick_meta(ids, wts, t, K, E, e_local, tid, slots,
                                       send_eloc + meta, send_w + meta);
             }
@@ -564,8 +564,8 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             int32_t* token_slot, const int32_t* tile_cnt,
                             const int32_t* tile_off, int32_t* send_cnt,
                             const PayloadSet& P, const QuantArgs* quant,
-                            int32_t* send_eloc, float* send_w, uint32_t* err,
-                            hipStream_t stream) {
+                            int32_t* send_eloc, float* send_w, int64_t meta_stride,
+                            uint32_t* err, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     int64_t max_vecs = quant ? quant->H / 8 : 0;
     for (int p = 0; p < P.n; ++p)
@@ -579,19 +579,19 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
     if (quant && quant->mode == 2)
         pack_copy_kernel<2, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
-            tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, err);
+            tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, meta_stride, err);
     else if (quant)
         pack_copy_kernel<1, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
-            tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, err);
+            tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, meta_stride, err);
     else if (pf)
         pack_copy_kernel<0, true><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
-            tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, err);
+            tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, meta_stride, err);
     else
         pack_copy_kernel<0, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
             ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
-            tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, err);
+            tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, meta_stride, err);
     return hipGetLastError();
 }
 

@@ -133,9 +133,15 @@ MOE_EP_API const char* moe_ep_status_string(int status);
  *                 (dst_stride = bytes between destination blocks,
  *                 >= cap * row_bytes).
  *   send_cnt      int32 [W] out: slots used per destination.
- *   send_eloc     int32 [W, cap, slots] out: local expert id of pick j of
- *                 slot (d, s), -1 for an unused column.
- *   send_w        fp32  [W, cap, slots] out: its weight, +0.0 unused.
+ *   send_eloc     int32 out: local expert id of pick j of slot (d, s), -1
+ *                 for an unused column; destination d's block [cap, slots]
+ *                 (dense) at send_eloc + d * meta_rank_stride, so it can be
+ *                 aimed at per-destination receive blocks as the payloads
+ *                 can.
+ *   send_w        fp32 out: its weight, +0.0 unused; same layout and stride.
+ *   meta_rank_stride  elements between destination blocks of send_eloc and
+ *                 send_w (>= cap * slots; EINVAL otherwise). Elements
+ *                 between blocks are not written.
  *   token_slot    int32 [T, W] out: slot of token t at destination d, -1
  *                 if none. Context for moe_ep_combine_unpack; keep it.
  *   err_flags     nullable; bits MOE_EP_ERR_ID_RANGE, MOE_EP_ERR_PICKS.
@@ -146,8 +152,9 @@ MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_w
                          int64_t max_num_tokens,
                          const moe_ep_payload* payloads, int32_t n_payloads,
                          int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                         int32_t* token_slot, uint32_t* err_flags,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         int64_t meta_rank_stride, int32_t* token_slot,
+                         uint32_t* err_flags, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * Dispatch with quantize-on-pack: moe_ep_dispatch_pack, but the bf16 hidden
@@ -156,12 +163,12 @@ MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_w
  * instead of the bf16 row (about half the bytes). The vLLM all2all page's
  * FlashInfer one-sided manager sizes its dispatch for quantised hidden rows
  * plus scale factors; the alltoall_batched page itself supports unquantised
- * MoE only. For each group of a row with amax > 0: scale = amax / 448 and
- * code = e4m3(x * r) with r = 448 / amax (fp32 divisions and product
- * rounded to nearest, the conversion to nearest even); scale = r = 1 when
- * amax = 0. NaN entries do not take part in amax, and every code carries
- * the sign bit of its input (so a NaN input, or an infinite one when the
- * group's amax is infinite and r = 0, gives the NaN code with that sign).
+ * MoE only. For each group of a row with amax > 0: scale s = amax / 448
+ * and code = e4m3(x / s) (both divisions rounded to fp32 to nearest, the
+ * conversion to nearest even: a plain scaled cast); s = 1 when amax = 0.
+ * NaN entries do not take part in amax, and every code carries the sign
+ * bit of its input (so a NaN input, or an infinite one when the group's
+ * amax, and so s, is infinite, gives the NaN code with that sign).
  * Dequantisation is code * scale.
  *
  *   hidden        bf16 [T, H]; hidden_stride = bytes between tokens
@@ -187,9 +194,9 @@ MOE_EP_API int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* to
                                         float* send_scale, int64_t scale_rank_stride,
                                         const moe_ep_payload* payloads, int32_t n_payloads,
                                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                                        int32_t* token_slot, uint32_t* err_flags,
-                                        void* workspace, size_t workspace_bytes,
-                                        void* stream);
+                                        int64_t meta_rank_stride, int32_t* token_slot,
+                                        uint32_t* err_flags, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /*
  * Dispatch with 4-bit quantize-on-pack: the FlashInfer one-sided manager on
@@ -198,8 +205,9 @@ MOE_EP_API int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* to
  * factors. Here each bf16 hidden row is quantised once, on the send side,
  * in blocks of 16 columns: amax = max |x|, the scale is the OCP E4M3 code
  * of amax / 6 (fp32 division, then nearest even, saturating at 448), and
- * with s its value each code is the OCP E2M1 code of x * r, r = 1 / s
- * (r = 0 when s = 0), to nearest with ties to even, saturating at 6. E2M1
+ * with s its value each code is the OCP E2M1 code of x / s (the division
+ * rounded to fp32; a zero of x's sign when s = 0), to nearest with ties to
+ * even, saturating at 6. E2M1
  * magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6. NaN entries do not take part
  * in amax, and every code carries the sign bit of its input (a NaN input
  * gives a zero of its sign). Dequantisation is value(code) * s. Two codes
@@ -227,9 +235,9 @@ MOE_EP_API int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* to
                                         void* send_scale, int64_t scale_rank_stride,
                                         const moe_ep_payload* payloads, int32_t n_payloads,
                                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                                        int32_t* token_slot, uint32_t* err_flags,
-                                        void* workspace, size_t workspace_bytes,
-                                        void* stream);
+                                        int64_t meta_rank_stride, int32_t* token_slot,
+                                        uint32_t* err_flags, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /*
  * Dispatch, receive side of one destination rank (prepare() on the vLLM

@@ -112,13 +112,15 @@ def _payloads(*descs):
 
 
 def _pack(T=16, K=2, E=8, W=4, cap=16, pl=None, npl=1, ws_bytes=1 << 20,
-          ws=FAKE, ids=FAKE):
+          ws=FAKE, ids=FAKE, meta=None):
     lib = B.load()
     if pl is None:
         pl = _payloads((FAKE, 512, FAKE, cap * 512, 512))
+    if meta is None:
+        meta = cap * min(K, E // W) if W > 0 and E % W == 0 else 0
     return lib.moe_ep_dispatch_pack(ids, FAKE, T, K, E, W, cap,
                                     ctypes.addressof(pl), npl, FAKE, FAKE,
-                                    FAKE, FAKE, None, ws, ws_bytes, None)
+                                    FAKE, meta, FAKE, None, ws, ws_bytes, None)
 
 
 def test_dispatch_pack_argument_checks():
@@ -141,6 +143,11 @@ def test_dispatch_pack_argument_checks():
     assert _pack(K=65, E=65 * 4) == B.EINVAL           # slots > 64
     # size limit W * cap * slots < 2^31
     assert _pack(T=0, cap=1 << 28, K=8, E=64, W=8) == B.EINVAL
+    # metadata blocks: at least cap * slots elements apart, and the offset
+    # of the last one must not overflow
+    assert _pack(meta=16 * 2 - 1) == B.EINVAL
+    assert _pack(meta=-1) == B.EINVAL
+    assert _pack(meta=(1 << 63) // 3) == B.EINVAL
 
 
 def test_dispatch_pack_fp4_argument_checks():
@@ -154,8 +161,8 @@ def test_dispatch_pack_fp4_argument_checks():
         pl = _payloads()
         return lib.moe_ep_dispatch_pack_fp4(FAKE, FAKE, 16, 2, 8, 4, cap, FAKE, hs, H,
                                             q, qs, sc, ss, ctypes.addressof(pl), 0,
-                                            FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
-                                            None)
+                                            FAKE, FAKE, FAKE, cap * 2, FAKE, None, FAKE,
+                                            1 << 20, None)
 
     assert B.fp4_scale_pitch(7168) == 448 and B.fp4_scale_pitch(544) == 48
     assert call(H=0) == B.EINVAL

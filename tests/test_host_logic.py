@@ -133,3 +133,165 @@ def test_prepared_calls_take_gpu_tensors_only():
     with pytest.raises(ValueError, match="one GPU"):
         B.moe_ep_combine_unpack(back, token_slot, 16, out)
     assert list(B._tensors((1, [back, (None, out)], token_slot))) == [back, out, token_slot]
+
+
+def _send_side_tensors(T=8, K=2, W=4, cap=8, slots=2, row=64):
+    z = torch.zeros
+    return dict(
+        topk_ids=z(T, K, dtype=torch.int32), topk_weights=z(T, K),
+        payloads=[(z(T, row, dtype=torch.uint8), z(W, cap, row, dtype=torch.uint8))],
+        send_cnt=z(W, dtype=torch.int32), send_eloc=z(W, cap, slots, dtype=torch.int32),
+        send_w=z(W, cap, slots), token_slot=z(T, W, dtype=torch.int32),
+        err_flags=z(1, dtype=torch.int32), workspace=z(4096, dtype=torch.uint8))
+
+
+def _pack_call(t, E=8, W=4, cap=8):
+    return B.prepare_dispatch_pack(t["topk_ids"], t["topk_weights"], E, W, cap,
+                                   t["payloads"], t["send_cnt"], t["send_eloc"],
+                                   t["send_w"], t["token_slot"], t["err_flags"],
+                                   t["workspace"])
+
+
+def test_binding_checks_pack_shapes_before_the_device():
+    """Every tensor of a pack call is checked against T, K, W, cap and slots
+    (the C ABI sees pointers only, so a short buffer would be written out of
+    bounds on the device). Correct shapes on host tensors reach the one-GPU
+    check; each wrong one is refused before it."""
+    with pytest.raises(ValueError, match="one GPU"):
+        _pack_call(_send_side_tensors())
+    z = torch.zeros
+    wrong = {
+        "topk_weights": z(8, 3),
+        "send_cnt": z(3, dtype=torch.int32),
+        "send_eloc": z(4, 7, 2, dtype=torch.int32),
+        "send_w": z(4, 8, 2, dtype=torch.float64),
+        "token_slot": z(8, 3, dtype=torch.int32),
+        "err_flags": z(0, dtype=torch.int32),
+        "payloads": [(z(7, 64, dtype=torch.uint8), z(4, 8, 64, dtype=torch.uint8))],
+    }
+    for name, bad in wrong.items():
+        t = _send_side_tensors()
+        t[name] = bad
+        with pytest.raises(ValueError) as e:
+            _pack_call(t)
+        assert "one GPU" not in str(e.value), name
+    t = _send_side_tensors()
+    t["payloads"] = [(z(8, 64, dtype=torch.uint8), z(4, 7, 64, dtype=torch.uint8))]
+    with pytest.raises(ValueError, match="at least"):
+        _pack_call(t)
+    # a padded metadata rank stride is accepted when both arrays share it
+    base_e = z(4, 16 + 5, dtype=torch.int32)
+    base_w = z(4, 16 + 5)
+    t = _send_side_tensors()
+    t["send_eloc"] = base_e[:, :16].view(4, 8, 2)
+    t["send_w"] = base_w[:, :16].view(4, 8, 2)
+    with pytest.raises(ValueError, match="one GPU"):
+        _pack_call(t)
+    t["send_w"] = z(4, 8, 2)
+    with pytest.raises(ValueError, match="share a rank stride"):
+        _pack_call(t)
+
+
+def test_binding_checks_quantised_pack_shapes():
+    t = _send_side_tensors(row=64)
+    z = torch.zeros
+    hidden = z(8, 32, dtype=torch.bfloat16)
+    args = lambda q, sc: (t["topk_ids"], t["topk_weights"], 8, 4, 8, hidden, 32, q, sc,
+                          [], t["send_cnt"], t["send_eloc"], t["send_w"],
+                          t["token_slot"], t["err_flags"], t["workspace"])
+    with pytest.raises(ValueError, match="one GPU"):
+        B.prepare_dispatch_pack_fp8(*args(z(4, 8, 32, dtype=torch.uint8), z(4, 8, 4)))
+    for q, sc in ((z(4, 8, 31, dtype=torch.uint8), z(4, 8, 4)),
+                  (z(4, 7, 32, dtype=torch.uint8), z(4, 8, 4)),
+                  (z(4, 8, 32, dtype=torch.uint8), z(4, 8, 3)),
+                  (z(4, 8, 32, dtype=torch.int32), z(4, 8, 4))):
+        with pytest.raises(ValueError) as e:
+            B.prepare_dispatch_pack_fp8(*args(q, sc))
+        assert "one GPU" not in str(e.value)
+    fp4 = lambda q, sc: B.prepare_dispatch_pack_fp4(
+        t["topk_ids"], t["topk_weights"], 8, 4, 8, hidden, q, sc, [], t["send_cnt"],
+        t["send_eloc"], t["send_w"], t["token_slot"], t["err_flags"], t["workspace"])
+    with pytest.raises(ValueError, match="one GPU"):
+        fp4(z(4, 8, 16, dtype=torch.uint8), z(4, 8, 16, dtype=torch.uint8))
+    for q, sc in ((z(4, 8, 8, dtype=torch.uint8), z(4, 8, 16, dtype=torch.uint8)),
+                  (z(4, 7, 16, dtype=torch.uint8), z(4, 8, 16, dtype=torch.uint8)),
+                  (z(4, 8, 16, dtype=torch.uint8), z(4, 8, 2, dtype=torch.uint8))):
+        with pytest.raises(ValueError) as e:
+            fp4(q, sc)
+        assert "one GPU" not in str(e.value)
+
+
+def test_binding_checks_receive_and_combine_shapes():
+    """Batch, sanitise, reduce and unpack calls: counts, local ids, rows,
+    expert batches and outputs against W, e_local, cap, slots and H."""
+    z = torch.zeros
+    W, el, K, cap, H = 4, 2, 2, 8, 32
+    ecap = W * cap
+    ok = dict(cnt=z(W, dtype=torch.int32), eloc=z(W, cap, 2, dtype=torch.int32),
+              pl=[(z(W, cap, 64, dtype=torch.uint8), z(el, ecap, 64, dtype=torch.uint8))],
+              ent=z(el, dtype=torch.int32), row=z(W, cap, 2, dtype=torch.int32),
+              err=z(1, dtype=torch.int32), ws=z(4096, dtype=torch.uint8))
+
+    def batch(d):
+        return B.prepare_expert_batch(d["cnt"], d["eloc"], W, el, K, cap, d["pl"],
+                                      d["ent"], d["row"], d["err"], d["ws"])
+
+    with pytest.raises(ValueError, match="one GPU"):
+        batch(ok)
+    for k, bad in (("cnt", z(W - 1, dtype=torch.int32)),
+                   ("eloc", z(W, cap - 1, 2, dtype=torch.int32)),
+                   ("ent", z(el + 1, dtype=torch.int32)),
+                   ("row", z(W, cap, 1, dtype=torch.int32)),
+                   ("pl", [(z(W, cap, 64, dtype=torch.uint8),
+                            z(el, ecap - 1, 64, dtype=torch.uint8))]),
+                   ("pl", [(z(W - 1, cap, 64, dtype=torch.uint8),
+                            z(el, ecap, 64, dtype=torch.uint8))])):
+        d = dict(ok)
+        d[k] = bad
+        with pytest.raises(ValueError) as e:
+            batch(d)
+        assert "one GPU" not in str(e.value), k
+    with pytest.raises(ValueError) as e:
+        B.prepare_sanitize_expert_ids(ok["cnt"], ok["eloc"], W, el, K, cap, -1,
+                                      z(W, cap, 3, dtype=torch.int32), None)
+    assert "one GPU" not in str(e.value)
+
+    Y = z(el, ecap, H, dtype=torch.bfloat16)
+    wts = z(W, cap, 2)
+    ret = z(W, cap, H, dtype=torch.bfloat16)
+
+    def reduce(Y=Y, wts=wts, ret=ret, row=ok["row"]):
+        return B.prepare_combine_reduce(Y, ok["cnt"], ok["eloc"], wts, row, W, el, K,
+                                        cap, ret)
+
+    with pytest.raises(ValueError, match="one GPU"):
+        reduce()
+    for kw in (dict(Y=z(el, ecap - 1, H, dtype=torch.bfloat16)),
+               dict(Y=z(el - 1, ecap, H, dtype=torch.bfloat16)),
+               dict(wts=z(W, cap, 1)),
+               dict(ret=z(W, cap, H - 8, dtype=torch.bfloat16)),
+               dict(ret=z(W, cap - 1, H, dtype=torch.bfloat16)),
+               dict(row=z(W, cap - 1, 2, dtype=torch.int32))):
+        with pytest.raises(ValueError) as e:
+            reduce(**kw)
+        assert "one GPU" not in str(e.value), kw
+    T = 6
+    ts = z(T, W, dtype=torch.int32)
+    out = z(T, H, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="one GPU"):
+        B.prepare_combine_unpack(ret, ts, cap, out)
+    for b, t_, o in ((z(W, cap - 1, H, dtype=torch.bfloat16), ts, out),
+                     (ret, z(T, W + 1, dtype=torch.int32), out),
+                     (ret, ts, z(T - 1, H, dtype=torch.bfloat16)),
+                     (ret, ts, z(T, H + 8, dtype=torch.bfloat16))):
+        with pytest.raises(ValueError) as e:
+            B.prepare_combine_unpack(b, t_, cap, o)
+        assert "one GPU" not in str(e.value)
+    own = dict(e=z(cap, 2, dtype=torch.int32), w=z(cap, 2), r=z(cap, 2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="one GPU"):
+        B.prepare_combine_unpack_fused(ret, ts, cap, 0, Y, own["e"], own["w"], own["r"],
+                                       el, K, out)
+    with pytest.raises(ValueError) as e:
+        B.prepare_combine_unpack_fused(ret, ts, cap, 0, Y, own["e"], own["w"],
+                                       z(cap - 1, 2, dtype=torch.int32), el, K, out)
+    assert "one GPU" not in str(e.value)
