@@ -17,7 +17,8 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
 
-OK, EINVAL, ECAP, EDTYPE, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, ECAP, EDTYPE, EALIGN, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+NOALLOC_SCRATCH_BYTES = 8 << 20
 BF16, F32 = 0, 1
 ERR_ID_RANGE, ERR_PICKS, ERR_ELOC, ERR_ROWCAP, ERR_CNT = 1, 2, 4, 8, 16
 MAX_PAYLOADS = 8
@@ -37,6 +38,7 @@ EXPORTED = (
     "moe_ep_combine_unpack",
     "moe_ep_combine_reduce_peers",
     "moe_ep_combine_unpack_fused",
+    "moe_ep_dispatch_pack_noalloc",
 )
 
 
@@ -77,6 +79,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_ep_dispatch_pack.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
         _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_dispatch_pack_noalloc.argtypes = [
+        _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
+        _P, _P, _P, _I64, _P, _P, _P]
     lib.moe_ep_dispatch_pack_fp8.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I64, _I64, _I32,
         _P, _I64, _P, _I64, _P, _I32, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
@@ -363,6 +368,34 @@ def prepare_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
     return PreparedCall("moe_ep_dispatch_pack", args,
                         (arr, topk_ids, topk_weights, payloads, send_cnt, send_eloc,
                          send_w, token_slot, err_flags, workspace))
+
+
+def prepare_dispatch_pack_noalloc(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                                  E: int, W: int, max_num_tokens: int,
+                                  payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                                  send_cnt: torch.Tensor, send_eloc: torch.Tensor,
+                                  send_w: torch.Tensor, token_slot: torch.Tensor,
+                                  err_flags: Optional[torch.Tensor]) -> PreparedCall:
+    """moe_ep_dispatch_pack without a workspace: the library's own device
+    scratch holds the send side's workspace (moe_ep_dispatch_pack_noalloc;
+    calls that overlap on one GPU race on it)."""
+    T, K, cap, _ = _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt,
+                              send_eloc, send_w, token_slot, err_flags)
+    arr = _payload_array(payloads, 1, 2, (T,), (W, cap))
+    args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
+            ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
+            _ptr(send_w), send_eloc.stride(0), _ptr(token_slot), _ptr(err_flags))
+    return PreparedCall("moe_ep_dispatch_pack_noalloc", args,
+                        (arr, topk_ids, topk_weights, payloads, send_cnt, send_eloc,
+                         send_w, token_slot, err_flags))
+
+
+def moe_ep_dispatch_pack_noalloc(topk_ids, topk_weights, E, W, max_num_tokens, payloads,
+                                 send_cnt, send_eloc, send_w, token_slot, err_flags,
+                                 stream=None) -> None:
+    prepare_dispatch_pack_noalloc(topk_ids, topk_weights, E, W, max_num_tokens, payloads,
+                                  send_cnt, send_eloc, send_w, token_slot,
+                                  err_flags)(stream)
 
 
 def scale_pitch(H: int, group: int) -> int:

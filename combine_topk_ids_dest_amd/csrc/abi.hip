@@ -4,11 +4,47 @@
 // unless all checks pass.
 #include <limits.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace moe_ep;
 
+// Scratch of moe_ep_dispatch_pack_noalloc: the send side's workspace (tile
+// counts, tile offsets, in-tile ranks) in a device array that the library
+// holds on every GPU it runs on until the process ends. In host code this
+// name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns for the current device (scratch_address).
+static __device__ __align__(256) uint8_t scratch[MOE_EP_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept. The stream must belong to the
+// current device: the address is per device.
+int scratch_address(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_EP_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_EP_EINVAL;
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_EP_EHIP;
+        if (sdev != dev) return MOE_EP_EINVAL;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return MOE_EP_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_EP_OK;
+}
 
 constexpr int64_t kI32Max = INT_MAX;
 
@@ -207,6 +243,8 @@ const char* moe_ep_status_string(int status) {
         case MOE_EP_EALIGN: return "pointer, stride or row not 16-byte aligned";
         case MOE_EP_EWORKSPACE: return "workspace missing or too small";
         case MOE_EP_EHIP: return "HIP kernel launch failed";
+        case MOE_EP_ESCRATCH:
+            return "sizes need more scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }
@@ -252,7 +290,7 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
              const QuantArgs* quant, int32_t* send_cnt, int32_t* send_eloc,
              float* send_w, int64_t meta_rank_stride, int32_t* token_slot,
              uint32_t* err_flags, void* workspace, size_t workspace_bytes,
-             void* stream) {
+             void* stream, bool use_scratch = false) {
     if (E <= 0 || W <= 0 || E % W != 0 || T < 0) return MOE_EP_EINVAL;
     Shape sh;
     int rc = check_shape(K, E / W, W, max_num_tokens, &sh);
@@ -294,11 +332,19 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
     const PackWs ws = pack_ws(T, W);
     // one tile of tokens needs no workspace (the pack routes by itself)
     const bool own_route = T > 0 && T <= kRouteTile;
-    if (ws.bytes > 0 && (!workspace || workspace_bytes < (size_t)ws.bytes))
-        return MOE_EP_EWORKSPACE;
-    if (workspace && !aligned16(workspace)) return MOE_EP_EALIGN;
+    if (use_scratch) {
+        if (ws.bytes > (int64_t)MOE_EP_NOALLOC_SCRATCH_BYTES) return MOE_EP_ESCRATCH;
+    } else {
+        if (ws.bytes > 0 && (!workspace || workspace_bytes < (size_t)ws.bytes))
+            return MOE_EP_EWORKSPACE;
+        if (workspace && !aligned16(workspace)) return MOE_EP_EALIGN;
+    }
 
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (use_scratch && !own_route) {
+        rc = scratch_address(st, &workspace);
+        if (rc) return rc;
+    }
     uint8_t* wsb = static_cast<uint8_t*>(workspace);
     int32_t* tile_cnt = reinterpret_cast<int32_t*>(wsb + ws.cnt_off);
     int32_t* tile_off = reinterpret_cast<int32_t*>(wsb + ws.off_off);
@@ -345,6 +391,18 @@ int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
                     n_payloads, nullptr, send_cnt, send_eloc, send_w, meta_rank_stride,
                     token_slot, err_flags, workspace, workspace_bytes, stream);
+}
+
+int moe_ep_dispatch_pack_noalloc(const int32_t* topk_ids, const float* topk_weights,
+                                 int64_t T, int32_t K, int32_t E, int32_t W,
+                                 int64_t max_num_tokens,
+                                 const moe_ep_payload* payloads, int32_t n_payloads,
+                                 int32_t* send_cnt, int32_t* send_eloc, float* send_w,
+                                 int64_t meta_rank_stride, int32_t* token_slot,
+                                 uint32_t* err_flags, void* stream) {
+    return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
+                    n_payloads, nullptr, send_cnt, send_eloc, send_w, meta_rank_stride,
+                    token_slot, err_flags, nullptr, 0, stream, true);
 }
 
 int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,

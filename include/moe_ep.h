@@ -66,6 +66,8 @@ extern "C" {
 #define MOE_EP_EALIGN     -4   /* pointer, stride or row not 16-B aligned  */
 #define MOE_EP_EWORKSPACE -5   /* workspace missing or too small           */
 #define MOE_EP_EHIP       -6   /* a kernel launch failed                    */
+#define MOE_EP_ESCRATCH   -7   /* more scratch than moe_ep_dispatch_pack_noalloc
+                                  holds (MOE_EP_NOALLOC_SCRATCH_BYTES)      */
 
 /* Combine data types (expert outputs, partials and token outputs). */
 #define MOE_EP_BF16 0
@@ -83,6 +85,9 @@ extern "C" {
 #define MOE_EP_MAX_WORLD        64
 #define MOE_EP_MAX_LOCAL_EXPERTS 1024
 #define MOE_EP_MAX_SLOTS        64
+
+/* Device scratch that moe_ep_dispatch_pack_noalloc uses, per GPU. */
+#define MOE_EP_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 /*
  * One payload: every byte of a row is moved as is (bf16, fp8, fp32 scales,
@@ -155,6 +160,40 @@ MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_w
                          int64_t meta_rank_stride, int32_t* token_slot,
                          uint32_t* err_flags, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * moe_ep_dispatch_pack for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. It
+ * takes no workspace; the send side's scratch (tile counts, tile offsets
+ * and in-tile ranks, the bytes moe_ep_workspace_bytes gives for the send
+ * side) lives in a device array of MOE_EP_NOALLOC_SCRATCH_BYTES (8 MiB)
+ * that the library holds on each GPU it runs on until the process ends.
+ * The call allocates nothing and makes no allocating library call.
+ *
+ *   - Sizes whose send-side scratch exceeds the array return
+ *     MOE_EP_ESCRATCH before anything is enqueued. The scratch is
+ *     2 * round_up(ceil(T / 256) * W * 4, 128) + round_up(T * W * 4, 128)
+ *     bytes (T <= 256 needs none): T * W up to about 2.08 million (token,
+ *     destination) pairs, e.g. T = 65536 at W = 16 or T = 16384 at W = 64.
+ *   - The stream must belong to the current device (EINVAL otherwise). The
+ *     first call on a device looks the array's address up (no allocation);
+ *     make it outside graph capture.
+ *   - Every call on a GPU shares that GPU's array, and it keeps the last
+ *     call's contents. Each call writes every scratch byte it reads before
+ *     reading it, so nothing has to be cleared, but calls that overlap on
+ *     one GPU (on different streams, or from different host threads) race
+ *     on the array: order them.
+ * Everything else, and every output, as moe_ep_dispatch_pack.
+ */
+MOE_EP_API int moe_ep_dispatch_pack_noalloc(const int32_t* topk_ids,
+                                            const float* topk_weights, int64_t T,
+                                            int32_t K, int32_t E, int32_t W,
+                                            int64_t max_num_tokens,
+                                            const moe_ep_payload* payloads,
+                                            int32_t n_payloads, int32_t* send_cnt,
+                                            int32_t* send_eloc, float* send_w,
+                                            int64_t meta_rank_stride, int32_t* token_slot,
+                                            uint32_t* err_flags, void* stream);
 
 /*
  * Dispatch with quantize-on-pack: moe_ep_dispatch_pack, but the bf16 hidden

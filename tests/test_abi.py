@@ -48,8 +48,11 @@ def test_python_constants_match_header():
     d = _defines()
     assert (d["MOE_EP_OK"], d["MOE_EP_EINVAL"], d["MOE_EP_ECAP"],
             d["MOE_EP_EDTYPE"], d["MOE_EP_EALIGN"], d["MOE_EP_EWORKSPACE"],
-            d["MOE_EP_EHIP"]) == (B.OK, B.EINVAL, B.ECAP, B.EDTYPE, B.EALIGN,
-                                  B.EWORKSPACE, B.EHIP)
+            d["MOE_EP_EHIP"], d["MOE_EP_ESCRATCH"]) == \
+        (B.OK, B.EINVAL, B.ECAP, B.EDTYPE, B.EALIGN, B.EWORKSPACE, B.EHIP, B.ESCRATCH)
+    m = re.search(r"#define\s+MOE_EP_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)",
+                  _header())
+    assert int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
     assert (d["MOE_EP_BF16"], d["MOE_EP_F32"]) == (B.BF16, B.F32)
     assert (d["MOE_EP_ERR_ID_RANGE"], d["MOE_EP_ERR_PICKS"], d["MOE_EP_ERR_ELOC"],
             d["MOE_EP_ERR_ROWCAP"], d["MOE_EP_ERR_CNT"]) == \
@@ -96,7 +99,8 @@ def test_capacities_and_workspace():
 
 
 def test_status_strings():
-    for code in (B.OK, B.EINVAL, B.ECAP, B.EDTYPE, B.EALIGN, B.EWORKSPACE, B.EHIP):
+    for code in (B.OK, B.EINVAL, B.ECAP, B.EDTYPE, B.EALIGN, B.EWORKSPACE, B.EHIP,
+                 B.ESCRATCH):
         s = B.status_string(code)
         assert s and s != "unknown status"
     assert B.status_string(12345) == "unknown status"
@@ -148,6 +152,38 @@ def test_dispatch_pack_argument_checks():
     assert _pack(meta=16 * 2 - 1) == B.EINVAL
     assert _pack(meta=-1) == B.EINVAL
     assert _pack(meta=(1 << 63) // 3) == B.EINVAL
+
+
+def _pack_noalloc(T=16, K=2, E=8, W=4, cap=16, npl=1, meta=None):
+    lib = B.load()
+    pl = _payloads((FAKE, 512, FAKE, cap * 512, 512))
+    if meta is None:
+        meta = cap * min(K, E // W) if W > 0 and E % W == 0 else 0
+    return lib.moe_ep_dispatch_pack_noalloc(FAKE, FAKE, T, K, E, W, cap,
+                                            ctypes.addressof(pl), npl, FAKE, FAKE,
+                                            FAKE, meta, FAKE, None, None)
+
+
+def _send_scratch(T, W):
+    r128 = lambda x: (x + 127) // 128 * 128
+    return 2 * r128(-(-T // 256) * W * 4) + r128(T * W * 4)
+
+
+def test_dispatch_pack_noalloc_argument_checks():
+    """The allocation-free pack checks its arguments like the pack, and
+    refuses sizes whose send-side scratch exceeds its device array before
+    any HIP call (so no GPU is needed here)."""
+    assert _pack_noalloc(W=0) == B.EINVAL
+    assert _pack_noalloc(T=17) == B.ECAP
+    assert _pack_noalloc(npl=9) == B.EINVAL
+    assert _pack_noalloc(meta=31) == B.EINVAL
+    # 2.1 M (token, destination) pairs: just past the 8 MiB array
+    T, W = 1 << 16, 32
+    assert _send_scratch(T, W) > B.NOALLOC_SCRATCH_BYTES
+    assert _pack_noalloc(T=T, K=2, E=64, W=W, cap=T) == B.ESCRATCH
+    assert _send_scratch(T, 31) <= B.NOALLOC_SCRATCH_BYTES
+    # the pack with a caller workspace takes the same sizes
+    assert _pack(T=T, K=2, E=64, W=W, cap=T, ws_bytes=8) == B.EWORKSPACE
 
 
 def test_dispatch_pack_fp4_argument_checks():
