@@ -5,10 +5,10 @@ one MI355X.
 A step is one pass of the whole path over W logical ranks with synthetic,
 seeded inputs already resident in HBM: W dispatch packs, then for every
 destination the expert batch and the combine reduce, then W combine
-unpacks. The ranks are spread over --lanes HIP streams (4 unless a step is
-tiny), so the kernels of one rank overlap those of another, as they would on
-W GPUs; each phase waits for the previous one on every stream. `value` is tokens/s over
-all W*T tokens of a step; effective GB/s
+unpacks. The ranks are spread over --lanes HIP streams (2, or 1 for a tiny
+step), so the kernels of one rank overlap those of another, as they would on
+W GPUs; each phase waits for the previous one on every stream. `value` is
+tokens/s over all W*T tokens of a step; effective GB/s
 uses the algorithmic byte model (what the method must read and write, from
 the run's actual counts):
 

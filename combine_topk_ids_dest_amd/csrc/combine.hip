@@ -4,8 +4,8 @@
 // the fp32 sum over its picks, in ascending pick order, of
 // fp32(expert output row) * router weight, each product rounded to fp32
 // before the add (__fmul_rn / __fadd_rn: no contraction into an FMA); the
-// slot's sum is stored in the data type (bf16: round to nearest even), so
-// the return transfer is token-sized.
+// slot's sum is stored in the data type (bf16: round to nearest even): one
+// row per (source, token) pair goes back, not one per expert.
 //
 // combine_unpack, on the source rank: each token's partials from the ranks
 // it went to, summed in fp32 in ascending rank order from +0.0f and rounded

@@ -9,9 +9,9 @@
  * its local expert ids and router weights as metadata (prepare(), send
  * side); the receive side re-batches rows per local expert
  * (prepare(), receive side); after the experts run, each destination
- * weights and reduces a token's experts into one token-sized row
- * (finalize(), first half) and each source sums its per-rank partials back
- * into token rows (finalize(), second half). The list of opaque payloads
+ * turns the expert rows of each received slot into one weighted row
+ * (finalize(), first half) and each source adds up the rows returned for
+ * each of its tokens (finalize(), second half). The list of opaque payloads
  * that travel with a token follows the FlashInfer module
  * "flashinfer/comm/trtllm_moe_alltoall.py" (moe_a2a_dispatch: several
  * [T, *] payloads per call, each received as [ep_size, max_tokens, *]).
@@ -360,8 +360,9 @@ MOE_EP_API int moe_ep_sanitize_expert_ids(const int32_t* recv_cnt, int64_t cnt_r
                                           uint32_t* err_flags, void* stream);
 
 /*
- * Combine, on the destination rank (finalize() on the vLLM page: weight
- * and reduce a token's experts so the return is token-sized). For every
+ * Combine, on the destination rank (vLLM alltoall_batched page,
+ * finalize(): one row per received slot, the weighted sum of its expert
+ * rows, so one row per (source, token) pair goes back). For every
  * valid received slot (s, slot) and column h:
  *   acc = +0.0f; for j ascending with recv_row >= 0:
  *     acc = acc + (fp32(Y[e_j, row_j, h]) * w_j)   (product rounded to
@@ -386,8 +387,9 @@ MOE_EP_API int moe_ep_combine_reduce(const void* expert_out, int64_t expert_stri
                           int64_t ret_rank_stride, void* stream);
 
 /*
- * Combine, on the source rank (finalize() on the vLLM page: sum each
- * token's per-rank partials). out[t, h] = sum over d ascending with
+ * Combine, on the source rank (vLLM alltoall_batched page, finalize():
+ * a token's row adds up what each of its destinations returned).
+ * out[t, h] = sum over d ascending with
  * token_slot[t, d] >= 0 of fp32(back[d, token_slot[t, d], h]), from +0.0f,
  * rounded once (bf16 to nearest-even). A token with no slot (padding)
  * gets +0.0. Every row of out is written.

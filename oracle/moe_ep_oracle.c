@@ -290,8 +290,8 @@ uint32_t oracle_expert_batch(
 }
 
 /* ------------------------------------------------------------------ */
-/* finalize(), on the destination rank: weight and reduce a token's     */
-/* experts so the return transfer is token-sized.                       */
+/* vLLM alltoall_batched page, finalize(), destination side: one row    */
+/* per received slot, the weighted sum of that slot's expert rows.      */
 /*                                                                      */
 /* For every valid received slot (s, slot): acc = +0.0f; for pick j     */
 /* ascending with recv_row >= 0: acc = acc + (fp32(Y[e_j, row_j, h]) *  */
@@ -352,7 +352,8 @@ uint32_t oracle_combine_reduce(
 }
 
 /* ------------------------------------------------------------------ */
-/* finalize(), on the source rank: sum each token's per-rank partials.  */
+/* vLLM alltoall_batched page, finalize(), source side: a token's row is */
+/* the sum of what each of its destination ranks returned for it.       */
 /*                                                                      */
 /* out[t, h] = round(sum over d ascending with token_slot[t,d] >= 0 of  */
 /* fp32(back[d, token_slot[t,d], h])), accumulated in fp32 from +0.0f   */
