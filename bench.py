@@ -26,12 +26,14 @@ with R_own expert rows) leaves the reduce and enters the fused unpack:
   unpack_fused (source s) (U - S_own)*Hb + R_own*Hb + S_own*slots*8 + T*Hb
 
 Besides the contract fields the line carries: per-call times (a separate
-pass with HIP events around each call), the time per rank share, the
-critical-path rate (T over the slowest rank's share, which sets the pace
-under skewed routing), the dispatch and combine split, and the same calls
-timed cold (each after a 1 GiB device write that evicts the 256 MB
-last-level cache), and the rate of the runtime's own 1 GiB device copy in
-the same session as a second roofline.
+pass with HIP events around each call; averages, which the roofline uses,
+and medians), the whole step with every call on one stream, the time per
+rank share, the critical-path rate (T over the slowest rank's share, which
+sets the pace under skewed routing), the dispatch and combine split, the
+same calls timed cold (each after a 1 GiB device write that evicts the
+256 MB last-level cache) together with whole cold steps over the lanes,
+and the rate of the runtime's own 1 GiB device copy in the same session as
+a second roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -449,23 +451,44 @@ def main():
     worst_share_ms = float(np.median([
         max(sum(t for t, rk in zip(times[k], rank_of) if rk == r) for r in range(w.W))
         for k in range(args.steps)]))
-    dispatch_ms = float(np.mean([sum(t for t, kd in zip(times[k], kinds)
-                                      if kd in ("pack", "batch_plan", "batch_copy"))
-                                  for k in range(args.steps)]))
-    combine_ms = float(np.mean([sum(t for t, kd in zip(times[k], kinds)
-                                     if kd in (k_red, k_unp))
-                                 for k in range(args.steps)]))
+    dispatch_ms = float(np.median([sum(t for t, kd in zip(times[k], kinds)
+                                        if kd in ("pack", "batch_plan", "batch_copy"))
+                                    for k in range(args.steps)]))
+    combine_ms = float(np.median([sum(t for t, kd in zip(times[k], kinds)
+                                       if kd in (k_red, k_unp))
+                                   for k in range(args.steps)]))
     # The same calls with the 256 MB last-level cache flushed before each
-    # one (a 1 GiB device write), so no call finds its inputs cached.
+    # one (a 1 GiB device write), so no call finds its inputs cached; and
+    # whole steps over the lanes, each after such a flush.
     cold_info = None
     if not args.no_cold:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         cold = timed_pass(flush)
-        del flush
-        cold_avg_us = {kd: float(np.mean([cold[k][i] for k in range(args.steps)
-                                          for i, x in enumerate(kinds) if x == kd])) * 1e3
-                       for kd in calls}
+        cold_calls = {kd: [cold[k][i] for k in range(args.steps)
+                           for i, x in enumerate(kinds) if x == kd] for kd in calls}
+        cold_avg_us = {kd: float(np.mean(v)) * 1e3 for kd, v in cold_calls.items()}
+        cold_med_us = {kd: float(np.median(v)) * 1e3 for kd, v in cold_calls.items()}
         cold_step_ms = float(np.mean([sum(c) for c in cold]))
+        cold_steps = []
+        for k in range(args.steps):
+            a, b = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            flush.fill_(k & 0xFF)
+            a.record(stream)
+            ep.step(fused_local=fused, streams=streams)
+            b.record(stream)
+            cold_steps.append((a, b))
+        torch.cuda.synchronize()
+        cold_lanes_ms = float(np.median([a.elapsed_time(b) for a, b in cold_steps]))
+        del flush
+
+    # The whole step with every call on one stream (the lanes' buffers, no
+    # overlap between ranks), timed like the headline region.
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        ep.step(fused_local=fused)
+    torch.cuda.synchronize()
+    one_stream_ms = (time.perf_counter() - t2) * 1e3 / args.steps
 
     send_cnt = ep.send_cnt.cpu().numpy().astype(np.int64)
     ent = ep.expert_num_tokens.cpu().numpy().astype(np.int64)
@@ -485,12 +508,20 @@ def main():
     copy_gbps = copy_rate(10)
     if not args.no_cold:
         cold_info = {
-            "note": "each call timed after a 1 GiB device write that evicts the last-level cache",
+            "note": "each call timed after a 1 GiB device write that evicts the last-level "
+                    "cache; step_over_lanes: whole steps as the timed region runs them, "
+                    "each after such a write (median)",
             "per_call_avg_us": {k: round(v, 2) for k, v in cold_avg_us.items()},
+            "per_call_median_us": {k: round(v, 2) for k, v in cold_med_us.items()},
             "tokens_per_s": round(tokens / (cold_step_ms / 1e3), 1),
-            "effective_gbps": round(step_bytes / (cold_step_ms / 1e3) / 1e9, 1)}
+            "effective_gbps": round(step_bytes / (cold_step_ms / 1e3) / 1e9, 1),
+            "step_over_lanes_ms": round(cold_lanes_ms, 4),
+            "step_over_lanes_tokens_per_s": round(tokens / (cold_lanes_ms / 1e3), 1),
+            "step_over_lanes_frac_of_peak_hbm": round(
+                step_bytes / (cold_lanes_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
     avg_us = {k: float(np.mean(v)) * 1e3 for k, v in per_kind.items()}
+    med_us = {k: float(np.median(v)) * 1e3 for k, v in per_kind.items()}
     total_ms = {k: float(np.sum(v)) for k, v in per_kind.items()}
     dom = max(total_ms, key=total_ms.get)
     bytes_per_launch = float(np.mean(bm[dom]))
@@ -507,6 +538,7 @@ def main():
         "traffic": traffic,
         "algorithmic_bytes_per_launch": int(bytes_per_launch),
         "avg_launch_us": round(avg_us[dom], 2),
+        "median_launch_us": round(med_us[dom], 2),
     }
 
     result = {
@@ -543,9 +575,12 @@ def main():
         "frac_of_copy_reference": round(gbps / copy_gbps, 4),
         "algorithmic_bytes_per_step": int(step_bytes),
         "per_call_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
+        "per_call_median_us": {k: round(v, 2) for k, v in med_us.items()},
         "per_call_gbps": {k: round(float(np.sum(bm[k])) / (total_ms[k] / args.steps / 1e3) / 1e9, 1)
                           for k in calls},
         "per_call_note": "per-call times come from a separate pass with HIP events around each call",
+        "one_stream_ms_per_step": round(one_stream_ms, 4),
+        "one_stream_tokens_per_s": round(tokens / (one_stream_ms / 1e3), 1),
         "per_rank_share_us": round(ms_per_step * 1e3 / w.W, 2),
         "critical_path_tokens_per_s": round(w.T / (worst_share_ms / 1e3), 1),
         "dispatch_ms_per_step": round(dispatch_ms, 4),
