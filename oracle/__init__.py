@@ -93,6 +93,8 @@ def _open(path: str):
     lib.oracle_combine_unpack.argtypes = [
         _P, _I64, _I64, _I32, _I64, _P, _I64, _I32, _P, _I64]
     lib.oracle_combine_unpack.restype = None
+    lib.oracle_pick_ranks.argtypes = [_P, _P, _I32, _I32, _I32, _I64, _P, _P]
+    lib.oracle_pick_ranks.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [ctypes.c_float]
     lib.oracle_round_bf16.restype = ctypes.c_uint16
     lib.oracle_round_bf16_bits.argtypes = [ctypes.c_uint32]
@@ -285,6 +287,23 @@ def dispatch_pack(topk_ids: np.ndarray, topk_weights: np.ndarray, E: int,
     return dict(send_cnt=send_cnt, send_eloc=send_eloc, send_w=send_w,
                 token_slot=token_slot, send=dsts, err=int(err),
                 cap=cap, slots=slots)
+
+
+def pick_ranks(send_cnt: np.ndarray, send_eloc: np.ndarray, e_local: int) -> dict:
+    """Send-side ranks of one source's pack outputs (send_cnt [W], send_eloc
+    [W, cap, slots]): send_rank [W, cap, slots] (-1 for unused columns;
+    slots past the count are -9, never written) and send_ecnt
+    [W, e_local]."""
+    cnt = np.ascontiguousarray(send_cnt, dtype=np.int32)
+    eloc = np.ascontiguousarray(send_eloc, dtype=np.int32)
+    W, cap, slots = eloc.shape
+    rank = np.full(eloc.shape, -9, np.int32)
+    ecnt = np.empty((W, e_local), np.int32)
+    rc = load().oracle_pick_ranks(_ptr(cnt), _ptr(eloc), W, e_local, slots, cap,
+                                  _ptr(rank), _ptr(ecnt))
+    if rc:
+        raise ValueError("oracle_pick_ranks: bad sizes")
+    return {"send_rank": rank, "send_ecnt": ecnt}
 
 
 def expert_batch(recv_cnt: np.ndarray, recv_eloc: np.ndarray, W: int,

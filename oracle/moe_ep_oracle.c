@@ -290,6 +290,48 @@ uint32_t oracle_expert_batch(
 }
 
 /* ------------------------------------------------------------------ */
+/* Send-side form of the receive rows. The page numbers a destination's */
+/* rows per local expert in (source, slot, column) order. Within one    */
+/* source that is the order the source sends in (slots by token, columns */
+/* by router order), so a source can count its own part: the rank of    */
+/* each used pick column among its earlier columns with the same local  */
+/* id, and the number of columns per local id. A destination's row for  */
+/* (s, slot, j) is then the counts of sources before s plus the rank.   */
+/*                                                                      */
+/* For every destination d of one source, over slots [0, send_cnt[d])  */
+/* ascending and columns ascending: a column with local id e >= 0 gets */
+/* send_rank = (columns of d with id e seen so far); a column with a    */
+/* negative id gets -1. send_ecnt[d, e] = columns of d with id e. Only  */
+/* the send_cnt[d] valid slots of send_rank are written; every entry of */
+/* send_ecnt is. Layouts as oracle_dispatch_pack's [W, cap, slots]     */
+/* metadata; send_ecnt is [W, e_local].                                 */
+/* ------------------------------------------------------------------ */
+int oracle_pick_ranks(const int32_t* send_cnt, const int32_t* send_eloc,
+                      int32_t W, int32_t e_local, int32_t slots, int64_t cap,
+                      int32_t* send_rank, int32_t* send_ecnt)
+{
+    if (W <= 0 || e_local <= 0 || slots <= 0 || cap < 0)
+        return -1;
+    for (int32_t d = 0; d < W; ++d) {
+        for (int32_t e = 0; e < e_local; ++e)
+            send_ecnt[(int64_t)d * e_local + e] = 0;
+        for (int64_t slot = 0; slot < send_cnt[d]; ++slot) {
+            for (int32_t j = 0; j < slots; ++j) {
+                int64_t at = ((int64_t)d * cap + slot) * slots + j;
+                int32_t e = send_eloc[at];
+                if (e < 0 || e >= e_local) {
+                    send_rank[at] = -1;
+                    continue;
+                }
+                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];
+                send_ecnt[(int64_t)d * e_local + e] += 1;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* vLLM alltoall_batched page, finalize(), destination side: one row    */
 /* per received slot, the weighted sum of that slot's expert rows.      */
 /*                                                                      */

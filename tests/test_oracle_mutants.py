@@ -118,6 +118,12 @@ MUTANTS = {
     "fp4_times_reciprocal_of_scale": (
         "const float y0 = s > 0.0f ? v0 / s : 0.0f;\n                const float y1 = s > 0.0f ? v1 / s : 0.0f;",
         "const float y0 = s > 0.0f ? v0 * (1.0f / s) : 0.0f;\n                const float y1 = s > 0.0f ? v1 * (1.0f / s) : 0.0f;"),
+    "pick_ranks_one_based": (
+        "                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];\n                send_ecnt[(int64_t)d * e_local + e] += 1;",
+        "                send_ecnt[(int64_t)d * e_local + e] += 1;\n                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];"),
+    "pick_ranks_columns_reversed": (
+        "            for (int32_t j = 0; j < slots; ++j) {\n                int64_t at = ((int64_t)d * cap + slot) * slots + j;\n                int32_t e = send_eloc[at];",
+        "            for (int32_t j = slots - 1; j >= 0; --j) {\n                int64_t at = ((int64_t)d * cap + slot) * slots + j;\n                int32_t e = send_eloc[at];"),
     "bf16_nan_drops_quiet_bit": (
         "return (uint16_t)(kept | 0x0040u);",
         "return (uint16_t)kept;"),
@@ -162,6 +168,9 @@ def _pin_battery():
         fp4pins.test_fp4_nonfinite_inputs,
         fp8pins.test_fp8_nonfinite_inputs,
         lambda: sanpins.test_sanitize_matches_brute_force_from_routing(4, 8, 3),
+        pins.test_golden_pick_ranks,
+        pins.test_pick_ranks_random_micro,
+        lambda: pins.test_pick_ranks_give_the_receive_rows(2),
     ]
 
 

@@ -624,3 +624,123 @@ def test_generators_are_deterministic_and_shaped():
     assert h1 == h2
     assert wl.WORKLOADS[3].n_pad == 245 and wl.WORKLOADS[5].n_pad == 819
     assert wl.WORKLOADS[4].n_pad == 12 and wl.WORKLOADS[1].n_pad == 3
+
+
+# ---------------------------------------------------------------------------
+# Send-side ranks (the rows of the receive side, counted by each source)
+# ---------------------------------------------------------------------------
+
+def test_golden_pick_ranks():
+    G = _gold("worked_example.json")
+    g, gp, gb = G["pick_ranks"], G["pack"], G["batch"]
+    cnt = np.array(gp["send_cnt"], np.int32)
+    eloc = np.full((gp["W"], gp["max_num_tokens"], gp["expect_slots"]), -1, np.int32)
+    for d in range(gp["W"]):
+        eloc[d, :cnt[d]] = gp["send_eloc"][d]
+    r = oracle.pick_ranks(cnt, eloc, gp["E"] // gp["W"])
+    for d in range(gp["W"]):
+        assert r["send_rank"][d, :cnt[d]].tolist() == g["send_rank"][d]
+    assert r["send_ecnt"].tolist() == g["send_ecnt"]
+    # the batch example's sources: counts before + rank = the golden rows
+    W, el, cap = gb["W"], gb["e_local"], gb["max_num_tokens"]
+    bcnt = np.array(gb["recv_cnt"], np.int32)
+    beloc = np.array(gb["recv_eloc"], np.int32)
+    before = np.zeros(el, np.int64)
+    for s in range(W):
+        rs = oracle.pick_ranks(bcnt[s:s + 1], beloc[s:s + 1], el)
+        c = int(bcnt[s])
+        assert rs["send_rank"][0, :c].tolist() == g["batch_source_ranks"][s]
+        assert rs["send_ecnt"][0].tolist() == g["batch_source_ecnt"][s]
+        rows = [[int(before[e]) + int(k) if e >= 0 else -1
+                 for e, k in zip(er, kr)]
+                for er, kr in zip(beloc[s, :c].tolist(), rs["send_rank"][0, :c].tolist())]
+        assert rows == gb["recv_row_valid"][s]
+        before += rs["send_ecnt"][0]
+    assert before.tolist() == gb["expert_num_tokens"]
+
+
+def _ranks_by_pairs(ids, E, W):
+    """rank of every kept pick by counting, over all (token, pick) pairs of
+    the source, the earlier kept picks with the same expert id (token order,
+    then router order); the kept picks come from the set formulation."""
+    cnt, slot, picks, _ = brute.pack_sets(ids, np.zeros(ids.shape, np.float32), E, W)
+    e_local = E // W
+    flat = []                         # (token, column, d, global id)
+    for (d, t), lst in picks.items():
+        for j, (e, _) in enumerate(lst):
+            flat.append((t, j, d, d * e_local + e))
+    ranks = {}
+    for (t, j, d, g) in flat:
+        ranks[(d, t, j)] = sum(1 for (t2, j2, d2, g2) in flat
+                               if g2 == g and (t2, j2) < (t, j))
+    ecnt = np.zeros((W, e_local), np.int64)
+    for (t, j, d, g) in flat:
+        ecnt[d, g - d * e_local] += 1
+    return cnt, slot, ranks, ecnt
+
+
+def _check_ranks_against_pairs(ids, E, W):
+    T, K = ids.shape
+    p = oracle.dispatch_pack(ids, np.ones((T, K), np.float32), E, W, T)
+    r = oracle.pick_ranks(p["send_cnt"], p["send_eloc"], E // W)
+    cnt, slot, ranks, ecnt = _ranks_by_pairs(ids, E, W)
+    assert r["send_ecnt"].tolist() == ecnt.tolist(), ids
+    for (d, t), sl in slot.items():
+        n = sum(1 for (d2, t2, _j) in ranks if (d2, t2) == (d, t))
+        want = [ranks[(d, t, j)] for j in range(n)] + [-1] * (p["slots"] - n)
+        assert r["send_rank"][d, sl].tolist() == want, (ids, d, t)
+
+
+@pytest.mark.parametrize("W,K", [(1, 2), (2, 2), (4, 1)])
+def test_pick_ranks_exhaustive_micro(W, K):
+    """Every id tuple over T=3 tokens, E=4 (duplicates and padding included):
+    the oracle's ranks, from the pack's outputs, equal counts over all
+    pairs of the source's kept picks."""
+    E, T = 4, 3
+    vals = [-1, 0, 1, 2, 3]
+    per_tok = list(itertools.product(vals, repeat=K))
+    for combo in itertools.product(per_tok, repeat=T):
+        _check_ranks_against_pairs(np.array(combo, np.int32).reshape(T, K), E, W)
+
+
+def test_pick_ranks_random_micro():
+    """Random sources with more picks per token, duplicates past the pick
+    columns and ids out of range, against the same pair counts."""
+    rng = np.random.default_rng(13)
+    for _ in range(1500):
+        W = int(rng.choice([1, 2, 3, 4]))
+        el = int(rng.integers(1, 4))
+        K = int(rng.integers(1, 6))
+        T = int(rng.integers(0, 8))
+        ids = rng.integers(-2, W * el + 2, size=(T, K)).astype(np.int32)
+        _check_ranks_against_pairs(ids, W * el, W)
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_pick_ranks_give_the_receive_rows(wid):
+    """On every workload (scaled): for each destination, the counts of the
+    sources before s plus the rank equal the receive-side rows of the
+    oracle's batch (taken in (source, slot, pick) order), and the summed
+    counts equal expert_num_tokens."""
+    w = wl.WORKLOADS[wid]
+    if w.T > 300:
+        w = w.scaled(T=300, cap=300)
+    packs, ranks = [], []
+    for s in range(w.W):
+        ids, wts = wl.routing(w, s, 4)
+        packs.append(oracle.dispatch_pack(ids, wts, w.E, w.W, w.cap))
+        ranks.append(oracle.pick_ranks(packs[-1]["send_cnt"], packs[-1]["send_eloc"],
+                                       w.e_local))
+    for r in range(w.W):
+        cnt = np.ascontiguousarray(np.stack([p["send_cnt"][r] for p in packs]))
+        eloc = np.ascontiguousarray(np.stack([p["send_eloc"][r] for p in packs]))
+        b = oracle.expert_batch(cnt, eloc, w.W, w.e_local, w.K, w.cap)
+        before = np.zeros(w.e_local, np.int64)
+        for s in range(w.W):
+            c = int(cnt[s])
+            e = eloc[s, :c]
+            k = ranks[s]["send_rank"][r, :c]
+            rows = np.where(e >= 0, before[np.maximum(e, 0)] + k, -1)
+            assert np.array_equal(rows, b["recv_row"][s, :c]), (r, s)
+            before += ranks[s]["send_ecnt"][r]
+        assert np.array_equal(before, b["expert_num_tokens"])
