@@ -56,6 +56,7 @@ PEAK_HBM_GBPS = 8000.0
 # the rows in each (moe_ep_expert_batch is timed as its two halves).
 KERNEL_OF_CALL = {
     "pack": "pack_copy_kernel",
+    "batch": "batch_copy_kernel",
     "batch_plan": "batch_local_kernel",
     "batch_copy": "batch_copy_kernel",
     "reduce": "combine_reduce_kernel",
@@ -65,6 +66,7 @@ KERNEL_OF_CALL = {
 }
 ABI_OF_CALL = {
     "pack": "moe_ep_dispatch_pack",
+    "batch": "moe_ep_expert_batch_ranked",
     "batch_plan": "moe_ep_expert_batch_plan",
     "batch_copy": "moe_ep_expert_batch_copy",
     "reduce": "moe_ep_combine_reduce",
@@ -123,11 +125,13 @@ def read_traffic(kernel: str, workload: str):
 
 
 def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None,
-               r_own=None):
+               r_own=None, ranked=False):
     """Algorithmic bytes per call kind (lists over ranks). row_bytes: the
     source rows a pack reads; send_row_bytes: the rows that travel (the
     same unless the pack quantises); r_own[s]: expert rows of rank s's
-    local slice (for the fused combine)."""
+    local slice (for the fused combine). ranked: the packs also write each
+    used slot's per-expert ranks and the counts per expert, and the receive
+    side ("batch") reads those instead of scanning."""
     import numpy as np
     P_src = int(sum(row_bytes))
     P = int(sum(send_row_bytes if send_row_bytes is not None else row_bytes))
@@ -143,6 +147,10 @@ def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None,
     unpack = [int(U[s]) * Hb + w.T * Hb for s in range(w.W)]
     out = {"pack": pack, "batch_plan": batch_plan, "batch_copy": batch_copy,
            "reduce": reduce, "unpack": unpack, "U": U, "S": S, "R": R}
+    if ranked:
+        out["pack"] = [pack[s] + int(U[s]) * slots * 4 + 4 * w.E for s in range(w.W)]
+        out["batch"] = [4 * w.W + int(S[r]) * slots * 8 + 4 * w.E + int(S[r]) * P
+                        + int(R[r]) * P + 4 * w.e_local for r in range(w.W)]
     if r_own is not None:
         S_own = [int(send_cnt[s, s]) for s in range(w.W)]
         out["reduce_peers"] = [(int(R[r]) - int(r_own[r])) * Hb
@@ -316,6 +324,9 @@ def main():
     ap.add_argument("--no-contiguous", action="store_true",
                     help="allocate every buffer from torch's caching allocator instead of "
                          "physically contiguous blocks for the large ones")
+    ap.add_argument("--ranked", action="store_true",
+                    help="the packs also write per-expert ranks and the receive side is "
+                         "moe_ep_expert_batch_ranked (no receive scan)")
     ap.add_argument("--fp8-group", type=int, default=None,
                     help="quantize-on-pack: send the bf16 hidden row as fp8 e4m3 "
                          "with one scale per this many columns")
@@ -357,7 +368,7 @@ def main():
         lanes = lanes_that_fit(w, row_bytes, args.fp8_group, args.fp4, int(args.lanes))
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
                    quant_group=args.fp8_group, quant_fp4=args.fp4, lanes=lanes,
-                   contiguous=not args.no_contiguous)
+                   contiguous=not args.no_contiguous, ranked=args.ranked)
     streams = [torch.cuda.Stream() for _ in range(lanes)] if lanes > 1 else None
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
@@ -410,12 +421,14 @@ def main():
     # add a few microseconds between calls, so these steps are timed
     # separately from the region above.
     k_red, k_unp = ("reduce_peers", "unpack_fused") if fused else ("reduce", "unpack")
-    kinds = (["pack"] * w.W + ["batch_plan", "batch_copy", k_red] * w.W
-             + [k_unp] * w.W)
+    recv_kinds = ["batch"] if args.ranked else ["batch_plan", "batch_copy"]
+    recv_calls = [ep.batch] if args.ranked else [ep.batch_plan, ep.batch_copy]
+    kinds = (["pack"] * w.W + (recv_kinds + [k_red]) * w.W + [k_unp] * w.W)
     red_call = ep.reduce_peers if fused else ep.reduce
     unp_call = ep.unpack_fused if fused else ep.unpack
     # rank each call belongs to (source for pack/unpack, destination else)
-    rank_of = list(range(w.W)) + [r for r in range(w.W) for _ in range(3)] + list(range(w.W))
+    rank_of = (list(range(w.W)) + [r for r in range(w.W) for _ in range(len(recv_kinds) + 1)]
+               + list(range(w.W)))
 
     def timed_pass(flush=None):
         ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -431,8 +444,8 @@ def main():
             for s in range(w.W):
                 one(k, i, ep.pack, s); i += 1
             for r in range(w.W):
-                one(k, i, ep.batch_plan, r); i += 1
-                one(k, i, ep.batch_copy, r); i += 1
+                for fn in recv_calls:
+                    one(k, i, fn, r); i += 1
                 one(k, i, red_call, r); i += 1
             for s in range(w.W):
                 one(k, i, unp_call, s); i += 1
@@ -441,7 +454,7 @@ def main():
                 for k in range(args.steps)]
 
     times = timed_pass()
-    calls = ["pack", "batch_plan", "batch_copy", k_red, k_unp]
+    calls = ["pack"] + recv_kinds + [k_red, k_unp]
     per_kind = {k: [] for k in calls}
     for k in range(args.steps):
         for i, kind in enumerate(kinds):
@@ -452,7 +465,8 @@ def main():
         max(sum(t for t, rk in zip(times[k], rank_of) if rk == r) for r in range(w.W))
         for k in range(args.steps)]))
     dispatch_ms = float(np.median([sum(t for t, kd in zip(times[k], kinds)
-                                        if kd in ("pack", "batch_plan", "batch_copy"))
+                                        if kd in ("pack", "batch", "batch_plan",
+                                                  "batch_copy"))
                                     for k in range(args.steps)]))
     combine_ms = float(np.median([sum(t for t, kd in zip(times[k], kinds)
                                        if kd in (k_red, k_unp))
@@ -498,7 +512,7 @@ def main():
         r_own = [int((ep.recv_row[s, s, :int(send_cnt[s, s])] >= 0).sum().item())
                  for s in range(w.W)]
     bm = byte_model(w, row_bytes, ep.slots, send_cnt, ent, routed, ep.send_row_bytes,
-                    r_own)
+                    r_own, ranked=args.ranked)
     step_bytes = sum(sum(bm[k]) for k in calls)
     gbps = step_bytes / (ms_per_step / 1e3) / 1e9
     tokens = w.W * w.T
@@ -567,6 +581,7 @@ def main():
             "large_buffers": ("physically_contiguous" if ep.contiguous_bytes
                               else "caching_allocator"),
             "local_slice_combine": "fused" if fused else "reduce_then_unpack",
+            "receive_rows": ("sender_ranks" if args.ranked else "receive_scan"),
             "parallelism": f"1 GPU, {w.W} logical expert-parallel ranks",
         },
         "effective_gbps": round(gbps, 1),

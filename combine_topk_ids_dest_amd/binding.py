@@ -39,6 +39,7 @@ EXPORTED = (
     "moe_ep_combine_reduce_peers",
     "moe_ep_combine_unpack_fused",
     "moe_ep_dispatch_pack_noalloc",
+    "moe_ep_expert_batch_ranked",
 )
 
 
@@ -78,13 +79,16 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_ep_status_string.restype = ctypes.c_char_p
     lib.moe_ep_dispatch_pack.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
-        _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
+        _P, _P, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_ep_dispatch_pack_noalloc.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
-        _P, _P, _P, _I64, _P, _P, _P]
+        _P, _P, _P, _I64, _P, _P, _P, _P, _P]
     lib.moe_ep_dispatch_pack_fp8.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I64, _I64, _I32,
-        _P, _I64, _P, _I64, _P, _I32, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
+        _P, _I64, _P, _I64, _P, _I32, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_ep_expert_batch_ranked.argtypes = [
+        _P, _I64, _P, _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
+        _P, _P, _P, _P]
     lib.moe_ep_expert_batch.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32,
         _P, _P, _P, _P, _SZ, _P]
@@ -94,7 +98,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _P, _I32, _P, _P, _P, _SZ, _P]
     lib.moe_ep_dispatch_pack_fp4.argtypes = [
         _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _I64, _I64, _P, _I64, _P, _I64,
-        _P, _I32, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
+        _P, _I32, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_ep_sanitize_expert_ids.argtypes = [
         _P, _I64, _P, _I64, _I32, _I32, _I32, _I64, _I32, _P, _I64, _P, _P]
     lib.moe_ep_combine_reduce.argtypes = [
@@ -273,6 +277,21 @@ def _sizes(K: int, E: int, W: int, max_num_tokens: int):
     return e_local, min(K, e_local), max_num_tokens, max_num_tokens * W
 
 
+def _ranks(send_rank, send_ecnt, send_eloc, W, E):
+    """Optional per-expert rank outputs of a pack: both or neither;
+    send_rank shaped and strided like send_eloc, send_ecnt [W, E/W] dense."""
+    if (send_rank is None) != (send_ecnt is None):
+        raise ValueError("send_rank and send_ecnt go together")
+    if send_rank is None:
+        return
+    _shape(send_rank, tuple(send_eloc.shape), "send_rank", _I32T)
+    _dense_from(send_rank, 1, "send_rank")
+    if send_rank.stride(0) != send_eloc.stride(0):
+        raise ValueError("send_rank and send_eloc must share a rank stride")
+    _shape(send_ecnt, (W, E // W), "send_ecnt", _I32T)
+    _dense_from(send_ecnt, 0, "send_ecnt")
+
+
 def _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt, send_eloc,
                send_w, token_slot, err_flags):
     """Checks the routing inputs and metadata outputs of a pack call;
@@ -354,20 +373,25 @@ def prepare_dispatch_pack(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                           send_cnt: torch.Tensor, send_eloc: torch.Tensor,
                           send_w: torch.Tensor, token_slot: torch.Tensor,
                           err_flags: Optional[torch.Tensor],
-                          workspace: torch.Tensor) -> PreparedCall:
+                          workspace: torch.Tensor,
+                          send_rank: Optional[torch.Tensor] = None,
+                          send_ecnt: Optional[torch.Tensor] = None) -> PreparedCall:
     """payloads: (src [T, ...], dst [W, cap, ...]) pairs; send_eloc /
     send_w: [W, cap, slots] with one free rank stride (meta_rank_stride);
-    the rank stride of each dst is free, everything below it dense."""
+    the rank stride of each dst is free, everything below it dense.
+    send_rank (like send_eloc) and send_ecnt [W, e_local]: the optional
+    per-expert ranks for moe_ep_expert_batch_ranked."""
     T, K, cap, _ = _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt,
                               send_eloc, send_w, token_slot, err_flags)
+    _ranks(send_rank, send_ecnt, send_eloc, W, E)
     arr = _payload_array(payloads, 1, 2, (T,), (W, cap))
     args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
             ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
-            _ptr(send_w), send_eloc.stride(0), _ptr(token_slot), _ptr(err_flags),
-            _ptr(workspace), _ws_bytes(workspace))
+            _ptr(send_w), send_eloc.stride(0), _ptr(send_rank), _ptr(send_ecnt),
+            _ptr(token_slot), _ptr(err_flags), _ptr(workspace), _ws_bytes(workspace))
     return PreparedCall("moe_ep_dispatch_pack", args,
                         (arr, topk_ids, topk_weights, payloads, send_cnt, send_eloc,
-                         send_w, token_slot, err_flags, workspace))
+                         send_w, send_rank, send_ecnt, token_slot, err_flags, workspace))
 
 
 def prepare_dispatch_pack_noalloc(topk_ids: torch.Tensor, topk_weights: torch.Tensor,
@@ -375,27 +399,31 @@ def prepare_dispatch_pack_noalloc(topk_ids: torch.Tensor, topk_weights: torch.Te
                                   payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
                                   send_cnt: torch.Tensor, send_eloc: torch.Tensor,
                                   send_w: torch.Tensor, token_slot: torch.Tensor,
-                                  err_flags: Optional[torch.Tensor]) -> PreparedCall:
+                                  err_flags: Optional[torch.Tensor],
+                                  send_rank: Optional[torch.Tensor] = None,
+                                  send_ecnt: Optional[torch.Tensor] = None) -> PreparedCall:
     """moe_ep_dispatch_pack without a workspace: the library's own device
     scratch holds the send side's workspace (moe_ep_dispatch_pack_noalloc;
     calls that overlap on one GPU race on it)."""
     T, K, cap, _ = _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt,
                               send_eloc, send_w, token_slot, err_flags)
+    _ranks(send_rank, send_ecnt, send_eloc, W, E)
     arr = _payload_array(payloads, 1, 2, (T,), (W, cap))
     args = (_ptr(topk_ids), _ptr(topk_weights), T, K, E, W, max_num_tokens,
             ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
-            _ptr(send_w), send_eloc.stride(0), _ptr(token_slot), _ptr(err_flags))
+            _ptr(send_w), send_eloc.stride(0), _ptr(send_rank), _ptr(send_ecnt),
+            _ptr(token_slot), _ptr(err_flags))
     return PreparedCall("moe_ep_dispatch_pack_noalloc", args,
                         (arr, topk_ids, topk_weights, payloads, send_cnt, send_eloc,
-                         send_w, token_slot, err_flags))
+                         send_w, send_rank, send_ecnt, token_slot, err_flags))
 
 
 def moe_ep_dispatch_pack_noalloc(topk_ids, topk_weights, E, W, max_num_tokens, payloads,
                                  send_cnt, send_eloc, send_w, token_slot, err_flags,
-                                 stream=None) -> None:
+                                 stream=None, send_rank=None, send_ecnt=None) -> None:
     prepare_dispatch_pack_noalloc(topk_ids, topk_weights, E, W, max_num_tokens, payloads,
-                                  send_cnt, send_eloc, send_w, token_slot,
-                                  err_flags)(stream)
+                                  send_cnt, send_eloc, send_w, token_slot, err_flags,
+                                  send_rank, send_ecnt)(stream)
 
 
 def scale_pitch(H: int, group: int) -> int:
@@ -411,12 +439,15 @@ def prepare_dispatch_pack_fp8(topk_ids: torch.Tensor, topk_weights: torch.Tensor
                               send_cnt: torch.Tensor, send_eloc: torch.Tensor,
                               send_w: torch.Tensor, token_slot: torch.Tensor,
                               err_flags: Optional[torch.Tensor],
-                              workspace: torch.Tensor) -> PreparedCall:
+                              workspace: torch.Tensor,
+                              send_rank: Optional[torch.Tensor] = None,
+                              send_ecnt: Optional[torch.Tensor] = None) -> PreparedCall:
     """hidden: bf16 [T, H] (token stride free, rows dense); send_q: fp8 codes
     [W, cap, H] (uint8 or float8, rank stride free); send_scale: fp32
     [W, cap, Gp], Gp = H/group rounded up to 4 (rank stride free)."""
     T, K, cap, _ = _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt,
                               send_eloc, send_w, token_slot, err_flags)
+    _ranks(send_rank, send_ecnt, send_eloc, W, E)
     if hidden.dtype != torch.bfloat16:
         raise ValueError("hidden must be bfloat16")
     if hidden.dim() != 2 or hidden.size(0) < T:
@@ -437,12 +468,12 @@ def prepare_dispatch_pack_fp8(topk_ids: torch.Tensor, topk_weights: torch.Tensor
             _ptr(send_q), send_q.stride(0) * send_q.element_size(),
             _ptr(send_scale), send_scale.stride(0),
             ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
-            _ptr(send_w), send_eloc.stride(0), _ptr(token_slot), _ptr(err_flags),
-            _ptr(workspace), _ws_bytes(workspace))
+            _ptr(send_w), send_eloc.stride(0), _ptr(send_rank), _ptr(send_ecnt),
+            _ptr(token_slot), _ptr(err_flags), _ptr(workspace), _ws_bytes(workspace))
     return PreparedCall("moe_ep_dispatch_pack_fp8", args,
                         (arr, topk_ids, topk_weights, hidden, send_q, send_scale,
-                         payloads, send_cnt, send_eloc, send_w, token_slot,
-                         err_flags, workspace))
+                         payloads, send_cnt, send_eloc, send_w, send_rank, send_ecnt,
+                         token_slot, err_flags, workspace))
 
 
 def moe_ep_dispatch_pack_fp8(topk_ids, topk_weights, E, W, max_num_tokens, hidden,
@@ -468,12 +499,15 @@ def prepare_dispatch_pack_fp4(topk_ids: torch.Tensor, topk_weights: torch.Tensor
                               send_cnt: torch.Tensor, send_eloc: torch.Tensor,
                               send_w: torch.Tensor, token_slot: torch.Tensor,
                               err_flags: Optional[torch.Tensor],
-                              workspace: torch.Tensor) -> PreparedCall:
+                              workspace: torch.Tensor,
+                              send_rank: Optional[torch.Tensor] = None,
+                              send_ecnt: Optional[torch.Tensor] = None) -> PreparedCall:
     """hidden: bf16 [T, H] (token stride free, rows dense); send_q: codes
     [W, cap, H/2] bytes; send_scale: e4m3 scale codes [W, cap, Sp] bytes,
     Sp = fp4_scale_pitch(H) (rank strides free)."""
     T, K, cap, _ = _send_side(topk_ids, topk_weights, E, W, max_num_tokens, send_cnt,
                               send_eloc, send_w, token_slot, err_flags)
+    _ranks(send_rank, send_ecnt, send_eloc, W, E)
     if hidden.dtype != torch.bfloat16:
         raise ValueError("hidden must be bfloat16")
     if hidden.dim() != 2 or hidden.size(0) < T:
@@ -495,12 +529,12 @@ def prepare_dispatch_pack_fp4(topk_ids: torch.Tensor, topk_weights: torch.Tensor
             _ptr(send_q), send_q.stride(0) * send_q.element_size(),
             _ptr(send_scale), send_scale.stride(0) * send_scale.element_size(),
             ctypes.addressof(arr), len(payloads), _ptr(send_cnt), _ptr(send_eloc),
-            _ptr(send_w), send_eloc.stride(0), _ptr(token_slot), _ptr(err_flags),
-            _ptr(workspace), _ws_bytes(workspace))
+            _ptr(send_w), send_eloc.stride(0), _ptr(send_rank), _ptr(send_ecnt),
+            _ptr(token_slot), _ptr(err_flags), _ptr(workspace), _ws_bytes(workspace))
     return PreparedCall("moe_ep_dispatch_pack_fp4", args,
                         (arr, topk_ids, topk_weights, hidden, send_q, send_scale,
-                         payloads, send_cnt, send_eloc, send_w, token_slot,
-                         err_flags, workspace))
+                         payloads, send_cnt, send_eloc, send_w, send_rank, send_ecnt,
+                         token_slot, err_flags, workspace))
 
 
 def moe_ep_dispatch_pack_fp4(topk_ids, topk_weights, E, W, max_num_tokens, hidden,
@@ -514,10 +548,10 @@ def moe_ep_dispatch_pack_fp4(topk_ids, topk_weights, E, W, max_num_tokens, hidde
 
 def moe_ep_dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens, payloads,
                          send_cnt, send_eloc, send_w, token_slot, err_flags,
-                         workspace, stream=None) -> None:
+                         workspace, stream=None, send_rank=None, send_ecnt=None) -> None:
     prepare_dispatch_pack(topk_ids, topk_weights, E, W, max_num_tokens, payloads,
                           send_cnt, send_eloc, send_w, token_slot, err_flags,
-                          workspace)(stream)
+                          workspace, send_rank, send_ecnt)(stream)
 
 
 def prepare_expert_batch(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
@@ -550,6 +584,44 @@ def moe_ep_expert_batch(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
     prepare_expert_batch(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens,
                          payloads, expert_num_tokens, recv_row, err_flags,
                          workspace)(stream)
+
+
+def prepare_expert_batch_ranked(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,
+                                recv_rank: torch.Tensor, recv_ecnt: torch.Tensor,
+                                W: int, e_local: int, K: int, max_num_tokens: int,
+                                payloads: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                                expert_num_tokens: torch.Tensor, recv_row: torch.Tensor,
+                                err_flags: Optional[torch.Tensor]) -> PreparedCall:
+    """moe_ep_expert_batch from the sources' per-expert ranks: recv_rank
+    [W, cap, slots] with recv_eloc's rank stride; recv_ecnt [W, e_local]
+    (rank stride free, rows dense). No workspace."""
+    slots, cap, ecap = _receive_side(recv_cnt, recv_eloc, W, e_local, K, max_num_tokens)
+    _blocks(recv_rank, W, cap * slots, "recv_rank", _I32T)
+    if recv_rank.stride(0) != recv_eloc.stride(0):
+        raise ValueError("recv_rank and recv_eloc must share a rank stride")
+    _shape(recv_ecnt, (W, e_local), "recv_ecnt", _I32T)
+    _dense_from(recv_ecnt, 1, "recv_ecnt")
+    _shape(recv_row, (W, cap, slots), "recv_row", _I32T)
+    _dense_from(recv_row, 0, "recv_row")
+    _shape(expert_num_tokens, (e_local,), "expert_num_tokens", _I32T)
+    _dense_from(expert_num_tokens, 0, "expert_num_tokens")
+    _err(err_flags)
+    arr = _payload_array(payloads, 2, 2, (W, cap), (e_local, ecap))
+    args = (_ptr(recv_cnt), recv_cnt.stride(0), _ptr(recv_eloc), _ptr(recv_rank),
+            recv_eloc.stride(0), _ptr(recv_ecnt), recv_ecnt.stride(0), W, e_local, K,
+            max_num_tokens, ctypes.addressof(arr), len(payloads), _ptr(expert_num_tokens),
+            _ptr(recv_row), _ptr(err_flags))
+    return PreparedCall("moe_ep_expert_batch_ranked", args,
+                        (arr, recv_cnt, recv_eloc, recv_rank, recv_ecnt, payloads,
+                         expert_num_tokens, recv_row, err_flags))
+
+
+def moe_ep_expert_batch_ranked(recv_cnt, recv_eloc, recv_rank, recv_ecnt, W, e_local, K,
+                               max_num_tokens, payloads, expert_num_tokens, recv_row,
+                               err_flags, stream=None) -> None:
+    prepare_expert_batch_ranked(recv_cnt, recv_eloc, recv_rank, recv_ecnt, W, e_local, K,
+                                max_num_tokens, payloads, expert_num_tokens, recv_row,
+                                err_flags)(stream)
 
 
 def prepare_expert_batch_plan(recv_cnt: torch.Tensor, recv_eloc: torch.Tensor,

@@ -90,10 +90,18 @@ int check_shape(int32_t K, int32_t e_local, int32_t W, int64_t max_num_tokens,
 }
 
 // Workspace regions, each padded to 128 bytes.
-struct PackWs { int64_t ntiles, cnt_off, off_off, rank_off, bytes; };
+struct PackWs {
+    int64_t ntiles, cnt_off, off_off, rank_off;
+    int64_t prank_off, ecnt_off, eoff_off;   // with the per-expert ranks
+    int64_t bytes;
+};
 struct BatchWs { int64_t ntiles, cnt_off, off_off, bytes; };
 
-PackWs pack_ws(int64_t T, int32_t W) {
+// Send side: destination tile counts and offsets [tiles][W], in-tile ranks
+// [W][T]; with the per-expert ranks also the in-tile ranks of the picks
+// [T * K] and expert tile counts and offsets [tiles][E]. (T, W, K and E are
+// bounded by the callers' checks, so nothing here overflows.)
+PackWs pack_ws(int64_t T, int32_t W, int32_t K, int32_t E, bool ranked) {
     PackWs w;
     w.ntiles = (T + kRouteTile - 1) / kRouteTile;
     const int64_t region = round_up(w.ntiles * W * 4, 128);
@@ -101,7 +109,24 @@ PackWs pack_ws(int64_t T, int32_t W) {
     w.off_off = region;
     w.rank_off = 2 * region;
     w.bytes = w.rank_off + round_up(T * W * 4, 128);
+    w.prank_off = w.ecnt_off = w.eoff_off = 0;
+    if (ranked) {
+        const int64_t eregion = round_up(w.ntiles * E * 4, 128);
+        w.prank_off = w.bytes;
+        w.ecnt_off = w.prank_off + round_up(T * K * 4, 128);
+        w.eoff_off = w.ecnt_off + eregion;
+        w.bytes = w.eoff_off + eregion;
+    }
     return w;
+}
+
+// The per-expert ranks fit their LDS tables for these sizes.
+inline bool rank_sizes_ok(int32_t K, int32_t E) { return K <= kRankMaxK && E <= kRankMaxE; }
+
+inline int id_bits(int32_t E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
 }
 
 BatchWs batch_ws(const Shape& sh) {
@@ -201,7 +226,7 @@ int launch_copy(const int32_t* recv_cnt, int64_t cnt_rank_stride,
     return hip_status(launch_batch_copy(recv_cnt, cnt_rank_stride, recv_eloc,
                                         eloc_rank_stride, sh.W, sh.e_local,
                                         sh.slots, sh.cap, tile_off, nullptr, 0, nullptr,
-                                        0, recv_row, P, err_flags, st));
+                                        nullptr, 0, nullptr, 0, recv_row, P, err_flags, st));
 }
 
 }  // namespace
@@ -228,7 +253,8 @@ int moe_ep_workspace_bytes(int64_t T, int32_t K, int32_t E, int32_t W,
     Shape sh;
     const int rc = check_shape(K, E / W, W, max_num_tokens, &sh);
     if (rc) return rc;
-    const int64_t a = pack_ws(max_num_tokens, W).bytes;
+    // the send side with the per-expert ranks where they are supported
+    const int64_t a = pack_ws(max_num_tokens, W, K, E, rank_sizes_ok(K, E)).bytes;
     const int64_t b = batch_ws(sh).bytes;
     *bytes = (size_t)(a > b ? a : b);
     return MOE_EP_OK;
@@ -288,9 +314,10 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
              int32_t K, int32_t E, int32_t W, int64_t max_num_tokens,
              const moe_ep_payload* payloads, int32_t n_payloads,
              const QuantArgs* quant, int32_t* send_cnt, int32_t* send_eloc,
-             float* send_w, int64_t meta_rank_stride, int32_t* token_slot,
-             uint32_t* err_flags, void* workspace, size_t workspace_bytes,
-             void* stream, bool use_scratch = false) {
+             float* send_w, int64_t meta_rank_stride, int32_t* send_rank,
+             int32_t* send_ecnt, int32_t* token_slot, uint32_t* err_flags,
+             void* workspace, size_t workspace_bytes, void* stream,
+             bool use_scratch = false) {
     if (E <= 0 || W <= 0 || E % W != 0 || T < 0) return MOE_EP_EINVAL;
     Shape sh;
     int rc = check_shape(K, E / W, W, max_num_tokens, &sh);
@@ -302,6 +329,9 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
     // the last block must fit in int64_t
     if (meta_rank_stride < sh.cap * sh.slots || meta_rank_stride > INT64_MAX / W)
         return MOE_EP_EINVAL;
+    // the per-expert ranks: both outputs or neither, within their limits
+    const bool ranked = send_rank != nullptr || send_ecnt != nullptr;
+    if (ranked && (!send_rank || !send_ecnt || !rank_sizes_ok(K, E))) return MOE_EP_EINVAL;
     if (T > 0 && (!topk_ids || !topk_weights || !token_slot)) return MOE_EP_EINVAL;
     PayloadSet P;
     rc = check_payloads(payloads, n_payloads, 1, sh.cap, T > 0, &P);
@@ -329,7 +359,7 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
             Q.q_stride % 16 || !aligned16(Q.s) || Q.s_stride % 16)
             return MOE_EP_EALIGN;
     }
-    const PackWs ws = pack_ws(T, W);
+    const PackWs ws = pack_ws(T, W, K, E, ranked);
     // one tile of tokens needs no workspace (the pack routes by itself)
     const bool own_route = T > 0 && T <= kRouteTile;
     if (use_scratch) {
@@ -349,31 +379,54 @@ int dispatch(const int32_t* topk_ids, const float* topk_weights, int64_t T,
     int32_t* tile_cnt = reinterpret_cast<int32_t*>(wsb + ws.cnt_off);
     int32_t* tile_off = reinterpret_cast<int32_t*>(wsb + ws.off_off);
     int32_t* rank = reinterpret_cast<int32_t*>(wsb + ws.rank_off);
+    RankArgs R{};
+    if (ranked) {
+        R.send_rank = send_rank;
+        R.send_ecnt = send_ecnt;
+        R.nbits = id_bits(E);
+    }
 
     // One tile of tokens (decode-sized batches): pack_copy routes by itself
-    // and writes send_cnt; no separate routing launch.
+    // and writes send_cnt (and, ranked, the ranks and send_ecnt); no
+    // separate routing launch.
     if (own_route)
         return hip_status(launch_pack_copy(topk_ids, topk_weights, T, K, E,
                                            sh.e_local, W, sh.slots, sh.cap, nullptr,
                                            token_slot, nullptr, nullptr, send_cnt, P,
                                            quant, send_eloc, send_w, meta_rank_stride,
-                                           err_flags, st));
-    rc = hip_status(launch_route_local(topk_ids, T, K, E, sh.e_local, W,
-                                       rank, tile_cnt, err_flags, st));
+                                           ranked ? &R : nullptr, err_flags, st));
+    int32_t* prank = ranked ? reinterpret_cast<int32_t*>(wsb + ws.prank_off) : nullptr;
+    int32_t* ecnt_tile = ranked ? reinterpret_cast<int32_t*>(wsb + ws.ecnt_off) : nullptr;
+    int32_t* eoff_tile = ranked ? reinterpret_cast<int32_t*>(wsb + ws.eoff_off) : nullptr;
+    rc = hip_status(launch_route_local(topk_ids, T, K, E, sh.e_local, W, sh.slots,
+                                       rank, tile_cnt, prank, ecnt_tile, R.nbits,
+                                       err_flags, st));
     if (rc) return rc;
     // Few tiles (or none): pack_copy sums the tile counts itself; the scan
-    // kernel still runs for T = 0 so that send_cnt is written.
+    // kernels still run for T = 0 so that send_cnt (and send_ecnt) are
+    // written.
     const bool fused = ws.ntiles > 0 && ws.ntiles <= kPackFuseTiles;
     if (!fused) {
         rc = hip_status(launch_column_scan(tile_cnt, (int)ws.ntiles, W, tile_off,
                                            send_cnt, INT_MAX, st));
         if (rc) return rc;
+        if (ranked) {
+            rc = hip_status(launch_column_scan(ecnt_tile, (int)ws.ntiles, E, eoff_tile,
+                                               send_ecnt, INT_MAX, st));
+            if (rc) return rc;
+        }
+    }
+    if (ranked) {
+        R.prank = prank;
+        R.ecnt_tile = ecnt_tile;
+        R.eoff_tile = fused ? nullptr : eoff_tile;
     }
     return hip_status(launch_pack_copy(topk_ids, topk_weights, T, K, E,
                                        sh.e_local, W, sh.slots, sh.cap, rank,
                                        token_slot, fused ? tile_cnt : nullptr,
                                        tile_off, send_cnt, P, quant, send_eloc,
-                                       send_w, meta_rank_stride, err_flags, st));
+                                       send_w, meta_rank_stride, ranked ? &R : nullptr,
+                                       err_flags, st));
 }
 
 }  // namespace
@@ -385,12 +438,13 @@ int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_weights,
                          int64_t max_num_tokens,
                          const moe_ep_payload* payloads, int32_t n_payloads,
                          int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                         int64_t meta_rank_stride, int32_t* token_slot,
-                         uint32_t* err_flags, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         int64_t meta_rank_stride, int32_t* send_rank, int32_t* send_ecnt,
+                         int32_t* token_slot, uint32_t* err_flags, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
                     n_payloads, nullptr, send_cnt, send_eloc, send_w, meta_rank_stride,
-                    token_slot, err_flags, workspace, workspace_bytes, stream);
+                    send_rank, send_ecnt, token_slot, err_flags, workspace,
+                    workspace_bytes, stream);
 }
 
 int moe_ep_dispatch_pack_noalloc(const int32_t* topk_ids, const float* topk_weights,
@@ -398,11 +452,12 @@ int moe_ep_dispatch_pack_noalloc(const int32_t* topk_ids, const float* topk_weig
                                  int64_t max_num_tokens,
                                  const moe_ep_payload* payloads, int32_t n_payloads,
                                  int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                                 int64_t meta_rank_stride, int32_t* token_slot,
+                                 int64_t meta_rank_stride, int32_t* send_rank,
+                                 int32_t* send_ecnt, int32_t* token_slot,
                                  uint32_t* err_flags, void* stream) {
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
                     n_payloads, nullptr, send_cnt, send_eloc, send_w, meta_rank_stride,
-                    token_slot, err_flags, nullptr, 0, stream, true);
+                    send_rank, send_ecnt, token_slot, err_flags, nullptr, 0, stream, true);
 }
 
 int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
@@ -413,9 +468,9 @@ int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
                              float* send_scale, int64_t scale_rank_stride,
                              const moe_ep_payload* payloads, int32_t n_payloads,
                              int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                             int64_t meta_rank_stride, int32_t* token_slot,
-                             uint32_t* err_flags, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             int64_t meta_rank_stride, int32_t* send_rank,
+                             int32_t* send_ecnt, int32_t* token_slot, uint32_t* err_flags,
+                             void* workspace, size_t workspace_bytes, void* stream) {
     QuantArgs Q;
     Q.src = static_cast<const uint8_t*>(hidden);
     Q.src_stride = hidden_stride;
@@ -433,7 +488,8 @@ int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* topk_weights,
     Q.mode = 1;
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
                     n_payloads, &Q, send_cnt, send_eloc, send_w, meta_rank_stride,
-                    token_slot, err_flags, workspace, workspace_bytes, stream);
+                    send_rank, send_ecnt, token_slot, err_flags, workspace,
+                    workspace_bytes, stream);
 }
 
 int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
@@ -444,9 +500,9 @@ int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
                              int64_t scale_rank_stride,
                              const moe_ep_payload* payloads, int32_t n_payloads,
                              int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                             int64_t meta_rank_stride, int32_t* token_slot,
-                             uint32_t* err_flags, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             int64_t meta_rank_stride, int32_t* send_rank,
+                             int32_t* send_ecnt, int32_t* token_slot, uint32_t* err_flags,
+                             void* workspace, size_t workspace_bytes, void* stream) {
     QuantArgs Q;
     Q.src = static_cast<const uint8_t*>(hidden);
     Q.src_stride = hidden_stride;
@@ -461,7 +517,8 @@ int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* topk_weights,
     Q.mode = 2;
     return dispatch(topk_ids, topk_weights, T, K, E, W, max_num_tokens, payloads,
                     n_payloads, &Q, send_cnt, send_eloc, send_w, meta_rank_stride,
-                    token_slot, err_flags, workspace, workspace_bytes, stream);
+                    send_rank, send_ecnt, token_slot, err_flags, workspace,
+                    workspace_bytes, stream);
 }
 
 int moe_ep_expert_batch_plan(const int32_t* recv_cnt, int64_t cnt_rank_stride,
@@ -538,14 +595,45 @@ int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_stride,
         return hip_status(launch_batch_copy(recv_cnt, cnt_rank_stride, recv_eloc,
                                             eloc_rank_stride, sh.W, sh.e_local, sh.slots,
                                             sh.cap, nullptr, tile_cnt, (int)ws.ntiles,
-                                            expert_num_tokens, clamp, recv_row, P,
-                                            err_flags, st));
+                                            nullptr, nullptr, 0, expert_num_tokens, clamp,
+                                            recv_row, P, err_flags, st));
     }
     rc = launch_plan(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride, sh, ws,
                      expert_num_tokens, recv_row, err_flags, workspace, st);
     if (rc) return rc;
     return launch_copy(recv_cnt, cnt_rank_stride, recv_eloc, eloc_rank_stride, sh, ws,
                        P, recv_row, err_flags, workspace, st);
+}
+
+int moe_ep_expert_batch_ranked(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                               const int32_t* recv_eloc, const int32_t* recv_rank,
+                               int64_t eloc_rank_stride, const int32_t* recv_ecnt,
+                               int64_t ecnt_rank_stride, int32_t W, int32_t e_local,
+                               int32_t K, int64_t max_num_tokens,
+                               const moe_ep_payload* payloads, int32_t n_payloads,
+                               int32_t* expert_num_tokens, int32_t* recv_row,
+                               uint32_t* err_flags, void* stream) {
+    Shape sh;
+    int rc = check_shape(K, e_local, W, max_num_tokens, &sh);
+    if (rc) return rc;
+    if (!recv_cnt || !recv_eloc || !recv_rank || !recv_ecnt || !expert_num_tokens ||
+        !recv_row)
+        return MOE_EP_EINVAL;
+    // the per-source counts' prefix is an LDS table of (W + 1) * e_local
+    if (!rank_sizes_ok(1, W * e_local)) return MOE_EP_EINVAL;
+    if (cnt_rank_stride < 1 || eloc_rank_stride < sh.cap * sh.slots ||
+        ecnt_rank_stride < e_local)
+        return MOE_EP_EINVAL;
+    PayloadSet P;
+    rc = check_payloads(payloads, n_payloads, sh.cap, sh.expert_cap, true, &P);
+    if (rc) return rc;
+    const int32_t clamp = sh.expert_cap < kI32Max ? (int32_t)sh.expert_cap : INT_MAX;
+    return hip_status(launch_batch_copy(recv_cnt, cnt_rank_stride, recv_eloc,
+                                        eloc_rank_stride, sh.W, sh.e_local, sh.slots,
+                                        sh.cap, nullptr, nullptr, 0, recv_rank, recv_ecnt,
+                                        ecnt_rank_stride, expert_num_tokens, clamp,
+                                        recv_row, P, err_flags,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int moe_ep_sanitize_expert_ids(const int32_t* recv_cnt, int64_t cnt_rank_stride,

@@ -18,7 +18,10 @@
 //     offset; the row is read once and stored to each of its experts' rows.
 // With few tiles (moe_ep_expert_batch, at most kBatchFuseTiles) there is no
 // column_scan: batch_copy sums the tile offset of each pick from the tile
-// counts itself and its block 0 writes expert_num_tokens.
+// counts itself and its block 0 writes expert_num_tokens. With the sources'
+// per-expert ranks (moe_ep_expert_batch_ranked) neither scan runs: a row is
+// the counts of the sources before plus the rank, so batch_copy is the
+// whole receive side.
 #include "common.h"
 
 namespace moe_ep {
@@ -136,16 +139,45 @@ constexpr int kBatchUnroll = 4;
 #define MOE_EP_BATCH_PREFETCH_VECS 512
 #endif
 
-// FUSED: tile offsets summed here from tile_cnt (fused_tiles tiles), and
-// block 0 writes expert_num_tokens (clamped to clamp_max); otherwise they
-// come from column_scan (tile_off).
-template <bool PREFETCH, bool FUSED>
+// Where a pick's expert row comes from:
+//   kRowsScanned: the receive scan (batch_local's in-tile rank in recv_row
+//     plus the tile offset from column_scan, tile_off);
+//   kRowsFused: the same, with the tile offset summed here from tile_cnt
+//     (fused_tiles tiles) and expert_num_tokens written by block 0;
+//   kRowsRanked: the sources' per-expert ranks (recv_rank, beside the local
+//     ids) plus the counts of the sources before, summed per pick from
+//     recv_ecnt; block 0 writes expert_num_tokens. No receive scan and no
+//     workspace.
+constexpr int kRowsScanned = 0;
+constexpr int kRowsFused = 1;
+constexpr int kRowsRanked = 2;
+
+// The counts of local expert e sent by the sources before s: the sum of
+// recv_ecnt[s', e] over s' < s, each clamped to [0, expert_cap] (loads
+// issued 8 at a time; a sum that reaches expert_cap only gives rows that
+// are dropped, so it stops growing there).
+__device__ __forceinline__ int64_t counts_before(const int32_t* __restrict__ recv_ecnt,
+                                                 int64_t ecnt_stride, int s, int e,
+                                                 int64_t expert_cap) {
+    int64_t sum = 0;
+    for (int s0 = 0; s0 < s; s0 += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = s0 + u < s ? recv_ecnt[(s0 + u) * ecnt_stride + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u] < 0 ? 0 : (v[u] > expert_cap ? expert_cap : v[u]);
+    }
+    return sum < expert_cap ? sum : expert_cap;
+}
+
+template <bool PREFETCH, int ROWS>
 __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
     const int32_t* __restrict__ recv_cnt, int64_t cnt_stride,
     const int32_t* __restrict__ recv_eloc, int64_t eloc_stride, int W,
     int e_local, int slots, int64_t cap, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ tile_cnt, int32_t fused_tiles,
-    int32_t* __restrict__ expert_num_tokens, int32_t clamp_max,
+    const int32_t* __restrict__ recv_rank, const int32_t* __restrict__ recv_ecnt,
+    int64_t ecnt_stride, int32_t* __restrict__ expert_num_tokens, int32_t clamp_max,
     int32_t* __restrict__ recv_row, const PayloadSet P,
     uint32_t* __restrict__ err) {
     __shared__ int32_t pre[MOE_EP_MAX_WORLD + 1];
@@ -155,11 +187,21 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
     const int tid = threadIdx.x;
     const int64_t expert_cap = (int64_t)W * cap;
 
-    if (tid < 64) load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre, nullptr);
-    if (FUSED && blockIdx.x == 0) {
+    // (a count outside [0, cap] is reported by the receive scan, or here
+    // by block 0 when no scan runs)
+    if (tid < 64)
+        load_recv_prefix(recv_cnt, cnt_stride, W, cap, pre,
+                         ROWS == kRowsRanked && blockIdx.x == 0 ? err : nullptr);
+    if (ROWS == kRowsFused && blockIdx.x == 0) {
         for (int e = tid; e < e_local; e += kBatchThreads) {
             const int32_t tot = sum_tile_column(tile_cnt, fused_tiles, e_local, e);
             expert_num_tokens[e] = tot < clamp_max ? tot : clamp_max;
+        }
+    }
+    if (ROWS == kRowsRanked && blockIdx.x == 0) {
+        for (int e = tid; e < e_local; e += kBatchThreads) {
+            const int64_t tot = counts_before(recv_ecnt, ecnt_stride, W, e, expert_cap);
+            expert_num_tokens[e] = tot < clamp_max ? (int32_t)tot : clamp_max;
         }
     }
     __syncthreads();
@@ -192,18 +234,33 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
             uint32_t bad = 0;
             if (j < slots) {
                 const int64_t at = ((int64_t)s * cap + slot) * slots + j;
-                // the provisional row is loaded with the id, not after it
-                e = recv_eloc[s * eloc_stride + (int64_t)slot * slots + j];
-                const int32_t prov = recv_row[at];
-                const bool ok = e >= 0 && e < e_local;
-                const int32_t q = v * slots + j;
-                const int32_t off =
-                    FUSED ? sum_tile_column(tile_cnt, q / kBatchTile, e_local, ok ? e : 0)
-                          : tile_off[(int64_t)(q / kBatchTile) * e_local + (ok ? e : 0)];
-                if (ok) {
-                    const int64_t r = (int64_t)prov + off;
-                    if (r < expert_cap) row = (int32_t)r;
-                    else bad |= MOE_EP_ERR_ROWCAP;
+                const int64_t meta = s * eloc_stride + (int64_t)slot * slots + j;
+                if (ROWS == kRowsRanked) {
+                    // the rank is loaded with the id, not after it
+                    e = recv_eloc[meta];
+                    const int32_t rk = recv_rank[meta];
+                    if (e >= e_local) bad |= MOE_EP_ERR_ELOC;
+                    if (e >= 0 && e < e_local) {
+                        const int64_t r =
+                            counts_before(recv_ecnt, ecnt_stride, s, e, expert_cap) + rk;
+                        if (rk >= 0 && r < expert_cap) row = (int32_t)r;
+                        else bad |= MOE_EP_ERR_ROWCAP;
+                    }
+                } else {
+                    // the provisional row is loaded with the id, not after it
+                    e = recv_eloc[meta];
+                    const int32_t prov = recv_row[at];
+                    const bool ok = e >= 0 && e < e_local;
+                    const int32_t q = v * slots + j;
+                    const int32_t off =
+                        ROWS == kRowsFused
+                            ? sum_tile_column(tile_cnt, q / kBatchTile, e_local, ok ? e : 0)
+                            : tile_off[(int64_t)(q / kBatchTile) * e_local + (ok ? e : 0)];
+                    if (ok) {
+                        const int64_t r = (int64_t)prov + off;
+                        if (r < expert_cap) row = (int32_t)r;
+                        else bad |= MOE_EP_ERR_ROWCAP;
+                    }
                 }
                 recv_row[at] = row;
             }
@@ -325,24 +382,32 @@ hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
                              const int32_t* recv_eloc, int64_t eloc_stride,
                              int W, int e_local, int slots, int64_t cap,
                              const int32_t* tile_off, const int32_t* tile_cnt,
-                             int fused_tiles, int32_t* expert_num_tokens,
-                             int32_t clamp_max, int32_t* recv_row,
-                             const PayloadSet& P, uint32_t* err,
+                             int fused_tiles, const int32_t* recv_rank,
+                             const int32_t* recv_ecnt, int64_t ecnt_stride,
+                             int32_t* expert_num_tokens, int32_t clamp_max,
+                             int32_t* recv_row, const PayloadSet& P, uint32_t* err,
                              hipStream_t stream) {
     const int64_t max_rows = (int64_t)W * cap;
-    if (max_rows == 0) return hipSuccess;
-    const int64_t grid = max_rows < MOE_EP_ROW_GRID ? max_rows : MOE_EP_ROW_GRID;
+    // (the ranked form also writes expert_num_tokens when nothing arrives)
+    if (max_rows == 0 && recv_rank == nullptr) return hipSuccess;
+    int64_t grid = max_rows < MOE_EP_ROW_GRID ? max_rows : MOE_EP_ROW_GRID;
+    if (grid < 1) grid = 1;
     const bool pf = P.n == 1 && P.row_bytes[0] / 16 > MOE_EP_BATCH_PREFETCH_VECS;
-#define MOE_EP_BATCH_COPY_LAUNCH(PFV, FUSEDV)                                              \
-    batch_copy_kernel<PFV, FUSEDV><<<dim3((unsigned)grid), dim3(kBatchThreads), 0, stream>>>( \
-        recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap, tile_off,     \
-        tile_cnt, fused_tiles, expert_num_tokens, clamp_max, recv_row, P, err)
-    if (tile_cnt) {
-        if (pf) MOE_EP_BATCH_COPY_LAUNCH(true, true);
-        else MOE_EP_BATCH_COPY_LAUNCH(false, true);
+    const size_t lds = 0;
+#define MOE_EP_BATCH_COPY_LAUNCH(PFV, ROWSV)                                                \
+    batch_copy_kernel<PFV, ROWSV><<<dim3((unsigned)grid), dim3(kBatchThreads), lds, stream>>>( \
+        recv_cnt, cnt_stride, recv_eloc, eloc_stride, W, e_local, slots, cap, tile_off,      \
+        tile_cnt, fused_tiles, recv_rank, recv_ecnt, ecnt_stride, expert_num_tokens,          \
+        clamp_max, recv_row, P, err)
+    if (recv_rank) {
+        if (pf) MOE_EP_BATCH_COPY_LAUNCH(true, kRowsRanked);
+        else MOE_EP_BATCH_COPY_LAUNCH(false, kRowsRanked);
+    } else if (tile_cnt) {
+        if (pf) MOE_EP_BATCH_COPY_LAUNCH(true, kRowsFused);
+        else MOE_EP_BATCH_COPY_LAUNCH(false, kRowsFused);
     } else {
-        if (pf) MOE_EP_BATCH_COPY_LAUNCH(true, false);
-        else MOE_EP_BATCH_COPY_LAUNCH(false, false);
+        if (pf) MOE_EP_BATCH_COPY_LAUNCH(true, kRowsScanned);
+        else MOE_EP_BATCH_COPY_LAUNCH(false, kRowsScanned);
     }
 #undef MOE_EP_BATCH_COPY_LAUNCH
     return hipGetLastError();

@@ -127,6 +127,152 @@ __device__ __forceinline__ uint64_t token_dest_mask(const int32_t* __restrict__ 
     return mask;
 }
 
+// ---------------------------------------------------------------------
+// Send-side per-expert ranks. On the vLLM alltoall_batched page the
+// receive side gives a local expert's rows to its picks in (source, slot,
+// column) order; within one source that is the order it sends in (tokens
+// ascending, router order), so a source can count its own share: each kept
+// pick's rank among the source's kept picks of the same expert, and the
+// number per expert. The receiver adds the counts of the sources before.
+// Limits of this form: K <= kRankMaxK picks per token and E <= kRankMaxE.
+// ---------------------------------------------------------------------
+constexpr int kRankMaxK = 16;
+constexpr int kRankMaxE = 4096;
+// Up to this many experts the masks of the fast form fit in LDS
+// (4 waves x E x 8 bytes).
+constexpr int kRankMaskE = 1024;
+
+struct RankArgs {
+    int32_t* send_rank;          // like send_eloc (meta stride); nullptr: not asked for
+    int32_t* send_ecnt;          // [W, e_local] dense, every entry written
+    const int32_t* prank;        // in-tile ranks [T * K] (route_local), or nullptr
+    const int32_t* ecnt_tile;    // [tiles][E] counts per tile (prefix summed here)
+    const int32_t* eoff_tile;    // [tiles][E] tile offsets (column_scan), or nullptr
+    int nbits;                   // bits of an expert id: E <= 2^nbits
+};
+
+// Kept picks of one token in router order, in registers: a valid id
+// (0 <= id < E) is kept while fewer than `slots` earlier valid picks of the
+// token go to the same rank (the others are dropped, as the pack drops
+// them). key[k] = id of a kept pick, else -1 (also for k >= K). K <=
+// kRankMaxK. Loops are unrolled to kRankMaxK so that the ids stay in
+// registers and their loads are all in flight together.
+__device__ __forceinline__ void kept_keys(const int32_t* __restrict__ row, int K, int E,
+                                          int e_local, int slots,
+                                          int32_t (&key)[kRankMaxK]) {
+    int32_t dst[kRankMaxK];
+#pragma unroll
+    for (int k = 0; k < kRankMaxK; ++k) key[k] = k < K ? row[k] : -1;
+#pragma unroll
+    for (int k = 0; k < kRankMaxK; ++k)
+        if (key[k] >= E) key[k] = -1;
+    if (slots >= K) return;   // a rank can take all K picks of a token
+#pragma unroll
+    for (int k = 0; k < kRankMaxK; ++k)
+        dst[k] = key[k] >= 0 ? (int32_t)((uint32_t)key[k] / (uint32_t)e_local) : -1;
+#pragma unroll
+    for (int k = kRankMaxK - 1; k > 0; --k) {
+        int before = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) before += (dst[k2] >= 0 && dst[k2] == dst[k]) ? 1 : 0;
+        if (before >= slots) key[k] = -1;
+    }
+}
+
+// Whether a token's kept ids hold an expert twice (only possible with
+// duplicate ids in its routing).
+__device__ __forceinline__ bool has_repeated_key(const int32_t (&key)[kRankMaxK]) {
+    bool rep = false;
+#pragma unroll
+    for (int k = 1; k < kRankMaxK; ++k)
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) rep |= key[k] >= 0 && key[k] == key[k2];
+    return rep;
+}
+
+// Ranks of the kept picks of one tile of tokens among the tile's kept picks
+// of the same expert, in (token, router order). keys[i], i = t_local*K + k
+// for the tile's n entries (LDS): expert id or -1. Wave w owns the entries
+// of its 64 tokens, [64*K*w, 64*K*(w+1)), and walks them in chunks of 64:
+// a multi-split over the nbits bits of the id gives each entry its rank
+// among the chunk's entries of the same expert, to which the wave's running
+// count of that expert (hist row w, LDS, zeroed by the caller) is added;
+// the group's first lane then advances that count. The rows of hist become
+// prefixes over the waves, and row `waves` the tile's count per expert.
+// rank[i] (LDS): the rank within the tile, -1 for an entry that is not a
+// kept pick. All threads of the block call this; it ends with a barrier.
+__device__ __forceinline__ void tile_expert_ranks(const int16_t* keys, int16_t* rank,
+                                                  int n, int K, int E, int nbits,
+                                                  int16_t* hist, int waves) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int16_t* h = hist + wave * E;
+    for (int c = 0; c < K; ++c) {
+        const int i = wave * 64 * K + c * 64 + lane;
+        const int32_t g = i < n ? keys[i] : -1;
+        uint64_t peers = __ballot(g >= 0);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t ones = __ballot(g >= 0 && ((g >> b) & 1));
+            peers &= ((g >> b) & 1) ? ones : ~ones;
+        }
+        // every lane reads the running count before the group's first lane
+        // advances it (one instruction stream: the read precedes the write)
+        const int32_t before = g >= 0 ? h[g] : 0;
+        const int r = rank_below(peers);
+        if (g >= 0 && r == 0) h[g] = (int16_t)(before + __popcll(peers));
+        if (i < n) rank[i] = (int16_t)(g >= 0 ? before + r : -1);
+    }
+    __syncthreads();
+    for (int g = threadIdx.x; g < E; g += blockDim.x) {
+        int32_t run = 0;
+        for (int w = 0; w < waves; ++w) {
+            const int32_t v = hist[w * E + g];
+            hist[w * E + g] = (int16_t)run;
+            run += v;
+        }
+        hist[waves * E + g] = (int16_t)run;
+    }
+    __syncthreads();
+    for (int c = 0; c < K; ++c) {
+        const int i = wave * 64 * K + c * 64 + lane;
+        if (i < n && keys[i] >= 0) rank[i] = (int16_t)(rank[i] + hist[wave * E + keys[i]]);
+    }
+    __syncthreads();
+}
+
+// The fast form of the per-expert ranks, for tiles where no token holds an
+// expert twice: then a pick's rank is the number of the tile's tokens
+// before its own that hold the same expert. Each wave ORs its lanes' bits
+// into masks[wave * E + g] for every kept id g of its tokens (LDS atomics:
+// the result does not depend on their order); masks must be zeroed before
+// and a barrier must separate this from the queries.
+__device__ __forceinline__ void mark_expert_masks(const int32_t (&key)[kRankMaxK],
+                                                  unsigned long long* masks, int E) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < kRankMaxK; ++k)
+        if (key[k] >= 0) atomicOr(&masks[wave * E + key[k]], 1ull << lane);
+}
+
+// Rank of expert g at tile-local token tl (fast form): the tokens of the
+// waves before tl's that hold g, plus those below tl in its own wave. All
+// WAVES masks of g are read at once (their loads in flight together).
+template <int WAVES>
+__device__ __forceinline__ int32_t mask_rank(const unsigned long long* masks, int E, int tl,
+                                             int32_t g) {
+    const int w = tl >> 6;
+    const unsigned long long below = (1ull << (tl & 63)) - 1ull;
+    unsigned long long m[WAVES];
+#pragma unroll
+    for (int w2 = 0; w2 < WAVES; ++w2) m[w2] = masks[w2 * E + g];
+    int32_t r = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < WAVES; ++w2)
+        r += w2 < w ? __popcll(m[w2]) : (w2 == w ? __popcll(m[w2] & below) : 0);
+    return r;
+}
+
 // Largest s in [0, W) with pre[s] <= v, for an ascending prefix array
 // pre[0..W] (pre[0] = 0) and v < pre[W].
 __device__ __forceinline__ int find_source(const int32_t* pre, int W, int32_t v) {
@@ -200,10 +346,12 @@ inline int row_split(int64_t rows, int64_t max_vecs) {
     return (int)s;
 }
 
+// prank != nullptr: also the per-expert in-tile ranks of the kept picks
+// (prank [T * K]) and the tiles' counts per expert (ecnt_tile [tiles][E]).
 hipError_t launch_route_local(const int32_t* ids, int64_t T, int K, int E,
-                              int e_local, int W, int32_t* rank,
-                              int32_t* tile_cnt, uint32_t* err,
-                              hipStream_t stream);
+                              int e_local, int W, int slots, int32_t* rank,
+                              int32_t* tile_cnt, int32_t* prank, int32_t* ecnt_tile,
+                              int nbits, uint32_t* err, hipStream_t stream);
 
 hipError_t launch_column_scan(const int32_t* cnt, int ntiles, int nkeys,
                               int32_t* off, int32_t* total, int32_t clamp_max,
@@ -221,7 +369,7 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             const int32_t* tile_off, int32_t* send_cnt,
                             const PayloadSet& P, const QuantArgs* quant,
                             int32_t* send_eloc, float* send_w, int64_t meta_stride,
-                            uint32_t* err, hipStream_t stream);
+                            const RankArgs* ranks, uint32_t* err, hipStream_t stream);
 
 hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
                               const int32_t* recv_eloc, int64_t eloc_stride,
@@ -233,13 +381,17 @@ hipError_t launch_batch_local(const int32_t* recv_cnt, int64_t cnt_stride,
 // kBatchFuseTiles): offsets are summed from tile_cnt and block 0 writes
 // expert_num_tokens (clamped to clamp_max); otherwise tile_off holds the
 // offsets from column_scan.
+// recv_rank != nullptr: rows from the sources' per-expert ranks (same
+// layout and stride as recv_eloc) and counts (recv_ecnt, source s's
+// [e_local] at recv_ecnt + s * ecnt_stride); no receive scan.
 hipError_t launch_batch_copy(const int32_t* recv_cnt, int64_t cnt_stride,
                              const int32_t* recv_eloc, int64_t eloc_stride,
                              int W, int e_local, int slots, int64_t cap,
                              const int32_t* tile_off, const int32_t* tile_cnt,
-                             int fused_tiles, int32_t* expert_num_tokens,
-                             int32_t clamp_max, int32_t* recv_row,
-                             const PayloadSet& P, uint32_t* err,
+                             int fused_tiles, const int32_t* recv_rank,
+                             const int32_t* recv_ecnt, int64_t ecnt_stride,
+                             int32_t* expert_num_tokens, int32_t clamp_max,
+                             int32_t* recv_row, const PayloadSet& P, uint32_t* err,
                              hipStream_t stream);
 
 hipError_t launch_sanitize_ids(const int32_t* recv_cnt, int64_t cnt_stride,

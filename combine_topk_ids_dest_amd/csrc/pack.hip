@@ -312,14 +312,41 @@ __device__ __forceinline__ void load_first_pass(const PayloadSet& P, int64_t b, 
     }
 }
 
+// The rank of kept pick k (router order) of token t among the source's kept
+// picks of its expert g, from the routing kernel: its rank within its tile
+// plus the tile's offset for g (from column_scan, or the sum of the earlier
+// tiles' counts, loads issued 8 at a time); -1 for a pick that is not kept.
+__device__ __forceinline__ int32_t source_rank(const int32_t* __restrict__ ids, int64_t t,
+                                               int K, int k, int E, const RankArgs& R) {
+    // the id and the in-tile rank are loaded together
+    const int32_t g = ids[t * K + k];
+    const int32_t in_tile = R.prank[t * K + k];
+    if (in_tile < 0) return -1;
+    const int64_t tile = t / kRouteTile;
+    if (R.eoff_tile) return in_tile + R.eoff_tile[tile * E + g];
+    int32_t off = 0;
+    for (int64_t j0 = 0; j0 < tile; j0 += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = j0 + u < tile ? R.ecnt_tile[(j0 + u) * E + g] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) off += v[u];
+    }
+    return in_tile + off;
+}
+
 // Pick metadata of token t for destination d: the local id and weight of
 // each of its picks on d in router order, then -1 / +0.0 up to `slots`.
 // Ids and weights are read 8 picks at a time, all 16 loads in flight before
-// the first is used.
+// the first is used. RANKED: also each kept pick's rank among the source's
+// kept picks of its expert (-1 for unused columns), which the block put in
+// s_prank[k] (router order) while it planned the slots.
+template <bool RANKED>
 __device__ __forceinline__ uint32_t write_pick_meta(const int32_t* __restrict__ ids,
                                                     const float* __restrict__ wts, int64_t t,
                                                     int K, int E, int e_local, int d, int slots,
-                                                    int32_t* eloc, float* w) {
+                                                    int32_t* eloc, float* w, int32_t* rk,
+                                                    const int32_t* s_prank) {
     uint32_t bad = 0;
     int j = 0;
     for (int k0 = 0; k0 < K; k0 += 8) {
@@ -337,12 +364,14 @@ __device__ __forceinline__ uint32_t write_pick_meta(const int32_t* __restrict__ 
             if (j >= slots) { bad |= MOE_EP_ERR_PICKS; continue; }
             eloc[j] = id - d * e_local;
             w[j] = w8[u];
+            if (RANKED) rk[j] = s_prank[k0 + u];
             ++j;
         }
     }
     for (; j < slots; ++j) {
         eloc[j] = -1;
         w[j] = 0.0f;
+        if (RANKED) rk[j] = -1;
     }
     return bad;
 }
@@ -350,8 +379,15 @@ __device__ __forceinline__ uint32_t write_pick_meta(const int32_t* __restrict__ 
 // QMODE 0: plain rows; 1: payload 0 quantised to fp8; 2: to fp4.
 // PF (plain rows): the first pass of the leading row of the block's first
 // item is loaded before the routing and the slot planning, so its latency
-// overlaps them.
-template <int QMODE, bool PF>
+// overlaps them. RANKED: the send-side per-expert ranks (RankArgs) as well.
+// While wave 0 plans the slots, the token's kept picks get their ranks among
+// the source's kept picks of the same expert, into s_prank: with the routing
+// kernel wave 1 adds the tile offsets to its in-tile ranks; with the
+// kernel's own routing the block finds, for each pick, the kept picks of the
+// same expert in the tokens before (the kept ids of all T tokens are in
+// dynamic LDS; per-wave token masks when no token holds an expert twice,
+// else counts) and block 0 writes the per-expert counts.
+template <int QMODE, bool PF, bool RANKED>
 __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t T,
     int K, int E, int e_local, int W, int slots, int64_t cap, int nsplit,
@@ -359,7 +395,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ tile_cnt, const int32_t* __restrict__ tile_off,
     int32_t* __restrict__ send_cnt, const PayloadSet P, const QuantArgs Q,
     int32_t* __restrict__ send_eloc, float* __restrict__ send_w, int64_t meta_stride,
-    uint32_t* __restrict__ err) {
+    const RankArgs R, uint32_t* __restrict__ err) {
+    // RANKED with own routing: per-wave expert masks or per-expert counts,
+    // then the kept ids of all T tokens (see the prologue)
+    extern __shared__ int32_t rank_lds[];
+    __shared__ int32_t s_prank[kRankMaxK];
     __shared__ int32_t s_dest[MOE_EP_MAX_WORLD];
     __shared__ int32_t s_slot[MOE_EP_MAX_WORLD];
     __shared__ int s_n;
@@ -398,9 +438,92 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             for (int w = 0; w * 64 < T; ++w) c += __popcll(s_bits[w][tid]);
             send_cnt[tid] = c;
         }
+        if (RANKED) {
+            // one item per block: its token t
+            const int64_t t = (int64_t)blockIdx.x / nsplit;
+            constexpr int waves = kPackThreads / 64;
+            const bool mask_ok = E <= kRankMaskE;
+            // the masks [waves * E] (fast form) or the counts [E] (int32),
+            // then the kept ids of all T tokens [T * K] (int16)
+            unsigned long long* masks = reinterpret_cast<unsigned long long*>(rank_lds);
+            int32_t* hist = rank_lds;
+            int16_t* keys = reinterpret_cast<int16_t*>(rank_lds + (mask_ok ? 2 * waves * E : E));
+            int32_t key[kRankMaxK];
+#pragma unroll
+            for (int k = 0; k < kRankMaxK; ++k) key[k] = -1;
+            if (tid < T) {
+                kept_keys(ids + (int64_t)tid * K, K, E, e_local, slots, key);
+#pragma unroll
+                for (int k = 0; k < kRankMaxK; ++k)
+                    if (k < K) keys[tid * K + k] = (int16_t)key[k];
+            }
+            // (a barrier: every token's kept ids are in LDS after it)
+            const bool fast = mask_ok && !__syncthreads_or(has_repeated_key(key));
+            if (fast) {
+                for (int i = tid; i < waves * E; i += kPackThreads) masks[i] = 0;
+                __syncthreads();
+                mark_expert_masks(key, masks, E);
+                __syncthreads();
+                // the thread of token t ranks its picks (queries all in flight)
+                if (tid == t) {
+#pragma unroll
+                    for (int k = 0; k < kRankMaxK; ++k)
+                        if (k < K)
+                            s_prank[k] = key[k] >= 0 ? mask_rank<waves>(masks, E, (int)t, key[k]) : -1;
+                }
+                if (blockIdx.x == 0)
+                    for (int g = tid; g < E; g += kPackThreads) {
+                        int32_t c = 0;
+                        for (int w = 0; w < waves; ++w) c += __popcll(masks[w * E + g]);
+                        R.send_ecnt[g] = c;
+                    }
+            } else {
+                // any input: for each pick, the kept picks of the same expert
+                // in the tokens before t (and in t's earlier columns); sums
+                // over the tokens are order-free, so LDS atomics give the
+                // same counts every run
+                if (blockIdx.x == 0)
+                    for (int g = tid; g < E; g += kPackThreads) hist[g] = 0;
+                if (tid < K) s_prank[tid] = 0;
+                __syncthreads();
+                if (tid <= t && tid < T) {
+                    int32_t mine[kRankMaxK];
+#pragma unroll
+                    for (int k2 = 0; k2 < kRankMaxK; ++k2)
+                        mine[k2] = k2 < K ? keys[tid * K + k2] : -2;
+                    for (int k = 0; k < K; ++k) {
+                        const int32_t q = keys[t * K + k];
+                        const int upto = tid < t ? K : k;
+                        int32_t c = 0;
+#pragma unroll
+                        for (int k2 = 0; k2 < kRankMaxK; ++k2)
+                            c += (k2 < upto && mine[k2] == q) ? 1 : 0;
+                        if (q >= 0 && c) atomicAdd(&s_prank[k], c);
+                    }
+                }
+                if (blockIdx.x == 0 && tid < T)
+                    for (int k = 0; k < K; ++k) {
+                        const int32_t g = keys[tid * K + k];
+                        if (g >= 0) atomicAdd(&hist[g], 1);
+                    }
+                __syncthreads();
+                if (tid < K && keys[t * K + tid] < 0) s_prank[tid] = -1;
+                if (blockIdx.x == 0)
+                    for (int g = tid; g < E; g += kPackThreads) R.send_ecnt[g] = hist[g];
+            }
+        }
         // (a barrier here also keeps the compiler from carrying prologue
         // values into the token loop, which costs registers)
         __syncthreads();
+    } else if (RANKED && blockIdx.x == 0 && R.eoff_tile == nullptr) {
+        // per-expert totals from the tile counts (column_scan writes them
+        // when it computes the tile offsets)
+        const int64_t tiles = (T + kRouteTile - 1) / kRouteTile;
+        for (int g = tid; g < E; g += kPackThreads) {
+            int32_t c = 0;
+            for (int64_t j = 0; j < tiles; ++j) c += R.ecnt_tile[j * E + g];
+            R.send_ecnt[g] = c;
+        }
     }
 
     for (int64_t b = blockIdx.x; b < T * nsplit; b += gridDim.x) {
@@ -466,6 +589,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
                 s_slot[pos] = slot;
             }
             if (tid == 0) s_n = __popcll(act);
+        } else if (RANKED && !own_route && part == 0 && tid - 64 < K) {
+            // wave 1, lane k: pick k's rank, in parallel with wave 0's slots
+            s_prank[tid - 64] = source_rank(ids, t, K, tid - 64, E, R);
         }
         __syncthreads();
         const int n = s_n;
@@ -549,8 +675,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             uint32_t bad = 0;
             if (slot >= 0) {
                 const int64_t meta = (int64_t)tid * meta_stride + (int64_t)slot * slots;
-                bad = write_pick_meta(ids, wts, t, K, E, e_local, tid, slots,
-                                      send_eloc + meta, send_w + meta);
+                bad = write_pick_meta<RANKED>(
+                    ids, wts, t, K, E, e_local, tid, slots, send_eloc + meta, send_w + meta,
+                    RANKED ? R.send_rank + meta : nullptr, s_prank);
             }
             report(err, bad);
         }
@@ -565,7 +692,7 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
                             const int32_t* tile_off, int32_t* send_cnt,
                             const PayloadSet& P, const QuantArgs* quant,
                             int32_t* send_eloc, float* send_w, int64_t meta_stride,
-                            uint32_t* err, hipStream_t stream) {
+                            const RankArgs* ranks, uint32_t* err, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     int64_t max_vecs = quant ? quant->H / 8 : 0;
     for (int p = 0; p < P.n; ++p)
@@ -576,22 +703,34 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
     // the early first pass pays with its own routing (short kernels) and
     // for leading rows wider than 8 KiB; 8 KiB rows measured slower with it
     const bool pf = P.n > 0 && (rank == nullptr || P.row_bytes[0] / 16 > kPackPrefetchVecs);
-    if (quant && quant->mode == 2)
-        pack_copy_kernel<2, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
-            ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
-            tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, meta_stride, err);
-    else if (quant)
-        pack_copy_kernel<1, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
-            ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
-            tile_cnt, tile_off, send_cnt, P, *quant, send_eloc, send_w, meta_stride, err);
-    else if (pf)
-        pack_copy_kernel<0, true><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
-            ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
-            tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, meta_stride, err);
-    else
-        pack_copy_kernel<0, false><<<dim3((unsigned)grid), dim3(kPackThreads), 0, stream>>>(
-            ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot,
-            tile_cnt, tile_off, send_cnt, P, QuantArgs{}, send_eloc, send_w, meta_stride, err);
+    const bool ranked = ranks != nullptr && ranks->send_rank != nullptr;
+    const RankArgs R = ranked ? *ranks : RankArgs{};
+    // own routing with ranks: the masks (or the per-expert counts) and all
+    // tokens' kept ids
+    const size_t lds = ranked && rank == nullptr
+        ? (E <= kRankMaskE ? sizeof(uint64_t) * (size_t)(kPackThreads / 64) * E
+                           : sizeof(int32_t) * (size_t)E) +
+              sizeof(int16_t) * (size_t)T * K
+        : 0;
+    const QuantArgs Q = quant ? *quant : QuantArgs{};
+#define MOE_EP_PACK_LAUNCH(QM, PFV, RK)                                                   \
+    pack_copy_kernel<QM, PFV, RK><<<dim3((unsigned)grid), dim3(kPackThreads), lds, stream>>>( \
+        ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot, tile_cnt,   \
+        tile_off, send_cnt, P, Q, send_eloc, send_w, meta_stride, R, err)
+    if (quant && quant->mode == 2) {
+        if (ranked) MOE_EP_PACK_LAUNCH(2, false, true);
+        else MOE_EP_PACK_LAUNCH(2, false, false);
+    } else if (quant) {
+        if (ranked) MOE_EP_PACK_LAUNCH(1, false, true);
+        else MOE_EP_PACK_LAUNCH(1, false, false);
+    } else if (pf) {
+        if (ranked) MOE_EP_PACK_LAUNCH(0, true, true);
+        else MOE_EP_PACK_LAUNCH(0, true, false);
+    } else {
+        if (ranked) MOE_EP_PACK_LAUNCH(0, false, true);
+        else MOE_EP_PACK_LAUNCH(0, false, false);
+    }
+#undef MOE_EP_PACK_LAUNCH
     return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@ Device layout (all dense, rank-major):
   send[p]         [W_src, W_dst, cap, row_p]
   send_cnt        [W_src, W_dst]           int32
   send_eloc/_w    [W_src, W_dst, cap, slots]
+  send_rank       [W_src, W_dst, cap, slots] int32 (ranked form only)
+  send_ecnt       [W_src, W_dst, e_local] int32 (ranked form only)
   token_slot      [W_src, T, W_dst]        int32 (unpack context)
   b[p]            [e_local, W*cap, row_p]  one buffer per lane, reused by the
                                            destinations of that lane
@@ -56,7 +58,7 @@ class LogicalEP:
                  row_bytes: Sequence[int], combine_dtype=torch.bfloat16,
                  device="cuda", fill: Optional[int] = None,
                  quant_group: Optional[int] = None, quant_fp4: bool = False,
-                 lanes: int = 1, contiguous: bool = True):
+                 lanes: int = 1, contiguous: bool = True, ranked: bool = False):
         """row_bytes: bytes per row of each source payload (payload 0 is the
         bf16 hidden row that the combine returns). fill: byte to pre-fill
         every buffer with (e.g. 0xFF, NaN in bf16/fp32) so unwritten tails
@@ -69,7 +71,11 @@ class LogicalEP:
         workspace and b buffers (see the module docstring). contiguous:
         buffers of at least CONTIGUOUS_MIN_BYTES are physically contiguous
         allocations where the device grants them (devmem), else come from
-        torch's allocator; self.contiguous_bytes counts the granted ones."""
+        torch's allocator; self.contiguous_bytes counts the granted ones.
+        ranked: the packs also write the per-expert ranks and counts
+        (send_rank, send_ecnt) and the receive side is
+        moe_ep_expert_batch_ranked (no receive scan); batch_plan and
+        batch_copy keep the scanned form."""
         if lanes < 1 or lanes > W:
             raise ValueError("lanes must be in [1, W]")
         self.lanes = lanes
@@ -119,6 +125,9 @@ class LogicalEP:
         self.send_cnt = alloc((W_, W_), torch.int32)
         self.send_eloc = alloc((W_, W_, cap, sl), torch.int32)
         self.send_w = alloc((W_, W_, cap, sl), torch.float32)
+        self.ranked = ranked
+        self.send_rank = alloc((W_, W_, cap, sl), torch.int32) if ranked else None
+        self.send_ecnt = alloc((W_, W_, el), torch.int32) if ranked else None
         self.token_slot = alloc((W_, T, W_), torch.int32)
         self.b_lanes = [[alloc((el, self.expert_cap, rb), torch.uint8)
                          for rb in self.send_row_bytes] for _ in range(lanes)]
@@ -166,13 +175,14 @@ class LogicalEP:
         return call
 
     def _prep_pack(self, s: int):
+        ranks = ((self.send_rank[s], self.send_ecnt[s]) if self.ranked else (None, None))
         if self.quant_fp4:
             return B.prepare_dispatch_pack_fp4(
                 self.ids[s], self.wts[s], self.E, self.W, self.cap,
                 self.src[0][s].view(torch.bfloat16), self.send[0][s], self.send[1][s],
                 [(self.src[p][s], self.send[p + 1][s]) for p in range(1, len(self.src))],
                 self.send_cnt[s], self.send_eloc[s], self.send_w[s],
-                self.token_slot[s], self.err, self.workspaces[s % self.lanes])
+                self.token_slot[s], self.err, self.workspaces[s % self.lanes], *ranks)
         if self.quant_group is not None:
             G = B.scale_pitch(self.H, self.quant_group)
             return B.prepare_dispatch_pack_fp8(
@@ -181,14 +191,21 @@ class LogicalEP:
                 self.send[0][s], self.send[1][s].view(torch.float32).view(self.W, self.cap, G),
                 [(self.src[p][s], self.send[p + 1][s]) for p in range(1, len(self.src))],
                 self.send_cnt[s], self.send_eloc[s], self.send_w[s],
-                self.token_slot[s], self.err, self.workspaces[s % self.lanes])
+                self.token_slot[s], self.err, self.workspaces[s % self.lanes], *ranks)
         return B.prepare_dispatch_pack(
             self.ids[s], self.wts[s], self.E, self.W, self.cap,
             [(self.src[p][s], self.send[p][s]) for p in range(len(self.src))],
             self.send_cnt[s], self.send_eloc[s], self.send_w[s],
-            self.token_slot[s], self.err, self.workspaces[s % self.lanes])
+            self.token_slot[s], self.err, self.workspaces[s % self.lanes], *ranks)
 
     def _prep_batch(self, r: int):
+        if self.ranked:
+            return B.prepare_expert_batch_ranked(
+                self.send_cnt[:, r], self.send_eloc[:, r], self.send_rank[:, r],
+                self.send_ecnt[:, r], self.W, self.e_local, self.K, self.cap,
+                [(self.send[p][:, r], self.b_lanes[r % self.lanes][p])
+                 for p in range(len(self.send))],
+                self.expert_num_tokens[r], self.recv_row[r], self.err)
         return B.prepare_expert_batch(
             self.send_cnt[:, r], self.send_eloc[:, r], self.W, self.e_local,
             self.K, self.cap,

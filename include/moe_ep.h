@@ -113,9 +113,10 @@ MOE_EP_API int moe_ep_capacities(int32_t K, int32_t E, int32_t W, int64_t max_nu
                       int64_t* cap, int32_t* slots, int64_t* expert_cap);
 
 /*
- * Bytes of workspace that moe_ep_dispatch_pack (any T <= max_num_tokens)
- * and moe_ep_expert_batch need for these sizes; one buffer of this size
- * serves both calls when they are ordered on one stream. Each region is
+ * Bytes of workspace that moe_ep_dispatch_pack (any T <= max_num_tokens,
+ * with or without the per-expert ranks) and moe_ep_expert_batch need for
+ * these sizes; one buffer of this size serves both calls when they are
+ * ordered on one stream. Each region is
  * padded to 128 bytes, as the FlashInfer module pads its workspace regions
  * (moe_a2a_get_workspace_size_per_rank). Host only.
  */
@@ -147,6 +148,18 @@ MOE_EP_API const char* moe_ep_status_string(int status);
  *   meta_rank_stride  elements between destination blocks of send_eloc and
  *                 send_w (>= cap * slots; EINVAL otherwise). Elements
  *                 between blocks are not written.
+ *   send_rank     int32, nullable, same layout and stride as send_eloc:
+ *                 the rank of each used pick column among this source's
+ *                 used columns of the same expert on that destination, in
+ *                 (slot, column) order; -1 for an unused column. The
+ *                 receive side numbers an expert's rows in (source, slot,
+ *                 column) order, and within one source that is this order,
+ *                 so a row is the counts of the sources before plus the
+ *                 rank (moe_ep_expert_batch_ranked).
+ *   send_ecnt     int32 [W, e_local], nullable, dense: used pick columns
+ *                 per (destination, local expert); every entry is written.
+ *                 send_rank and send_ecnt are given together or not at all,
+ *                 and need K <= 16 and E <= 4096 (EINVAL otherwise).
  *   token_slot    int32 [T, W] out: slot of token t at destination d, -1
  *                 if none. Context for moe_ep_combine_unpack; keep it.
  *   err_flags     nullable; bits MOE_EP_ERR_ID_RANGE, MOE_EP_ERR_PICKS.
@@ -157,9 +170,9 @@ MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_w
                          int64_t max_num_tokens,
                          const moe_ep_payload* payloads, int32_t n_payloads,
                          int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                         int64_t meta_rank_stride, int32_t* token_slot,
-                         uint32_t* err_flags, void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         int64_t meta_rank_stride, int32_t* send_rank, int32_t* send_ecnt,
+                         int32_t* token_slot, uint32_t* err_flags, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * moe_ep_dispatch_pack for callers that cannot allocate: code under HIP
@@ -175,6 +188,8 @@ MOE_EP_API int moe_ep_dispatch_pack(const int32_t* topk_ids, const float* topk_w
  *     2 * round_up(ceil(T / 256) * W * 4, 128) + round_up(T * W * 4, 128)
  *     bytes (T <= 256 needs none): T * W up to about 2.08 million (token,
  *     destination) pairs, e.g. T = 65536 at W = 16 or T = 16384 at W = 64.
+ *     With send_rank and send_ecnt another round_up(T * K * 4, 128) +
+ *     2 * round_up(ceil(T / 256) * E * 4, 128) bytes.
  *   - The stream must belong to the current device (EINVAL otherwise). The
  *     first call on a device looks the array's address up (no allocation);
  *     make it outside graph capture.
@@ -192,7 +207,8 @@ MOE_EP_API int moe_ep_dispatch_pack_noalloc(const int32_t* topk_ids,
                                             const moe_ep_payload* payloads,
                                             int32_t n_payloads, int32_t* send_cnt,
                                             int32_t* send_eloc, float* send_w,
-                                            int64_t meta_rank_stride, int32_t* token_slot,
+                                            int64_t meta_rank_stride, int32_t* send_rank,
+                                            int32_t* send_ecnt, int32_t* token_slot,
                                             uint32_t* err_flags, void* stream);
 
 /*
@@ -233,7 +249,8 @@ MOE_EP_API int moe_ep_dispatch_pack_fp8(const int32_t* topk_ids, const float* to
                                         float* send_scale, int64_t scale_rank_stride,
                                         const moe_ep_payload* payloads, int32_t n_payloads,
                                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                                        int64_t meta_rank_stride, int32_t* token_slot,
+                                        int64_t meta_rank_stride, int32_t* send_rank,
+                                        int32_t* send_ecnt, int32_t* token_slot,
                                         uint32_t* err_flags, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
@@ -274,7 +291,8 @@ MOE_EP_API int moe_ep_dispatch_pack_fp4(const int32_t* topk_ids, const float* to
                                         void* send_scale, int64_t scale_rank_stride,
                                         const moe_ep_payload* payloads, int32_t n_payloads,
                                         int32_t* send_cnt, int32_t* send_eloc, float* send_w,
-                                        int64_t meta_rank_stride, int32_t* token_slot,
+                                        int64_t meta_rank_stride, int32_t* send_rank,
+                                        int32_t* send_ecnt, int32_t* token_slot,
                                         uint32_t* err_flags, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
@@ -306,6 +324,37 @@ MOE_EP_API int moe_ep_expert_batch(const int32_t* recv_cnt, int64_t cnt_rank_str
                         int32_t* expert_num_tokens, int32_t* recv_row,
                         uint32_t* err_flags, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * moe_ep_expert_batch from the sources' per-expert ranks (send_rank and
+ * send_ecnt of moe_ep_dispatch_pack, exchanged with the local ids): the row
+ * of a valid pick (s, slot, j) of local expert e is
+ *   sum over s' < s of recv_ecnt[s', e]  +  recv_rank[s, slot, j],
+ * which with metadata from moe_ep_dispatch_pack is the row
+ * moe_ep_expert_batch gives (the vLLM alltoall_batched page's (source,
+ * slot, column) order); expert_num_tokens[e] = the sum over all sources,
+ * clamped to expert_cap. No receive scan runs and no workspace is needed:
+ * one kernel moves the rows.
+ *
+ *   recv_rank     int32, same layout and stride as recv_eloc.
+ *   recv_ecnt     int32, source s's [e_local] counts at
+ *                 recv_ecnt + s * ecnt_rank_stride (elements, >= e_local).
+ *   W * e_local <= 4096 (EINVAL otherwise).
+ * Everything else as moe_ep_expert_batch. Data errors: a received local id
+ * >= e_local is dropped (MOE_EP_ERR_ELOC); a valid pick whose rank is
+ * negative or whose row reaches expert_cap is dropped (MOE_EP_ERR_ROWCAP);
+ * counts are clamped to [0, expert_cap]. Rows follow the ranks as received:
+ * metadata that did not come from moe_ep_dispatch_pack may give two picks
+ * the same row.
+ */
+MOE_EP_API int moe_ep_expert_batch_ranked(const int32_t* recv_cnt, int64_t cnt_rank_stride,
+                                          const int32_t* recv_eloc, const int32_t* recv_rank,
+                                          int64_t eloc_rank_stride, const int32_t* recv_ecnt,
+                                          int64_t ecnt_rank_stride, int32_t W,
+                                          int32_t e_local, int32_t K, int64_t max_num_tokens,
+                                          const moe_ep_payload* payloads, int32_t n_payloads,
+                                          int32_t* expert_num_tokens, int32_t* recv_row,
+                                          uint32_t* err_flags, void* stream);
 
 /*
  * The two halves of moe_ep_expert_batch, for callers that overlap them with

@@ -84,11 +84,31 @@ def assert_bytes_equal(got: np.ndarray, exp: np.ndarray, what: str):
     raise AssertionError(f"{what}: {len(bad)} bytes differ; first {shown}")
 
 
+def check_pick_ranks(ep, packs, w):
+    """The packs' per-expert ranks and counts (ranked form) against the
+    oracle's, computed from the oracle's own pack outputs: valid slots and
+    every count bit-exact, slots past the count untouched."""
+    g_rank = ep.send_rank.cpu().numpy()
+    g_ecnt = ep.send_ecnt.cpu().numpy()
+    for s in range(w.W):
+        exp = oracle.pick_ranks(packs[s]["send_cnt"], packs[s]["send_eloc"], w.e_local)
+        assert np.array_equal(g_ecnt[s], exp["send_ecnt"]), f"send_ecnt src {s}"
+        for d in range(w.W):
+            c = int(packs[s]["send_cnt"][d])
+            assert np.array_equal(g_rank[s, d, :c], exp["send_rank"][d, :c]), \
+                f"send_rank {s}->{d}"
+            assert (g_rank[s, d, c:].view(np.uint32) == 0xFFFFFFFF).all(), \
+                f"send_rank tail {s}->{d} written"
+
+
 def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
                     srcs=None, pls=None, corrupt_cnt=None, split_batch=False,
-                    fp8_group=None, fused_local=False, fp4=False):
+                    fp8_group=None, fused_local=False, fp4=False, ranked=False):
     """Whole path on W logical ranks, every output compared element by
-    element with the oracle. Returns (ep, oracle result)."""
+    element with the oracle. ranked: the packs also write the per-expert
+    ranks (checked against the oracle's) and the receive side is the
+    ranked batch (its rows checked against the oracle's scanned batch).
+    Returns (ep, oracle result)."""
     if srcs is None:
         srcs, pls = inputs(w, salt, f32_hidden=f32)
     ids_l = [s[0] for s in srcs]
@@ -145,12 +165,14 @@ def run_full_parity(w: wl.Workload, salt: int = 0, f32: bool = False,
     row_bytes = [p.shape[1] * p.itemsize for p in pls[0]]
     dt = torch.float32 if f32 else torch.bfloat16
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, dt, "cuda",
-                   fill=SENTINEL, quant_group=fp8_group, quant_fp4=fp4)
+                   fill=SENTINEL, quant_group=fp8_group, quant_fp4=fp4, ranked=ranked)
     for s in range(w.W):
         ep.set_source(s, ids_l[s], wts_l[s], pls[s])
     for s in range(w.W):
         ep.pack(s)
     torch.cuda.synchronize()
+    if ranked:
+        check_pick_ranks(ep, packs, w)
     g_cnt = ep.send_cnt.cpu().numpy()
     g_eloc = ep.send_eloc.cpu().numpy()
     g_w = ep.send_w.cpu().numpy()
@@ -260,19 +282,21 @@ def column_windows(nbytes: int, width: int = 64):
     return np.array(sorted(set(out)), dtype=np.int64)
 
 
-def run_fullsize(w: wl.Workload, seed: int = 0, fp8_group=None, fp4=False):
+def run_fullsize(w: wl.Workload, seed: int = 0, fp8_group=None, fp4=False, ranked=False):
     """Whole path at full size. Every integer output and every valid payload
     byte is compared; the combine is compared on column windows that the
     oracle computes exactly (the reduction is independent per column). With
     fp8_group the pack quantises payload 0; the oracle quantises the same
-    rows and its codes and scales are the expected rows."""
+    rows and its codes and scales are the expected rows. ranked: the packs'
+    per-expert ranks are compared too and the receive side is the ranked
+    batch."""
     dev = torch.device("cuda")
     say(f"[fullsize] {w.name}: generating inputs")
     srcs = [wl.routing(w, s, seed) for s in range(w.W)]
     pls = [wl.payloads(w, s, seed, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
     row_bytes = [p.shape[1] for p in pls[0]]
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, row_bytes, torch.bfloat16, dev,
-                   fill=SENTINEL, quant_group=fp8_group, quant_fp4=fp4)
+                   fill=SENTINEL, quant_group=fp8_group, quant_fp4=fp4, ranked=ranked)
     n_pl = len(ep.send)
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
@@ -332,6 +356,8 @@ def run_fullsize(w: wl.Workload, seed: int = 0, fp8_group=None, fp4=False):
             assert np.array_equal(g_eloc[s, d, :c], send_eloc[s, d, :c]), f"eloc {s}->{d}"
             assert np.array_equal(g_w[s, d, :c].view(np.uint32),
                                   send_w[s, d, :c].view(np.uint32)), f"w {s}->{d}"
+    if ranked:
+        check_pick_ranks(ep, packs, w)
     # every valid payload byte: send[s, d, slot] is the source row of the
     # token the oracle put in that slot
     tok_of = {}
@@ -423,7 +449,8 @@ STEP_OUTPUTS = ("send_cnt", "token_slot", "send_eloc", "send_w", "expert_num_tok
 def snapshot_step(ep):
     """Device copies of every output of a step, and the valid rows of the
     last destination's expert batch."""
-    snap = {n: getattr(ep, n).clone() for n in STEP_OUTPUTS}
+    names = STEP_OUTPUTS + (("send_rank", "send_ecnt") if ep.ranked else ())
+    snap = {n: getattr(ep, n).clone() for n in names}
     snap["send"] = [x.clone() for x in ep.send]
     r = ep.W - 1
     ent = ep.expert_num_tokens[r].tolist()
@@ -432,16 +459,17 @@ def snapshot_step(ep):
     return snap
 
 
-def check_lanes_step(w: wl.Workload, ref, lanes: int, seed: int = 0):
+def check_lanes_step(w: wl.Workload, ref, lanes: int, seed: int = 0, ranked: bool = False):
     """The whole step as bench.py times it, with the ranks over `lanes` HIP
     streams, on the inputs of run_fullsize: every output byte equals the
     one-stream outputs in `ref` (snapshot_step of the path that run_fullsize
     checked against the oracle)."""
-    say(f"[fullsize] {w.name}: whole step over {lanes} lanes")
+    say(f"[fullsize] {w.name}: whole step over {lanes} lanes (ranked={ranked})")
     srcs = [wl.routing(w, s, seed) for s in range(w.W)]
     pls = [wl.payloads(w, s, seed, ids=srcs[s][0], wts=srcs[s][1]) for s in range(w.W)]
     ep = LogicalEP(w.T, w.H, w.E, w.K, w.W, w.cap, [p.shape[1] for p in pls[0]],
-                   torch.bfloat16, torch.device("cuda"), fill=SENTINEL, lanes=lanes)
+                   torch.bfloat16, torch.device("cuda"), fill=SENTINEL, lanes=lanes,
+                   ranked=ranked)
     for s in range(w.W):
         ep.set_source(s, srcs[s][0], srcs[s][1], pls[s])
     wl.expert_outputs_device(ep.Y, seed=2000 + w.wid)
@@ -450,7 +478,7 @@ def check_lanes_step(w: wl.Workload, ref, lanes: int, seed: int = 0):
     ep.step(streams=streams)
     torch.cuda.synchronize()
     got = snapshot_step(ep)
-    for n in STEP_OUTPUTS:
+    for n in STEP_OUTPUTS + (("send_rank", "send_ecnt") if ranked else ()):
         assert torch.equal(got[n].view(torch.uint8), ref[n].view(torch.uint8)), f"lanes: {n}"
     for p, (a, b) in enumerate(zip(got["send"], ref["send"])):
         assert torch.equal(a, b), f"lanes: send payload {p}"

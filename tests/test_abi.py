@@ -72,9 +72,11 @@ def test_capacities_and_workspace():
     ws = B.moe_ep_workspace_bytes(4096, 8, 256, 8, 4096)
     assert ws > 0 and ws % 128 == 0
     # send side: 16 token tiles x 8 ranks (counts and offsets, each padded to
-    # 128 B) + in-tile ranks [4096, 8]; receive side: 8*4096*8/1024 tiles x
-    # 32 experts x 4 B x 2. The larger wins.
-    send = 2 * 512 + 4096 * 8 * 4
+    # 128 B) + in-tile ranks [4096, 8], and for the per-expert ranks the
+    # picks' in-tile ranks [4096 * 8] and 16 tiles x 256 experts (counts and
+    # offsets); receive side: 8*4096*8/1024 tiles x 32 experts x 4 B x 2.
+    # The larger wins.
+    send = 2 * 512 + 4096 * 8 * 4 + 4096 * 8 * 4 + 2 * 16 * 256 * 4
     recv = 256 * 32 * 4 * 2
     assert ws == max(send, recv) == send
     with pytest.raises(B.MoeEpError) as e:
@@ -116,7 +118,7 @@ def _payloads(*descs):
 
 
 def _pack(T=16, K=2, E=8, W=4, cap=16, pl=None, npl=1, ws_bytes=1 << 20,
-          ws=FAKE, ids=FAKE, meta=None):
+          ws=FAKE, ids=FAKE, meta=None, rank=None, ecnt=None):
     lib = B.load()
     if pl is None:
         pl = _payloads((FAKE, 512, FAKE, cap * 512, 512))
@@ -124,7 +126,7 @@ def _pack(T=16, K=2, E=8, W=4, cap=16, pl=None, npl=1, ws_bytes=1 << 20,
         meta = cap * min(K, E // W) if W > 0 and E % W == 0 else 0
     return lib.moe_ep_dispatch_pack(ids, FAKE, T, K, E, W, cap,
                                     ctypes.addressof(pl), npl, FAKE, FAKE,
-                                    FAKE, meta, FAKE, None, ws, ws_bytes, None)
+                                    FAKE, meta, rank, ecnt, FAKE, None, ws, ws_bytes, None)
 
 
 def test_dispatch_pack_argument_checks():
@@ -152,16 +154,29 @@ def test_dispatch_pack_argument_checks():
     assert _pack(meta=16 * 2 - 1) == B.EINVAL
     assert _pack(meta=-1) == B.EINVAL
     assert _pack(meta=(1 << 63) // 3) == B.EINVAL
+    # per-expert ranks: both outputs or neither, K <= 16 and E <= 4096; the
+    # workspace must hold the ranks' tables too
+    assert _pack(rank=FAKE) == B.EINVAL
+    assert _pack(ecnt=FAKE) == B.EINVAL
+    assert _pack(rank=FAKE, ecnt=FAKE, K=17, E=4 * 32) == B.EINVAL
+    assert _pack(rank=FAKE, ecnt=FAKE, K=2, E=8 * 520, W=8) == B.EINVAL
+    T, W = 600, 4
+    r128 = lambda x: (x + 127) // 128 * 128
+    plain = 2 * r128(3 * W * 4) + r128(T * W * 4)
+    ranked = plain + r128(T * 2 * 4) + 2 * r128(3 * 8 * 4)
+    assert _pack(T=T, cap=T, ws_bytes=plain, rank=FAKE, ecnt=FAKE) == B.EWORKSPACE
+    assert _pack(T=T, cap=T, ws_bytes=ranked - 1, rank=FAKE, ecnt=FAKE) == B.EWORKSPACE
+    assert B.moe_ep_workspace_bytes(T, 2, 8, W, T) == ranked
 
 
-def _pack_noalloc(T=16, K=2, E=8, W=4, cap=16, npl=1, meta=None):
+def _pack_noalloc(T=16, K=2, E=8, W=4, cap=16, npl=1, meta=None, rank=None, ecnt=None):
     lib = B.load()
     pl = _payloads((FAKE, 512, FAKE, cap * 512, 512))
     if meta is None:
         meta = cap * min(K, E // W) if W > 0 and E % W == 0 else 0
     return lib.moe_ep_dispatch_pack_noalloc(FAKE, FAKE, T, K, E, W, cap,
                                             ctypes.addressof(pl), npl, FAKE, FAKE,
-                                            FAKE, meta, FAKE, None, None)
+                                            FAKE, meta, rank, ecnt, FAKE, None, None)
 
 
 def _send_scratch(T, W):
@@ -186,6 +201,25 @@ def test_dispatch_pack_noalloc_argument_checks():
     assert _pack(T=T, K=2, E=64, W=W, cap=T, ws_bytes=8) == B.EWORKSPACE
 
 
+def test_expert_batch_ranked_argument_checks():
+    lib = B.load()
+
+    def call(W=4, el=2, K=2, cap=16, ecnt_stride=None, rank=FAKE, eloc_stride=None):
+        slots = min(K, el)
+        pl = _payloads((FAKE, cap * 512, FAKE, W * cap * 512, 512))
+        es = cap * slots if eloc_stride is None else eloc_stride
+        cs = el if ecnt_stride is None else ecnt_stride
+        return lib.moe_ep_expert_batch_ranked(FAKE, 1, FAKE, rank, es, FAKE, cs, W, el, K,
+                                              cap, ctypes.addressof(pl), 1, FAKE, FAKE,
+                                              None, None)
+
+    assert call(rank=None) == B.EINVAL
+    assert call(ecnt_stride=1) == B.EINVAL             # rows of e_local counts
+    assert call(eloc_stride=31) == B.EINVAL
+    assert call(W=8, el=513) == B.EINVAL               # W * e_local > 4096
+    assert call(W=0) == B.EINVAL
+
+
 def test_dispatch_pack_fp4_argument_checks():
     lib = B.load()
 
@@ -197,8 +231,8 @@ def test_dispatch_pack_fp4_argument_checks():
         pl = _payloads()
         return lib.moe_ep_dispatch_pack_fp4(FAKE, FAKE, 16, 2, 8, 4, cap, FAKE, hs, H,
                                             q, qs, sc, ss, ctypes.addressof(pl), 0,
-                                            FAKE, FAKE, FAKE, cap * 2, FAKE, None, FAKE,
-                                            1 << 20, None)
+                                            FAKE, FAKE, FAKE, cap * 2, None, None, FAKE,
+                                            None, FAKE, 1 << 20, None)
 
     assert B.fp4_scale_pitch(7168) == 448 and B.fp4_scale_pitch(544) == 48
     assert call(H=0) == B.EINVAL

@@ -33,6 +33,24 @@ def test_fullsize(wid):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_fullsize_ranked(wid):
+    """The packs with per-expert ranks and the ranked receive side at full
+    size (ranks and counts against the oracle's, rows and every batched byte
+    as in test_fullsize), and the whole step over the lanes bench.py uses."""
+    w = wl.WORKLOADS[wid]
+    say(f"[fullsize ranked] start {w.name}")
+    ep = run_fullsize(w, ranked=True)
+    lanes = bench.auto_lanes(w, ep.row_bytes)
+    if lanes > 1:
+        ref = snapshot_step(ep)
+        del ep
+        gc.collect()
+        torch.cuda.empty_cache()
+        check_lanes_step(w, ref, lanes, ranked=True)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("wid", [2, 5])
 def test_fullsize_fp8_pack(wid):
     """Quantize-on-pack at the DeepSeek-V3 and multi-payload shapes."""

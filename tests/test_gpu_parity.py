@@ -60,6 +60,60 @@ def test_parity(name):
     run_full_parity(w, salt=3)
 
 
+# the per-expert ranks need K <= 16 and E <= 4096 (every case but max_slots)
+RANKED_CASES = sorted(n for n, w in CASES.items() if w.K <= 16 and w.E <= 4096)
+
+
+@pytest.mark.parametrize("name", RANKED_CASES)
+def test_parity_ranked(name):
+    """Packs with the per-expert ranks (moe_ep_dispatch_pack's send_rank and
+    send_ecnt, against the oracle's) and the receive side from them
+    (moe_ep_expert_batch_ranked): every output as in test_parity."""
+    w = CASES[name]
+    say(f"[parity ranked] {name}: T={w.T} H={w.H} E={w.E} K={w.K} W={w.W} cap={w.cap}")
+    run_full_parity(w, salt=3, ranked=True)
+
+
+def test_parity_ranked_bad_ids_duplicates_and_corrupt_count():
+    """Dropped ids, duplicates past the pick columns and a corrupted
+    received count, through the ranked pack and batch: bit-exact with the
+    oracle, flags included."""
+    w = W1.scaled(W=4, E=8, K=3, T=300, cap=300, H=64, pad_frac=0.0)
+    srcs, pls = [], []
+    for s in range(w.W):
+        ids, wts = wl.routing(w, s, 7)
+        ids = ids.copy()
+        ids[3, 1] = 8 + s            # out of range
+        ids[5] = [2, 2, 2]           # duplicates: e_local 2 -> slots 2
+        ids[260] = [3, 3, 1]         # in the second routing tile
+        ids[9, 0] = -5               # any negative id is padding
+        srcs.append((ids, wts))
+        pls.append(wl.payloads(w, s, 7))
+    say("[parity ranked] bad ids")
+    run_full_parity(w, srcs=srcs, pls=pls, ranked=True)
+    say("[parity ranked] corrupt count")
+    run_full_parity(W1.scaled(W=4, E=8, K=2, T=50, cap=50, H=64), salt=9,
+                    corrupt_cnt=(1, 2, 77), ranked=True)
+
+
+@pytest.mark.parametrize("name", ["dsv3_small", "decode", "many_route_tiles"])
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_parity_ranked_quantised(name, fmt):
+    w = CASES[name]
+    say(f"[parity ranked {fmt}] {name}")
+    if fmt == "fp8":
+        run_full_parity(w.scaled(H=1024) if w.H % 128 else w, salt=21, fp8_group=128,
+                        ranked=True)
+    else:
+        run_full_parity(w.scaled(H=1024) if w.H % 32 else w, salt=37, fp4=True, ranked=True)
+
+
+@pytest.mark.parametrize("name", ["dsv3_small", "decode", "w64"])
+def test_parity_ranked_fused_local(name):
+    say(f"[parity ranked fused local] {name}")
+    run_full_parity(CASES[name], salt=23, fused_local=True, ranked=True)
+
+
 @pytest.mark.parametrize("name", ["tiny", "dsv3_small", "mixtral_small", "wide_row",
                                   "whole_row_unpack"])
 def test_parity_fp32_combine(name):

@@ -29,7 +29,7 @@ def _buffers(w, slots, dev):
         err=torch.zeros(1, dtype=torch.int32, device=dev))
 
 
-def _one(w, salt):
+def _one(w, salt, ranked=False):
     dev = torch.device("cuda")
     slots = min(w.K, w.e_local)
     ids, wts = wl.routing(w, 0, salt)
@@ -39,13 +39,17 @@ def _one(w, salt):
     src = torch.from_numpy(hidden.view(np.uint8).reshape(w.T, 2 * w.H)).to(dev)
     a = _buffers(w, slots, dev)
     b = _buffers(w, slots, dev)
+    for x in (a, b):
+        x["send_rank"] = torch.full((w.W, w.cap, slots), -7, dtype=torch.int32, device=dev)
+        x["send_ecnt"] = torch.full((w.W, w.e_local), -7, dtype=torch.int32, device=dev)
+    rk = lambda x: dict(send_rank=x["send_rank"], send_ecnt=x["send_ecnt"]) if ranked else {}
     ws = torch.empty(max(B.moe_ep_workspace_bytes(w.T, w.K, w.E, w.W, w.cap), 16),
                      dtype=torch.uint8, device=dev)
     B.moe_ep_dispatch_pack(d_ids, d_wts, w.E, w.W, w.cap, [(src, a["send"])], a["send_cnt"],
-                           a["send_eloc"], a["send_w"], a["token_slot"], a["err"], ws)
+                           a["send_eloc"], a["send_w"], a["token_slot"], a["err"], ws, **rk(a))
     B.moe_ep_dispatch_pack_noalloc(d_ids, d_wts, w.E, w.W, w.cap, [(src, b["send"])],
                                    b["send_cnt"], b["send_eloc"], b["send_w"],
-                                   b["token_slot"], b["err"])
+                                   b["token_slot"], b["err"], **rk(b))
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), k
@@ -60,6 +64,13 @@ def _one(w, salt):
         assert np.array_equal(ge[d, :c], exp["send_eloc"][d, :c])
         assert np.array_equal(gs[d, :c], exp["send"][0][d, :c])
     assert int(b["err"].item()) == exp["err"]
+    if ranked:
+        er = oracle.pick_ranks(exp["send_cnt"], exp["send_eloc"], w.e_local)
+        assert np.array_equal(b["send_ecnt"].cpu().numpy(), er["send_ecnt"])
+        gr = b["send_rank"].cpu().numpy()
+        for d in range(w.W):
+            c = int(exp["send_cnt"][d])
+            assert np.array_equal(gr[d, :c], er["send_rank"][d, :c])
 
 
 def test_noalloc_pack_matches_the_pack_on_successive_calls():
@@ -71,3 +82,7 @@ def test_noalloc_pack_matches_the_pack_on_successive_calls():
     for i, w in enumerate((first, second, third, decode)):
         say(f"[noalloc] call {i}: T={w.T} W={w.W} E={w.E} K={w.K} H={w.H}")
         _one(w, 60 + i)
+    # with the per-expert ranks (their tables in the scratch as well)
+    for i, w in enumerate((second, first, third, decode)):
+        say(f"[noalloc ranked] call {i}: T={w.T} W={w.W} E={w.E} K={w.K} H={w.H}")
+        _one(w, 70 + i, ranked=True)
