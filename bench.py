@@ -83,8 +83,12 @@ def log(*a):
 # The source file of each kernel; with the shared header and the build
 # flags it determines the kernel's code.
 KERNEL_SOURCE = {
+    "route_local_kernel": "route.hip",
+    "column_scan_kernel": "route.hip",
     "pack_copy_kernel": "pack.hip",
+    "batch_local_kernel": "batch.hip",
     "batch_copy_kernel": "batch.hip",
+    "sanitize_ids_kernel": "batch.hip",
     "combine_reduce_kernel": "combine.hip",
     "combine_unpack_kernel": "combine.hip",
     "combine_unpack_fused_kernel": "combine.hip",
@@ -122,6 +126,21 @@ def read_traffic(kernel: str, workload: str):
         return float(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def mode_suffix(args) -> str:
+    """The part of a counter summary's name that tells the dispatch format
+    and the receive form: the counters of one form do not describe another."""
+    s = ""
+    if args.fp8_group:
+        s += f"_fp8_g{args.fp8_group}"
+    if args.fp4:
+        s += "_fp4"
+    if args.fused_local:
+        s += "_fused_local"
+    if args.ranked:
+        s += "_ranked"
+    return s
 
 
 def byte_model(w, row_bytes, slots, send_cnt, ent, routed, send_row_bytes=None,
@@ -540,7 +559,7 @@ def main():
     dom = max(total_ms, key=total_ms.get)
     bytes_per_launch = float(np.mean(bm[dom]))
     achieved = bytes_per_launch / (avg_us[dom] * 1e-6) / 1e9
-    traffic = read_traffic(KERNEL_OF_CALL[dom], w.name)
+    traffic = read_traffic(KERNEL_OF_CALL[dom], w.name + mode_suffix(args))
     roofline = {
         "bound": "hbm",
         "kernel": KERNEL_OF_CALL[dom],

@@ -94,6 +94,28 @@ def test_parity_ranked_bad_ids_duplicates_and_corrupt_count():
     say("[parity ranked] corrupt count")
     run_full_parity(W1.scaled(W=4, E=8, K=2, T=50, cap=50, H=64), salt=9,
                     corrupt_cnt=(1, 2, 77), ranked=True)
+    # one tile of tokens (the pack ranks by itself) with duplicates
+    w = W1.scaled(W=4, E=8, K=3, T=70, cap=70, H=64, pad_frac=0.0)
+    srcs, pls = [], []
+    for s in range(w.W):
+        ids, wts = wl.routing(w, s, 8)
+        ids = ids.copy()
+        ids[1] = [5, 5, 4]
+        ids[40] = [1, 0, 1]
+        srcs.append((ids, wts))
+        pls.append(wl.payloads(w, s, 8))
+    say("[parity ranked] duplicates, one tile")
+    run_full_parity(w, srcs=srcs, pls=pls, ranked=True)
+
+
+@pytest.mark.parametrize("T", [100, 300])
+def test_parity_ranked_many_experts(T):
+    """More experts than the token masks of the fast form cover (E = 2048):
+    the ranks come from the general forms (counts in the pack for one tile,
+    the multi-split in the routing kernel)."""
+    w = W1.scaled(W=4, E=2048, K=8, T=T, cap=T, H=64)
+    say(f"[parity ranked] E={w.E} T={T}")
+    run_full_parity(w, salt=19, ranked=True)
 
 
 @pytest.mark.parametrize("name", ["dsv3_small", "decode", "many_route_tiles"])
