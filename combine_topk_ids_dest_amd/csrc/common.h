@@ -151,21 +151,39 @@ struct RankArgs {
     int nbits;                   // bits of an expert id: E <= 2^nbits
 };
 
-// Kept picks of one token in router order, in registers: a valid id
-// (0 <= id < E) is kept while fewer than `slots` earlier valid picks of the
-// token go to the same rank (the others are dropped, as the pack drops
-// them). key[k] = id of a kept pick, else -1 (also for k >= K). K <=
-// kRankMaxK. Loops are unrolled to kRankMaxK so that the ids stay in
-// registers and their loads are all in flight together.
-__device__ __forceinline__ void kept_keys(const int32_t* __restrict__ row, int K, int E,
-                                          int e_local, int slots,
+// The K ids of one token into registers (v[k] = -1 for k >= K), all loads
+// in flight together. K <= kRankMaxK.
+__device__ __forceinline__ void load_row_ids(const int32_t* __restrict__ row, int K,
+                                             int32_t (&v)[kRankMaxK]) {
+#pragma unroll
+    for (int k = 0; k < kRankMaxK; ++k) v[k] = k < K ? row[k] : -1;
+}
+
+// Destination mask of one token from its ids in registers (as
+// token_dest_mask).
+__device__ __forceinline__ uint64_t dest_mask_of(const int32_t (&v)[kRankMaxK], int E,
+                                                 int e_local, uint32_t& bad) {
+    uint64_t mask = 0;
+#pragma unroll
+    for (int k = 0; k < kRankMaxK; ++k) {
+        if (v[k] >= E) bad |= MOE_EP_ERR_ID_RANGE;
+        if (v[k] >= 0 && v[k] < E) mask |= 1ull << ((uint32_t)v[k] / (uint32_t)e_local);
+    }
+    return mask;
+}
+
+// Kept picks of one token in router order, in place on its ids in
+// registers: a valid id (0 <= id < E) is kept while fewer than `slots`
+// earlier valid picks of the token go to the same rank (the others are
+// dropped, as the pack drops them). key[k] = id of a kept pick, else -1
+// (also for k >= K). Loops are unrolled to kRankMaxK so that the ids stay
+// in registers.
+__device__ __forceinline__ void keep_keys(int K, int E, int e_local, int slots,
                                           int32_t (&key)[kRankMaxK]) {
     int32_t dst[kRankMaxK];
 #pragma unroll
-    for (int k = 0; k < kRankMaxK; ++k) key[k] = k < K ? row[k] : -1;
-#pragma unroll
     for (int k = 0; k < kRankMaxK; ++k)
-        if (key[k] >= E) key[k] = -1;
+        if (key[k] >= E || key[k] < 0) key[k] = -1;
     if (slots >= K) return;   // a rank can take all K picks of a token
 #pragma unroll
     for (int k = 0; k < kRankMaxK; ++k)
@@ -177,6 +195,15 @@ __device__ __forceinline__ void kept_keys(const int32_t* __restrict__ row, int K
         for (int k2 = 0; k2 < k; ++k2) before += (dst[k2] >= 0 && dst[k2] == dst[k]) ? 1 : 0;
         if (before >= slots) key[k] = -1;
     }
+}
+
+// The kept picks of one token read from its row of ids (load_row_ids, then
+// keep_keys).
+__device__ __forceinline__ void kept_keys(const int32_t* __restrict__ row, int K, int E,
+                                          int e_local, int slots,
+                                          int32_t (&key)[kRankMaxK]) {
+    load_row_ids(row, K, key);
+    keep_keys(K, E, e_local, slots, key);
 }
 
 // Whether a token's kept ids hold an expert twice (only possible with

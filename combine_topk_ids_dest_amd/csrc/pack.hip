@@ -376,18 +376,70 @@ __device__ __forceinline__ uint32_t write_pick_meta(const int32_t* __restrict__ 
     return bad;
 }
 
+// Per-expert counts per block with the kernel's own routing: block b
+// counts experts [b * r, b * r + r) when r = ceil(E / blocks) is at most
+// this; otherwise block 0 counts them all with LDS atomics.
+constexpr int kEcntPerBlock = 4;
+
+// With the kernel's own routing (T at most one tile; thread i < T holds
+// token i, whose kept ids are key; lanes past T hold none): the partial
+// ranks of token t's kept picks among the source's kept picks of the same
+// expert, in (token, router order). For kept pick k of t (kept id q[k]),
+// the wave counts the kept picks of its tokens with that expert: all of a
+// token's picks when the token is before t, those in columns before k for
+// t itself. One ballot per pair (k, k2) of t's pick and a token's column,
+// masked to the lanes whose tokens count, gives the wave's share; lane 0
+// writes it to s_part[wave][k]. Also, when ge >= 0, the wave's kept picks of
+// experts ge .. ge + ne - 1 into s_epart[wave][j]. KB: the unrolled bound on
+// K (8 or kRankMaxK). Every lane of the block takes part (the ballots).
+template <int KB>
+__device__ __forceinline__ void own_route_counts(const int32_t (&key)[kRankMaxK],
+                                                 const int32_t* q, int K, int64_t t,
+                                                 int32_t (*s_part)[kRankMaxK], int ge,
+                                                 int ne,
+                                                 int32_t (*s_epart)[kEcntPerBlock]) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const uint64_t upto = __ballot(tid <= t);   // tokens up to t
+    const uint64_t before = __ballot(tid < t);  // tokens before t
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        if (k < K) {   // K is the same in every lane
+            const int32_t g = q[k];
+            int32_t sum = 0;
+            if (g >= 0) {
+#pragma unroll
+                for (int k2 = 0; k2 < KB; ++k2)
+                    if (k2 < K)
+                        sum += __popcll(__ballot(key[k2] == g) & (k2 < k ? upto : before));
+            }
+            if (lane == 0) s_part[wave][k] = sum;
+        }
+    }
+    for (int j = 0; j < ne; ++j) {
+        const int32_t g = ge + j;
+        int32_t sum = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < KB; ++k2)
+            if (k2 < K) sum += __popcll(__ballot(key[k2] == g));
+        if (lane == 0) s_epart[wave][j] = sum;
+    }
+}
+
 // QMODE 0: plain rows; 1: payload 0 quantised to fp8; 2: to fp4.
 // PF (plain rows): the first pass of the leading row of the block's first
 // item is loaded before the routing and the slot planning, so its latency
-// overlaps them. RANKED: the send-side per-expert ranks (RankArgs) as well.
-// While wave 0 plans the slots, the token's kept picks get their ranks among
-// the source's kept picks of the same expert, into s_prank: with the routing
-// kernel wave 1 adds the tile offsets to its in-tile ranks; with the
-// kernel's own routing the block finds, for each pick, the kept picks of the
-// same expert in the tokens before (the kept ids of all T tokens are in
-// dynamic LDS; per-wave token masks when no token holds an expert twice,
-// else counts) and block 0 writes the per-expert counts.
-template <int QMODE, bool PF, bool RANKED>
+// overlaps them. RANKED: the send-side per-expert ranks (RankArgs) as well,
+// 1 with the routing kernel's in-tile ranks, 2 with the kernel's own routing
+// (its own instantiation, so that the counting code does not raise the
+// register count of the other forms).
+// The token's kept picks get their ranks among the source's kept picks of
+// the same expert, into s_prank: with the routing kernel, wave 1 adds the
+// tile offsets to its in-tile ranks while wave 0 plans the slots; with the
+// kernel's own routing the block counts them with its routing
+// (own_route_counts), and the blocks write the per-expert counts.
+template <int QMODE, bool PF, int RANKED>
 __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int64_t T,
     int K, int E, int e_local, int W, int slots, int64_t cap, int nsplit,
@@ -396,10 +448,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     int32_t* __restrict__ send_cnt, const PayloadSet P, const QuantArgs Q,
     int32_t* __restrict__ send_eloc, float* __restrict__ send_w, int64_t meta_stride,
     const RankArgs R, uint32_t* __restrict__ err) {
-    // RANKED with own routing: per-wave expert masks or per-expert counts,
-    // then the kept ids of all T tokens (see the prologue)
+    // RANKED with own routing: block 0's per-expert counts [E]
     extern __shared__ int32_t rank_lds[];
     __shared__ int32_t s_prank[kRankMaxK];
+    __shared__ int32_t s_part[RANKED == 2 ? kPackThreads / 64 : 1][kRankMaxK];
+    __shared__ int32_t s_epart[RANKED == 2 ? kPackThreads / 64 : 1][kEcntPerBlock];
+    __shared__ __align__(16) int32_t s_q[kRankMaxK];
     __shared__ int32_t s_dest[MOE_EP_MAX_WORLD];
     __shared__ int32_t s_slot[MOE_EP_MAX_WORLD];
     __shared__ int s_n;
@@ -422,7 +476,25 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
     if (own_route) {
         uint64_t mask = 0;
         uint32_t bad = 0;
-        if (tid < T) mask = token_dest_mask(ids + (int64_t)tid * K, K, E, e_local, bad);
+        // RANKED: the token's ids, loaded once for its routing and its kept
+        // ids; the thread of the block's token (one item per block) shares
+        // them through s_q
+        int32_t key[kRankMaxK];
+        if (RANKED == 2) {
+#pragma unroll
+            for (int k = 0; k < kRankMaxK; ++k) key[k] = -1;
+            if (tid < T) load_row_ids(ids + (int64_t)tid * K, K, key);
+            mask = dest_mask_of(key, E, e_local, bad);
+            keep_keys(K, E, e_local, slots, key);
+            if (tid == (int64_t)blockIdx.x / nsplit) {
+#pragma unroll
+                for (int k = 0; k < kRankMaxK; ++k) s_q[k] = key[k];
+            }
+            if (blockIdx.x == 0 && (E + gridDim.x - 1) / gridDim.x > kEcntPerBlock)
+                for (int g = tid; g < E; g += kPackThreads) rank_lds[g] = 0;
+        } else if (tid < T) {
+            mask = token_dest_mask(ids + (int64_t)tid * K, K, E, e_local, bad);
+        }
         if (blockIdx.x == 0) report(err, bad);
         if (wave * 64 < T) {   // the waves that hold tokens
             uint64_t mine = 0;
@@ -438,84 +510,45 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             for (int w = 0; w * 64 < T; ++w) c += __popcll(s_bits[w][tid]);
             send_cnt[tid] = c;
         }
-        if (RANKED) {
-            // one item per block: its token t
-            const int64_t t = (int64_t)blockIdx.x / nsplit;
-            constexpr int waves = kPackThreads / 64;
-            const bool mask_ok = E <= kRankMaskE;
-            // the masks [waves * E] (fast form) or the counts [E] (int32),
-            // then the kept ids of all T tokens [T * K] (int16)
-            unsigned long long* masks = reinterpret_cast<unsigned long long*>(rank_lds);
-            int32_t* hist = rank_lds;
-            int16_t* keys = reinterpret_cast<int16_t*>(rank_lds + (mask_ok ? 2 * waves * E : E));
-            int32_t key[kRankMaxK];
+        // RANKED: the partial ranks of the block's picks (summed over the
+        // waves by wave 1 in the slot phase) and the per-expert counts
+        const int ecnt_r = RANKED == 2 ? (E + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+        const int ecnt_g = (int)blockIdx.x * ecnt_r;
+        if (RANKED == 2) {
+            const int64_t t0 = (int64_t)blockIdx.x / nsplit;
+            int32_t q[kRankMaxK];
 #pragma unroll
-            for (int k = 0; k < kRankMaxK; ++k) key[k] = -1;
-            if (tid < T) {
-                kept_keys(ids + (int64_t)tid * K, K, E, e_local, slots, key);
+            for (int k = 0; k < kRankMaxK; k += 4) {
+                const int4 v = *reinterpret_cast<const int4*>(s_q + k);
+                q[k] = v.x; q[k + 1] = v.y; q[k + 2] = v.z; q[k + 3] = v.w;
+            }
+            const bool spread = ecnt_r <= kEcntPerBlock;
+            const int ne = !spread ? 0 : ecnt_g + ecnt_r <= E ? ecnt_r
+                         : ecnt_g < E ? E - ecnt_g : 0;
+            if (K <= 8) own_route_counts<8>(key, q, K, t0, s_part, ecnt_g, ne, s_epart);
+            else own_route_counts<kRankMaxK>(key, q, K, t0, s_part, ecnt_g, ne, s_epart);
+            if (!spread && blockIdx.x == 0) {
 #pragma unroll
                 for (int k = 0; k < kRankMaxK; ++k)
-                    if (k < K) keys[tid * K + k] = (int16_t)key[k];
-            }
-            // (a barrier: every token's kept ids are in LDS after it)
-            const bool fast = mask_ok && !__syncthreads_or(has_repeated_key(key));
-            if (fast) {
-                for (int i = tid; i < waves * E; i += kPackThreads) masks[i] = 0;
-                __syncthreads();
-                mark_expert_masks(key, masks, E);
-                __syncthreads();
-                // the thread of token t ranks its picks (queries all in flight)
-                if (tid == t) {
-#pragma unroll
-                    for (int k = 0; k < kRankMaxK; ++k)
-                        if (k < K)
-                            s_prank[k] = key[k] >= 0 ? mask_rank<waves>(masks, E, (int)t, key[k]) : -1;
-                }
-                if (blockIdx.x == 0)
-                    for (int g = tid; g < E; g += kPackThreads) {
-                        int32_t c = 0;
-                        for (int w = 0; w < waves; ++w) c += __popcll(masks[w * E + g]);
-                        R.send_ecnt[g] = c;
-                    }
-            } else {
-                // any input: for each pick, the kept picks of the same expert
-                // in the tokens before t (and in t's earlier columns); sums
-                // over the tokens are order-free, so LDS atomics give the
-                // same counts every run
-                if (blockIdx.x == 0)
-                    for (int g = tid; g < E; g += kPackThreads) hist[g] = 0;
-                if (tid < K) s_prank[tid] = 0;
-                __syncthreads();
-                if (tid <= t && tid < T) {
-                    int32_t mine[kRankMaxK];
-#pragma unroll
-                    for (int k2 = 0; k2 < kRankMaxK; ++k2)
-                        mine[k2] = k2 < K ? keys[tid * K + k2] : -2;
-                    for (int k = 0; k < K; ++k) {
-                        const int32_t q = keys[t * K + k];
-                        const int upto = tid < t ? K : k;
-                        int32_t c = 0;
-#pragma unroll
-                        for (int k2 = 0; k2 < kRankMaxK; ++k2)
-                            c += (k2 < upto && mine[k2] == q) ? 1 : 0;
-                        if (q >= 0 && c) atomicAdd(&s_prank[k], c);
-                    }
-                }
-                if (blockIdx.x == 0 && tid < T)
-                    for (int k = 0; k < K; ++k) {
-                        const int32_t g = keys[tid * K + k];
-                        if (g >= 0) atomicAdd(&hist[g], 1);
-                    }
-                __syncthreads();
-                if (tid < K && keys[t * K + tid] < 0) s_prank[tid] = -1;
-                if (blockIdx.x == 0)
-                    for (int g = tid; g < E; g += kPackThreads) R.send_ecnt[g] = hist[g];
+                    if (key[k] >= 0) atomicAdd(&rank_lds[key[k]], 1);
             }
         }
         // (a barrier here also keeps the compiler from carrying prologue
         // values into the token loop, which costs registers)
         __syncthreads();
-    } else if (RANKED && blockIdx.x == 0 && R.eoff_tile == nullptr) {
+        if (RANKED == 2) {
+            if (ecnt_r <= kEcntPerBlock) {
+                if (tid < ecnt_r && ecnt_g + tid < E) {
+                    int32_t c = 0;
+#pragma unroll
+                    for (int w = 0; w < kPackThreads / 64; ++w) c += s_epart[w][tid];
+                    R.send_ecnt[ecnt_g + tid] = c;
+                }
+            } else if (blockIdx.x == 0) {
+                for (int g = tid; g < E; g += kPackThreads) R.send_ecnt[g] = rank_lds[g];
+            }
+        }
+    } else if (RANKED == 1 && blockIdx.x == 0 && R.eoff_tile == nullptr) {
         // per-expert totals from the tile counts (column_scan writes them
         // when it computes the tile offsets)
         const int64_t tiles = (T + kRouteTile - 1) / kRouteTile;
@@ -589,9 +622,14 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
                 s_slot[pos] = slot;
             }
             if (tid == 0) s_n = __popcll(act);
-        } else if (RANKED && !own_route && part == 0 && tid - 64 < K) {
+        } else if (RANKED == 1 && !own_route && part == 0 && tid - 64 < K) {
             // wave 1, lane k: pick k's rank, in parallel with wave 0's slots
             s_prank[tid - 64] = source_rank(ids, t, K, tid - 64, E, R);
+        } else if (RANKED == 2 && part == 0 && tid - 64 < K) {
+            int32_t r = 0;
+#pragma unroll
+            for (int w = 0; w < kPackThreads / 64; ++w) r += s_part[w][tid - 64];
+            s_prank[tid - 64] = r;   // read only for kept picks
         }
         __syncthreads();
         const int n = s_n;
@@ -675,7 +713,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
             uint32_t bad = 0;
             if (slot >= 0) {
                 const int64_t meta = (int64_t)tid * meta_stride + (int64_t)slot * slots;
-                bad = write_pick_meta<RANKED>(
+                bad = write_pick_meta<RANKED != 0>(
                     ids, wts, t, K, E, e_local, tid, slots, send_eloc + meta, send_w + meta,
                     RANKED ? R.send_rank + meta : nullptr, s_prank);
             }
@@ -705,31 +743,31 @@ hipError_t launch_pack_copy(const int32_t* ids, const float* wts, int64_t T,
     const bool pf = P.n > 0 && (rank == nullptr || P.row_bytes[0] / 16 > kPackPrefetchVecs);
     const bool ranked = ranks != nullptr && ranks->send_rank != nullptr;
     const RankArgs R = ranked ? *ranks : RankArgs{};
-    // own routing with ranks: the masks (or the per-expert counts) and all
-    // tokens' kept ids
-    const size_t lds = ranked && rank == nullptr
-        ? (E <= kRankMaskE ? sizeof(uint64_t) * (size_t)(kPackThreads / 64) * E
-                           : sizeof(int32_t) * (size_t)E) +
-              sizeof(int16_t) * (size_t)T * K
-        : 0;
+    // own routing with ranks: block 0's per-expert counts, unless the
+    // blocks share them out
+    const size_t lds = ranked && rank == nullptr && (E + grid - 1) / grid > kEcntPerBlock
+                           ? sizeof(int32_t) * (size_t)E : 0;
     const QuantArgs Q = quant ? *quant : QuantArgs{};
 #define MOE_EP_PACK_LAUNCH(QM, PFV, RK)                                                   \
     pack_copy_kernel<QM, PFV, RK><<<dim3((unsigned)grid), dim3(kPackThreads), lds, stream>>>( \
         ids, wts, T, K, E, e_local, W, slots, cap, nsplit, rank, token_slot, tile_cnt,   \
         tile_off, send_cnt, P, Q, send_eloc, send_w, meta_stride, R, err)
+    // ranks from the routing kernel (1) or counted by the pack itself (2)
+    const int rk = !ranked ? 0 : rank != nullptr ? 1 : 2;
+#define MOE_EP_PACK_RANKED(QM, PFV)                                                       \
+    if (rk == 2) MOE_EP_PACK_LAUNCH(QM, PFV, 2);                                          \
+    else if (rk == 1) MOE_EP_PACK_LAUNCH(QM, PFV, 1);                                     \
+    else MOE_EP_PACK_LAUNCH(QM, PFV, 0);
     if (quant && quant->mode == 2) {
-        if (ranked) MOE_EP_PACK_LAUNCH(2, false, true);
-        else MOE_EP_PACK_LAUNCH(2, false, false);
+        MOE_EP_PACK_RANKED(2, false)
     } else if (quant) {
-        if (ranked) MOE_EP_PACK_LAUNCH(1, false, true);
-        else MOE_EP_PACK_LAUNCH(1, false, false);
+        MOE_EP_PACK_RANKED(1, false)
     } else if (pf) {
-        if (ranked) MOE_EP_PACK_LAUNCH(0, true, true);
-        else MOE_EP_PACK_LAUNCH(0, true, false);
+        MOE_EP_PACK_RANKED(0, true)
     } else {
-        if (ranked) MOE_EP_PACK_LAUNCH(0, false, true);
-        else MOE_EP_PACK_LAUNCH(0, false, false);
+        MOE_EP_PACK_RANKED(0, false)
     }
+#undef MOE_EP_PACK_RANKED
 #undef MOE_EP_PACK_LAUNCH
     return hipGetLastError();
 }
