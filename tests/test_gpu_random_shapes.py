@@ -2,7 +2,9 @@
 hidden sizes that are not powers of two, K above and below e_local, cap
 above T, partial padding, skewed routing, and every form of the path
 (plain, fp32 combine, fp8 and fp4 quantize-on-pack, fused local combine),
-each compared element by element with the oracle."""
+each with the receive side's own scan and, in every other group of five
+cases, with the senders' per-expert ranks, compared element by element
+with the oracle."""
 import numpy as np
 import pytest
 
@@ -25,6 +27,7 @@ def _case(i):
     T = int(rng.integers(0, 400))
     cap = T + int(rng.integers(0, 50))
     mode = ["plain", "f32", "fp8", "fp4", "fused"][i % 5]
+    ranked = (i // 5) % 2 == 1
     # bf16 rows are 16-byte multiples (H % 8); the quantised rows need more
     H = int(rng.choice([32, 96, 256, 544, 1024])) if mode in ("fp8", "fp4") \
         else int(rng.choice([8, 24, 64, 120, 256, 1000]))
@@ -34,15 +37,15 @@ def _case(i):
     w = wl.WORKLOADS[1].scaled(T=T, H=H, E=E, K=K, W=W, cap=cap, routing=routing,
                                zipf_s=1.1 if routing == "zipf" else 0.0,
                                pad_frac=float(rng.choice([0.0, 0.05, 0.3])))
-    return w, mode
+    return w, mode, ranked
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape_parity(i):
-    w, mode = _case(i)
-    say(f"[random {i}] {mode} T={w.T} H={w.H} E={w.E} K={w.K} W={w.W} cap={w.cap} "
-        f"{w.routing} pad={w.pad_frac}")
-    kw = {}
+    w, mode, ranked = _case(i)
+    say(f"[random {i}] {mode}{' ranked' if ranked else ''} T={w.T} H={w.H} E={w.E} K={w.K} "
+        f"W={w.W} cap={w.cap} {w.routing} pad={w.pad_frac}")
+    kw = {"ranked": ranked}
     if mode == "f32":
         kw["f32"] = True
     elif mode == "fp8":
