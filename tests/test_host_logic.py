@@ -295,3 +295,13 @@ def test_binding_checks_receive_and_combine_shapes():
         B.prepare_combine_unpack_fused(ret, ts, cap, 0, Y, own["e"], own["w"],
                                        z(cap - 1, 2, dtype=torch.int32), el, K, out)
     assert "one GPU" not in str(e.value)
+
+
+def test_bench_receive_form():
+    """--receive auto takes the sender-ranked receive side for batches of one
+    routing tile (decode, tiny) and the receiver's scan above."""
+    W = wl.WORKLOADS
+    assert bench.receive_ranked("auto", W[1].T) and bench.receive_ranked("auto", W[4].T)
+    assert not any(bench.receive_ranked("auto", W[i].T) for i in (2, 3, 5))
+    assert bench.receive_ranked("auto", 256) and not bench.receive_ranked("auto", 257)
+    assert bench.receive_ranked("ranked", 4096) and not bench.receive_ranked("scan", 64)
