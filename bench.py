@@ -25,6 +25,13 @@ with R_own expert rows) leaves the reduce and enters the fused unpack:
   reduce_peers (dest r)   (R - R_own)*Hb + (S - S_own)*(slots*8 + Hb)
   unpack_fused (source s) (U - S_own)*Hb + R_own*Hb + S_own*slots*8 + T*Hb
 
+With the sender-ranked receive side (--receive ranked, and --receive auto
+when T <= 256) the pack also writes each used slot's ranks and the counts
+per expert, and the receive side reads those instead of scanning:
+
+  pack (source s)      ... + U*slots*4 + 4*E
+  batch (dest r)       4*W + S*slots*8 + 4*E + S*P + R*P + 4*e_local
+
 Besides the contract fields the line carries: per-call times (a separate
 pass with HIP events around each call; averages, which the roofline uses,
 and medians), the whole step with every call on one stream, the time per
@@ -36,6 +43,7 @@ and the rate of the runtime's own 1 GiB device copy in the same session as
 a second roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+                       [--receive auto|scan|ranked] [--fp8-group G | --fp4] [--fused-local]
 """
 import argparse
 import gc
