@@ -619,7 +619,8 @@ int moe_ep_expert_batch_ranked(const int32_t* recv_cnt, int64_t cnt_rank_stride,
     if (!recv_cnt || !recv_eloc || !recv_rank || !recv_ecnt || !expert_num_tokens ||
         !recv_row)
         return MOE_EP_EINVAL;
-    // the per-source counts' prefix is an LDS table of (W + 1) * e_local
+    // the ranks come from packs limited to E = W * e_local <= kRankMaxE; the
+    // receive side takes the same limit, so the form has one domain
     if (!rank_sizes_ok(1, W * e_local)) return MOE_EP_EINVAL;
     if (cnt_rank_stride < 1 || eloc_rank_stride < sh.cap * sh.slots ||
         ecnt_rank_stride < e_local)

@@ -389,9 +389,10 @@ constexpr int kEcntPerBlock = 4;
 // token's picks when the token is before t, those in columns before k for
 // t itself. One ballot per pair (k, k2) of t's pick and a token's column,
 // masked to the lanes whose tokens count, gives the wave's share; lane 0
-// writes it to s_part[wave][k]. Also, when ge >= 0, the wave's kept picks of
-// experts ge .. ge + ne - 1 into s_epart[wave][j]. KB: the unrolled bound on
-// K (8 or kRankMaxK). Every lane of the block takes part (the ballots).
+// writes it to s_part[wave][k]. Also the wave's kept picks of experts
+// ge .. ge + ne - 1 (none when ne = 0) into s_epart[wave][j]. KB: the
+// unrolled bound on K (8 or kRankMaxK). Every lane of the block takes part
+// (the ballots).
 template <int KB>
 __device__ __forceinline__ void own_route_counts(const int32_t (&key)[kRankMaxK],
                                                  const int32_t* q, int K, int64_t t,
