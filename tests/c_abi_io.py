@@ -7,6 +7,18 @@ import numpy as np
 EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "moe_ep_path")
 
 
+def program() -> str:
+    """The built program; builds it (gcc, about a second) when it is missing."""
+    if not os.path.exists(EXE):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "c_abi_build", os.path.join(os.path.dirname(EXE), "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    return EXE
+
+
 def write_inputs(path, w, srcs, hidden, header=None):
     """srcs: (topk_ids [T, K] int32, topk_weights [T, K] fp32) per source;
     hidden: bf16 bits [T, H] per source. header overrides (T, H, E, K, W,

@@ -2,24 +2,12 @@
 library with -Wall -Wextra -Werror, checks its arguments, and reports a
 status from the library's host checks by name (moe_ep_capacities rejects
 E % W != 0 before any device call)."""
-import os
 import subprocess
 
 import numpy as np
 
 import workloads as wl
-from c_abi_io import EXE, write_inputs
-
-
-def _exe():
-    if not os.path.exists(EXE):
-        import importlib.util
-        spec = importlib.util.spec_from_file_location(
-            "c_abi_build", os.path.join(os.path.dirname(EXE), "build.py"))
-        mod = importlib.util.module_from_spec(spec)
-        spec.loader.exec_module(mod)
-        mod.build()
-    return EXE
+from c_abi_io import program as _exe, write_inputs
 
 
 def test_usage_without_arguments():

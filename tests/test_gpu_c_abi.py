@@ -4,7 +4,6 @@ the packs, the receive sides and combine reduces, and the unpacks for W
 logical ranks with identity experts (an expert's output rows are its
 batched input rows). Its counts, token slots, expert_num_tokens, error
 flags and combined rows must be the oracle's, bit for bit."""
-import os
 import subprocess
 
 import numpy as np
@@ -13,7 +12,7 @@ import pytest
 import oracle
 import workloads as wl
 from parity import say
-from c_abi_io import EXE, read_outputs, write_inputs
+from c_abi_io import program, read_outputs, write_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -29,15 +28,14 @@ CASES = {
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_c_program_runs_the_path(name, tmp_path):
-    if not os.path.exists(EXE):
-        pytest.fail(f"{EXE} is not built: run __graft_entry__.build()")
+    exe = program()
     w = CASES[name]
     srcs = [wl.routing(w, s, 31) for s in range(w.W)]
     hid = [wl.hidden_bf16(w, s, 31) for s in range(w.W)]
     inp, outp = tmp_path / "in.bin", tmp_path / "out.bin"
     write_inputs(inp, w, srcs, hid)
     say(f"[c abi] {name}: T={w.T} H={w.H} E={w.E} K={w.K} W={w.W} cap={w.cap}")
-    r = subprocess.run([EXE, str(inp), str(outp)], capture_output=True, text=True, timeout=120)
+    r = subprocess.run([exe, str(inp), str(outp)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     got = read_outputs(outp, w)
 
