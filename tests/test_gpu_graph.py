@@ -26,8 +26,9 @@ def _setup(w, seed, **mode):
 
 
 def _outputs(ep):
-    return [x.clone() for x in (ep.send_cnt, ep.token_slot, ep.send_eloc,
-                                ep.expert_num_tokens, ep.recv_row, ep.out)] + \
+    ranks = [ep.send_rank, ep.send_ecnt] if ep.ranked else []
+    return [x.clone() for x in [ep.send_cnt, ep.token_slot, ep.send_eloc,
+                                ep.expert_num_tokens, ep.recv_row, ep.out] + ranks] + \
            [x.clone() for x in ep.send]
 
 
@@ -40,6 +41,10 @@ CASES = [
     (2, SMALL_DSV3, dict(quant_group=128), False),
     (4, None, dict(quant_fp4=True), False),
     (2, SMALL_DSV3, {}, True),
+    # the senders' per-expert ranks and the ranked receive side, counted by
+    # the pack itself (one tile) and by the routing kernel (three tiles)
+    (4, None, dict(ranked=True), False),
+    (2, SMALL_DSV3, dict(ranked=True), False),
 ]
 
 
@@ -69,6 +74,8 @@ def test_graph_replay_matches_eager(wid, scale, mode, fused):
         ep.token_slot.fill_(-9)
         ep.send_cnt.fill_(-9)
         ep.expert_num_tokens.fill_(-9)
+        if ep.ranked:
+            ep.send_ecnt.fill_(-9)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
