@@ -31,11 +31,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Row data is touched once per call. The combine kernels and the expert
 // batch copy load and store it with the nontemporal hint, which measured
-// faster on gfx950; the pack (one read, several writes per token) uses plain
-// loads and stores, which measured faster for it. Knobs for tuning builds;
-// the defaults are the product settings.
-#ifndef MOE_EP_PACK_NT
-#define MOE_EP_PACK_NT 0
+// faster on gfx950; the pack (one read, several writes per token) stores
+// with the hint but loads without it (nontemporal loads measured slower
+// there). Knobs for tuning builds; the defaults are the product settings.
+#ifndef MOE_EP_PACK_LD_NT
+#define MOE_EP_PACK_LD_NT 0
+#endif
+#ifndef MOE_EP_PACK_ST_NT
+#define MOE_EP_PACK_ST_NT 1
 #endif
 #ifndef MOE_EP_BATCH_LD_NT
 #define MOE_EP_BATCH_LD_NT 1

@@ -108,8 +108,8 @@ __device__ __forceinline__ void quantize_pass(const uint8_t* __restrict__ src,
     for (int u = 0; u < kQU; ++u) {
         const int64_t i = base + u * kPackThreads + threadIdx.x;
         if (i < hi) {
-            v[u][0] = ld_row<MOE_EP_PACK_NT>(src + i * 32);
-            v[u][1] = ld_row<MOE_EP_PACK_NT>(src + i * 32 + 16);
+            v[u][0] = ld_row<MOE_EP_PACK_LD_NT>(src + i * 32);
+            v[u][1] = ld_row<MOE_EP_PACK_LD_NT>(src + i * 32 + 16);
         }
     }
 #pragma unroll
@@ -224,8 +224,8 @@ __device__ __forceinline__ void quantize_pass_fp4(const uint8_t* __restrict__ sr
     for (int u = 0; u < kQU; ++u) {
         const int64_t i = base + u * kPackThreads + threadIdx.x;
         if (i < hi) {
-            v[u][0] = ld_row<MOE_EP_PACK_NT>(src + i * 32);
-            v[u][1] = ld_row<MOE_EP_PACK_NT>(src + i * 32 + 16);
+            v[u][0] = ld_row<MOE_EP_PACK_LD_NT>(src + i * 32);
+            v[u][1] = ld_row<MOE_EP_PACK_LD_NT>(src + i * 32 + 16);
         }
     }
 #pragma unroll
@@ -286,7 +286,7 @@ __device__ __forceinline__ void store_quant_pass(const QuantArgs& Q, int64_t bas
         for (int u = 0; u < kQU; ++u) {
             const int64_t i = base + u * kPackThreads + threadIdx.x;
             if (i < hi) {
-                st_row<MOE_EP_PACK_NT>(qrow + i * 16, qp.codes[u]);
+                st_row<MOE_EP_PACK_ST_NT>(qrow + i * 16, qp.codes[u]);
                 if ((i % gu) == 0) srow[i / gu] = qp.scale[u];
             }
         }
@@ -308,7 +308,7 @@ __device__ __forceinline__ void load_first_pass(const PayloadSet& P, int64_t b, 
 #pragma unroll
     for (int u = 0; u < kPackUnroll; ++u) {
         const int64_t i = p_lo + u * kPackThreads + (int64_t)threadIdx.x;
-        if (i < p_mid) pre[u] = ld_row<MOE_EP_PACK_NT>(src + i * 16);
+        if (i < p_mid) pre[u] = ld_row<MOE_EP_PACK_LD_NT>(src + i * 16);
     }
 }
 
@@ -676,7 +676,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                 for (int u = 0; u < kPackUnroll; ++u) {
                     const int64_t i = p_lo + u * kPackThreads + tid;
-                    if (i < p_mid) st_row<MOE_EP_PACK_NT>(dst + i * 16, pre[u]);
+                    if (i < p_mid) st_row<MOE_EP_PACK_ST_NT>(dst + i * 16, pre[u]);
                 }
             }
         }
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                 for (int u = 0; u < kPackUnroll; ++u) {
                     const int64_t i = i0 + u * kPackThreads;
-                    if (i < v_hi) v[u] = ld_row<MOE_EP_PACK_NT>(src + i * 16);
+                    if (i < v_hi) v[u] = ld_row<MOE_EP_PACK_LD_NT>(src + i * 16);
                 }
                 for (int a = 0; a < n; ++a) {
                     uint8_t* dst = P.dst[p] + s_dest[a] * P.dst_stride[p] +
@@ -703,7 +703,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
 #pragma unroll
                     for (int u = 0; u < kPackUnroll; ++u) {
                         const int64_t i = i0 + u * kPackThreads;
-                        if (i < v_hi) st_row<MOE_EP_PACK_NT>(dst + i * 16, v[u]);
+                        if (i < v_hi) st_row<MOE_EP_PACK_ST_NT>(dst + i * 16, v[u]);
                     }
                 }
             }
