@@ -305,3 +305,14 @@ def test_bench_receive_form():
     assert not any(bench.receive_ranked("auto", W[i].T) for i in (2, 3, 5))
     assert bench.receive_ranked("auto", 256) and not bench.receive_ranked("auto", 257)
     assert bench.receive_ranked("ranked", 4096) and not bench.receive_ranked("scan", 64)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench measures one GPU (the W ranks are logical partitions of it):
+    --gpus above 1 exits with a message before touching any device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus must be 1" in r.stderr
