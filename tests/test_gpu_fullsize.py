@@ -69,6 +69,20 @@ def test_fullsize_fp4_pack(wid):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("wid,mode", [(2, "fp8"), (4, "fp4")])
+def test_fullsize_ranked_quantised(wid, mode):
+    """The quantising packs with the per-expert ranks and the ranked receive
+    side at full size: DS-V3 with fp8 (the routing kernel's ranks) and
+    decode with 4-bit codes (the pack counts the ranks itself)."""
+    w = wl.WORKLOADS[wid]
+    say(f"[fullsize ranked {mode}] start {w.name}")
+    if mode == "fp8":
+        run_fullsize(w, fp8_group=128, ranked=True)
+    else:
+        run_fullsize(w, fp4=True, ranked=True)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("wid", [2, 3, 4])
 def test_fullsize_fused_local_combine(wid):
     """The fused combine of each rank's local slice at full size (the shared
