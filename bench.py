@@ -143,9 +143,18 @@ def read_traffic(kernel: str, workload: str):
 RANKED_MAX_T = 256
 
 
-def receive_ranked(receive: str, T: int) -> bool:
-    """Whether the step uses the sender-ranked receive side (--receive)."""
-    return receive == "ranked" or (receive == "auto" and T <= RANKED_MAX_T)
+# The sender-ranked form's limits (the library returns EINVAL beyond them).
+RANKED_MAX_K = 16
+RANKED_MAX_E = 4096
+
+
+def receive_ranked(receive: str, T: int, K: int = 1, E: int = 1) -> bool:
+    """Whether the step uses the sender-ranked receive side (--receive):
+    always for "ranked"; for "auto" when the batch is one routing tile and
+    the shape is within the form's limits."""
+    if receive == "ranked":
+        return True
+    return receive == "auto" and T <= RANKED_MAX_T and K <= RANKED_MAX_K and E <= RANKED_MAX_E
 
 
 def mode_suffix(args) -> str:
@@ -400,7 +409,7 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.ranked:
         args.receive = "ranked"
-    args.ranked = receive_ranked(args.receive, w.T)
+    args.ranked = receive_ranked(args.receive, w.T, w.K, w.E)
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     srcs = [wl.routing(w, s) for s in range(w.W)]

@@ -305,6 +305,9 @@ def test_bench_receive_form():
     assert not any(bench.receive_ranked("auto", W[i].T) for i in (2, 3, 5))
     assert bench.receive_ranked("auto", 256) and not bench.receive_ranked("auto", 257)
     assert bench.receive_ranked("ranked", 4096) and not bench.receive_ranked("scan", 64)
+    # auto keeps the scan where the ranked form does not apply
+    assert not bench.receive_ranked("auto", 64, K=64, E=128)
+    assert not bench.receive_ranked("auto", 64, K=8, E=8192)
 
 
 def test_bench_refuses_more_than_one_gpu():
