@@ -156,10 +156,11 @@ struct RankArgs {
 
 // The K ids of one token into registers (v[k] = -1 for k >= K), all loads
 // in flight together. K <= kRankMaxK.
+template <int KB = kRankMaxK>
 __device__ __forceinline__ void load_row_ids(const int32_t* __restrict__ row, int K,
                                              int32_t (&v)[kRankMaxK]) {
 #pragma unroll
-    for (int k = 0; k < kRankMaxK; ++k) v[k] = k < K ? row[k] : -1;
+    for (int k = 0; k < KB; ++k) v[k] = k < K ? row[k] : -1;
 }
 
 // Destination mask of one token from its ids in registers (as
@@ -181,18 +182,19 @@ __device__ __forceinline__ uint64_t dest_mask_of(const int32_t (&v)[kRankMaxK], 
 // dropped, as the pack drops them). key[k] = id of a kept pick, else -1
 // (also for k >= K). Loops are unrolled to kRankMaxK so that the ids stay
 // in registers.
+template <int KB = kRankMaxK>
 __device__ __forceinline__ void keep_keys(int K, int E, int e_local, int slots,
                                           int32_t (&key)[kRankMaxK]) {
     int32_t dst[kRankMaxK];
 #pragma unroll
-    for (int k = 0; k < kRankMaxK; ++k)
+    for (int k = 0; k < KB; ++k)
         if (key[k] >= E || key[k] < 0) key[k] = -1;
     if (slots >= K) return;   // a rank can take all K picks of a token
 #pragma unroll
-    for (int k = 0; k < kRankMaxK; ++k)
+    for (int k = 0; k < KB; ++k)
         dst[k] = key[k] >= 0 ? (int32_t)((uint32_t)key[k] / (uint32_t)e_local) : -1;
 #pragma unroll
-    for (int k = kRankMaxK - 1; k > 0; --k) {
+    for (int k = KB - 1; k > 0; --k) {
         int before = 0;
 #pragma unroll
         for (int k2 = 0; k2 < k; ++k2) before += (dst[k2] >= 0 && dst[k2] == dst[k]) ? 1 : 0;
@@ -202,19 +204,21 @@ __device__ __forceinline__ void keep_keys(int K, int E, int e_local, int slots,
 
 // The kept picks of one token read from its row of ids (load_row_ids, then
 // keep_keys).
+template <int KB = kRankMaxK>
 __device__ __forceinline__ void kept_keys(const int32_t* __restrict__ row, int K, int E,
                                           int e_local, int slots,
                                           int32_t (&key)[kRankMaxK]) {
-    load_row_ids(row, K, key);
-    keep_keys(K, E, e_local, slots, key);
+    load_row_ids<KB>(row, K, key);
+    keep_keys<KB>(K, E, e_local, slots, key);
 }
 
 // Whether a token's kept ids hold an expert twice (only possible with
 // duplicate ids in its routing).
+template <int KB = kRankMaxK>
 __device__ __forceinline__ bool has_repeated_key(const int32_t (&key)[kRankMaxK]) {
     bool rep = false;
 #pragma unroll
-    for (int k = 1; k < kRankMaxK; ++k)
+    for (int k = 1; k < KB; ++k)
 #pragma unroll
         for (int k2 = 0; k2 < k; ++k2) rep |= key[k] >= 0 && key[k] == key[k2];
     return rep;
@@ -276,12 +280,13 @@ __device__ __forceinline__ void tile_expert_ranks(const int16_t* keys, int16_t* 
 // into masks[wave * E + g] for every kept id g of its tokens (LDS atomics:
 // the result does not depend on their order); masks must be zeroed before
 // and a barrier must separate this from the queries.
+template <int KB = kRankMaxK>
 __device__ __forceinline__ void mark_expert_masks(const int32_t (&key)[kRankMaxK],
                                                   unsigned long long* masks, int E) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int k = 0; k < kRankMaxK; ++k)
+    for (int k = 0; k < KB; ++k)
         if (key[k] >= 0) atomicOr(&masks[wave * E + key[k]], 1ull << lane);
 }
 

@@ -18,7 +18,8 @@
 // (T <= 256, decode-sized batches) neither kernel runs: every pack_copy
 // block derives the ranks of its token from the masks of all T tokens.
 //
-// RANKED (the send-side per-expert ranks, RankArgs): route_local also ranks
+// With the send-side per-expert ranks (RankArgs; KB > 0, the number of
+// picks per token the ranking code is unrolled for): route_local also ranks
 // each kept pick of the tile among the tile's kept picks of the same expert
 // into prank [T * K], and writes the tile's count per expert to ecnt_tile
 // [tiles][E]; the tile offsets per expert are summed by pack_copy or come
@@ -30,7 +31,9 @@
 
 namespace moe_ep {
 
-template <bool RANKED>
+// KB: 0 without the per-expert ranks, else the unrolled bound on K (8 or
+// kRankMaxK) of the ranking code.
+template <int KB>
 __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
     const int32_t* __restrict__ ids, int64_t T, int K, int E, int e_local,
     int W, int slots, int nbits, int32_t* __restrict__ rank,
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
             rank[d * T + t] = ((mask >> d) & 1ull) ? before + rank_below(b) : -1;
     }
 
-    if (RANKED) {
+    if (KB > 0) {
         constexpr int waves = kRouteTile / 64;
         int16_t* keys = rank_lds;
         int16_t* rnk = keys + kRouteTile * K;
@@ -91,16 +94,16 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
         int32_t key[kRankMaxK];
 #pragma unroll
         for (int k = 0; k < kRankMaxK; ++k) key[k] = -1;
-        if (t < T) kept_keys(ids + t * K, K, E, e_local, slots, key);
-        const bool fast = E <= kRankMaskE && !__syncthreads_or(has_repeated_key(key));
+        if (t < T) kept_keys<KB>(ids + t * K, K, E, e_local, slots, key);
+        const bool fast = E <= kRankMaskE && !__syncthreads_or(has_repeated_key<KB>(key));
         if (fast) {
             for (int i = tid; i < waves * E; i += kRouteTile) masks[i] = 0;
             __syncthreads();
-            mark_expert_masks(key, masks, E);
+            mark_expert_masks<KB>(key, masks, E);
             __syncthreads();
             // this thread's token's picks (queries unrolled, all in flight)
 #pragma unroll
-            for (int k = 0; k < kRankMaxK; ++k)
+            for (int k = 0; k < KB; ++k)
                 if (k < K && t < T)
                     prank[t * K + k] = key[k] >= 0 ? mask_rank<waves>(masks, E, tid, key[k]) : -1;
             for (int g = tid; g < E; g += kRouteTile) {
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < kRankMaxK; ++k)
+            for (int k = 0; k < KB; ++k)
                 if (k < K && t < T) keys[tid * K + k] = (int16_t)key[k];
             for (int i = tid; i < (waves + 1) * E; i += kRouteTile) hist[i] = 0;
             __syncthreads();
@@ -201,10 +204,15 @@ hipError_t launch_route_local(const int32_t* ids, int64_t T, int K, int E,
                                              : 0;
         const size_t lds = sizeof(int16_t) * (size_t)2 * kRouteTile * K +
                            (counts > masks ? counts : masks);
-        route_local_kernel<true><<<dim3((unsigned)ntiles), dim3(kRouteTile), lds, stream>>>(
-            ids, T, K, E, e_local, W, slots, nbits, rank, tile_cnt, prank, ecnt_tile, err);
+        if (K <= 8)
+            route_local_kernel<8><<<dim3((unsigned)ntiles), dim3(kRouteTile), lds, stream>>>(
+                ids, T, K, E, e_local, W, slots, nbits, rank, tile_cnt, prank, ecnt_tile, err);
+        else
+            route_local_kernel<kRankMaxK><<<dim3((unsigned)ntiles), dim3(kRouteTile), lds,
+                                            stream>>>(ids, T, K, E, e_local, W, slots, nbits,
+                                                      rank, tile_cnt, prank, ecnt_tile, err);
     } else {
-        route_local_kernel<false><<<dim3((unsigned)ntiles), dim3(kRouteTile), 0, stream>>>(
+        route_local_kernel<0><<<dim3((unsigned)ntiles), dim3(kRouteTile), 0, stream>>>(
             ids, T, K, E, e_local, W, slots, nbits, rank, tile_cnt, nullptr, nullptr, err);
     }
     return hipGetLastError();

@@ -118,6 +118,17 @@ def test_parity_ranked_many_experts(T):
     run_full_parity(w, salt=19, ranked=True)
 
 
+@pytest.mark.parametrize("K,E,W,T", [(12, 32, 8, 600), (16, 64, 4, 600), (16, 64, 4, 200),
+                                     (9, 16, 8, 300)])
+def test_parity_ranked_wide_topk(K, E, W, T):
+    """More than 8 picks per token (up to the form's limit of 16), over
+    several routing tiles and within one: the code unrolled to 16 picks.
+    With e_local < K a token keeps at most e_local picks per rank."""
+    w = W1.scaled(W=W, E=E, K=K, T=T, cap=T, H=64)
+    say(f"[parity ranked] K={K} E={E} W={W} T={T}")
+    run_full_parity(w, salt=31, ranked=True)
+
+
 @pytest.mark.parametrize("name", ["dsv3_small", "decode", "many_route_tiles"])
 @pytest.mark.parametrize("fmt", ["fp8", "fp4"])
 def test_parity_ranked_quantised(name, fmt):
