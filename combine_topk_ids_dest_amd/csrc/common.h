@@ -165,11 +165,12 @@ __device__ __forceinline__ void load_row_ids(const int32_t* __restrict__ row, in
 
 // Destination mask of one token from its ids in registers (as
 // token_dest_mask).
+template <int KB = kRankMaxK>
 __device__ __forceinline__ uint64_t dest_mask_of(const int32_t (&v)[kRankMaxK], int E,
                                                  int e_local, uint32_t& bad) {
     uint64_t mask = 0;
 #pragma unroll
-    for (int k = 0; k < kRankMaxK; ++k) {
+    for (int k = 0; k < KB; ++k) {
         if (v[k] >= E) bad |= MOE_EP_ERR_ID_RANGE;
         if (v[k] >= 0 && v[k] < E) mask |= 1ull << ((uint32_t)v[k] / (uint32_t)e_local);
     }

@@ -484,9 +484,15 @@ __global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(
         if (RANKED == 2) {
 #pragma unroll
             for (int k = 0; k < kRankMaxK; ++k) key[k] = -1;
-            if (tid < T) load_row_ids(ids + (int64_t)tid * K, K, key);
-            mask = dest_mask_of(key, E, e_local, bad);
-            keep_keys(K, E, e_local, slots, key);
+            if (K <= 8) {
+                if (tid < T) load_row_ids<8>(ids + (int64_t)tid * K, K, key);
+                mask = dest_mask_of<8>(key, E, e_local, bad);
+                keep_keys<8>(K, E, e_local, slots, key);
+            } else {
+                if (tid < T) load_row_ids(ids + (int64_t)tid * K, K, key);
+                mask = dest_mask_of(key, E, e_local, bad);
+                keep_keys(K, E, e_local, slots, key);
+            }
             if (tid == (int64_t)blockIdx.x / nsplit) {
 #pragma unroll
                 for (int k = 0; k < kRankMaxK; ++k) s_q[k] = key[k];
