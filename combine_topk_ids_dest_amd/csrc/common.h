@@ -203,16 +203,6 @@ __device__ __forceinline__ void keep_keys(int K, int E, int e_local, int slots,
     }
 }
 
-// The kept picks of one token read from its row of ids (load_row_ids, then
-// keep_keys).
-template <int KB = kRankMaxK>
-__device__ __forceinline__ void kept_keys(const int32_t* __restrict__ row, int K, int E,
-                                          int e_local, int slots,
-                                          int32_t (&key)[kRankMaxK]) {
-    load_row_ids<KB>(row, K, key);
-    keep_keys<KB>(K, E, e_local, slots, key);
-}
-
 // Whether a token's kept ids hold an expert twice (only possible with
 // duplicate ids in its routing).
 template <int KB = kRankMaxK>

@@ -50,9 +50,20 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
 
     // Destination mask of the token: bit d set when some routed pick of the
     // token lives on rank d. Negative ids are padding; ids >= E are dropped.
+    // With the ranks the ids stay in registers for the kept ids below (one
+    // load of them instead of two).
     uint64_t mask = 0;
     uint32_t bad = 0;
-    if (t < T) mask = token_dest_mask(ids + t * K, K, E, e_local, bad);
+    int32_t key[kRankMaxK];
+    constexpr int KL = KB > 0 ? KB : 1;
+    if (KB > 0) {
+#pragma unroll
+        for (int k = 0; k < kRankMaxK; ++k) key[k] = -1;
+        if (t < T) load_row_ids<KL>(ids + t * K, K, key);
+        mask = dest_mask_of<KL>(key, E, e_local, bad);
+    } else if (t < T) {
+        mask = token_dest_mask(ids + t * K, K, E, e_local, bad);
+    }
     report(err, bad);
 
     for (int d = 0; d < W; ++d) {
@@ -91,10 +102,7 @@ __global__ __launch_bounds__(kRouteTile) void route_local_kernel(
         const int64_t t0 = (int64_t)blockIdx.x * kRouteTile;
         const int ntok = T - t0 < kRouteTile ? (int)(T - t0) : kRouteTile;
         const int n = ntok * K;
-        int32_t key[kRankMaxK];
-#pragma unroll
-        for (int k = 0; k < kRankMaxK; ++k) key[k] = -1;
-        if (t < T) kept_keys<KB>(ids + t * K, K, E, e_local, slots, key);
+        keep_keys<KB>(K, E, e_local, slots, key);
         const bool fast = E <= kRankMaskE && !__syncthreads_or(has_repeated_key<KB>(key));
         if (fast) {
             for (int i = tid; i < waves * E; i += kRouteTile) masks[i] = 0;
