@@ -230,12 +230,26 @@ __global__ __launch_bounds__(kBatchThreads) void batch_copy_kernel(
             const int64_t rb = P.row_bytes[0];
             const int64_t nvec = rb >> 4;
             const uint8_t* src = P.src[0] + s * P.src_stride[0] + (int64_t)slot * rb;
-            // (guarded loads: the compiler issues them one after another,
-            // which measured faster here than clamped loads all in flight)
+            if (ROWS == kRowsRanked) {
+                // all of the lane's loads in flight at once (buffer loads:
+                // no branch per load); the planning's only global loads
+                // follow them
+                const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, rb);
 #pragma unroll
-            for (int u = 0; u < kBatchUnroll; ++u) {
-                const int64_t i = tid + u * kBatchThreads;
-                if (i < nvec) x0[u] = ld_row<MOE_EP_BATCH_LD_NT>(src + i * 16);
+                for (int u = 0; u < kBatchUnroll; ++u)
+                    x0[u] = ld_row_buf<MOE_EP_BATCH_LD_NT>(
+                        rs, (uint32_t)(tid + u * kBatchThreads) * 16u);
+            } else {
+                // guarded loads: the compiler waits for each before the
+                // next, which measured faster for the scanned rows than
+                // all four in flight (buffer loads: DS-V3 148.9-149.5
+                // against 145.5 us), while the ranked rows gain from it
+                // (decode 10.6 against 11.2 us)
+#pragma unroll
+                for (int u = 0; u < kBatchUnroll; ++u) {
+                    const int64_t i = tid + u * kBatchThreads;
+                    if (i < nvec) x0[u] = ld_row<MOE_EP_BATCH_LD_NT>(src + i * 16);
+                }
             }
             first = kBatchThreads * kBatchUnroll;
         }

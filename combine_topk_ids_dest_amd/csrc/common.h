@@ -66,6 +66,26 @@ __device__ __forceinline__ void st_row(uint8_t* p, const u32x4& v) {
     else *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// A row of `bytes` bytes as a buffer resource (a longer row is covered up to
+// 2^31 - 1 bytes): a 16-byte load at an offset past that end returns zeros
+// without touching memory (the
+// buffer unit's range check), so lanes past the end need no branch and a
+// lane's loads are issued back to back. (Loads under a per-lane branch
+// whose registers stay live past it are each followed by a wait, for the
+// copy that merges the branch.) Dword 3 selects the 32-bit data format,
+// which raw buffer accesses need on gfx9.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0,
+                                             (int)(bytes < INT32_MAX ? bytes : INT32_MAX),
+                                             0x00020000);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_row_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0));
+}
+
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Quantize-on-pack arguments: bf16 rows in; codes and per-group scale rows
