@@ -319,3 +319,13 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and "--gpus must be 1" in r.stderr
+
+
+def test_bench_roofline_call_skips_the_receive_plan():
+    """The roofline names the call with the most time among those that move
+    rows; the receive plan (index data only) never is that call."""
+    import bench
+    assert bench.roofline_call({"pack": 11.5, "batch_plan": 12.0, "batch_copy": 9.0,
+                                "reduce": 11.0, "unpack": 7.0}) == "pack"
+    assert bench.roofline_call({"pack": 1.0, "batch": 3.0, "reduce": 2.0}) == "batch"
+    assert bench.roofline_call({"batch_plan": 1.0}) == "batch_plan"
