@@ -118,6 +118,17 @@ def test_parity_ranked_many_experts(T):
     run_full_parity(w, salt=19, ranked=True)
 
 
+@pytest.mark.parametrize("T", [200, 300])
+def test_parity_ranked_at_the_form_limits(T):
+    """K = 16 picks and E = 4096 experts, the largest the ranked form takes
+    (1,024 local experts on each of 4 ranks): the largest LDS tables of the
+    routing kernel's general ranks, the pack's own counts and the ranked
+    batch copy's count table."""
+    w = W1.scaled(W=4, E=4096, K=16, T=T, cap=T, H=64)
+    say(f"[parity ranked] limits K=16 E=4096 T={T}")
+    run_full_parity(w, salt=37, ranked=True)
+
+
 @pytest.mark.parametrize("K,E,W,T", [(12, 32, 8, 600), (16, 64, 4, 600), (16, 64, 4, 200),
                                      (9, 16, 8, 300)])
 def test_parity_ranked_wide_topk(K, E, W, T):
