@@ -121,6 +121,9 @@ MUTANTS = {
     "pick_ranks_one_based": (
         "                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];\n                send_ecnt[(int64_t)d * e_local + e] += 1;",
         "                send_ecnt[(int64_t)d * e_local + e] += 1;\n                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];"),
+    "pick_ranks_shared_across_destinations": (
+        "                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];\n                send_ecnt[(int64_t)d * e_local + e] += 1;",
+        "                send_rank[at] = send_ecnt[e];\n                send_ecnt[e] += 1;"),
     "pick_ranks_columns_reversed": (
         "            for (int32_t j = 0; j < slots; ++j) {\n                int64_t at = ((int64_t)d * cap + slot) * slots + j;\n                int32_t e = send_eloc[at];",
         "            for (int32_t j = slots - 1; j >= 0; --j) {\n                int64_t at = ((int64_t)d * cap + slot) * slots + j;\n                int32_t e = send_eloc[at];"),
