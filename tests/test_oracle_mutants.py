@@ -121,6 +121,12 @@ MUTANTS = {
     "pick_ranks_one_based": (
         "                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];\n                send_ecnt[(int64_t)d * e_local + e] += 1;",
         "                send_ecnt[(int64_t)d * e_local + e] += 1;\n                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];"),
+    "expert_num_tokens_unclamped": (
+        "        expert_num_tokens[e] = (int32_t)(n[e] < expert_cap ? n[e] : expert_cap);",
+        "        expert_num_tokens[e] = (int32_t)n[e];"),
+    "batch_padding_pick_flagged": (
+        "                if (e < 0) {\n                    recv_row[at] = -1;\n                    continue;",
+        "                if (e < 0) {\n                    err |= ORACLE_ERR_ELOC;\n                    recv_row[at] = -1;\n                    continue;"),
     "pick_ranks_shared_across_destinations": (
         "                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];\n                send_ecnt[(int64_t)d * e_local + e] += 1;",
         "                send_rank[at] = send_ecnt[e];\n                send_ecnt[e] += 1;"),
@@ -171,6 +177,7 @@ def _pin_battery():
         fp4pins.test_fp4_nonfinite_inputs,
         fp8pins.test_fp8_nonfinite_inputs,
         lambda: sanpins.test_sanitize_matches_brute_force_from_routing(4, 8, 3),
+        pins.test_error_bits,
         pins.test_golden_pick_ranks,
         pins.test_pick_ranks_random_micro,
         lambda: pins.test_pick_ranks_give_the_receive_rows(2),

@@ -598,6 +598,16 @@ def test_error_bits():
     assert b["err"] == oracle.ERR_ELOC | oracle.ERR_CNT
     assert b["recv_row"][0, :, 0].tolist() == [0, -1]
     assert b["expert_num_tokens"].tolist() == [1, 1]
+    # rows past expert_cap (only duplicate ids can get there) dropped (bit 3),
+    # and expert_num_tokens clamped to expert_cap: W = 1, e_local = 2, K = 2
+    # (slots 2), cap 2, so expert_cap = 2; both slots hold local expert 0
+    # twice, which asks for rows 0, 1, 2, 3 of it
+    cnt = np.array([2], np.int32)
+    eloc = np.array([[[0, 0], [0, 0]]], np.int32)
+    b = oracle.expert_batch(cnt, eloc, 1, 2, 2, 2)
+    assert b["err"] == oracle.ERR_ROWCAP
+    assert b["recv_row"][0].tolist() == [[0, 1], [-1, -1]]
+    assert b["expert_num_tokens"].tolist() == [2, 0]
 
 
 # --------------------------------------------------------------------------
