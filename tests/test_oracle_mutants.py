@@ -121,6 +121,21 @@ MUTANTS = {
     "pick_ranks_one_based": (
         "                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];\n                send_ecnt[(int64_t)d * e_local + e] += 1;",
         "                send_ecnt[(int64_t)d * e_local + e] += 1;\n                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];"),
+    "reduce_sum_starts_at_negative_zero": (
+        "                float acc = 0.0f;\n                for (int32_t j = 0; j < slots; ++j) {",
+        "                float acc = -0.0f;\n                for (int32_t j = 0; j < slots; ++j) {"),
+    "unpack_sum_starts_at_negative_zero": (
+        "            float acc = 0.0f;\n            for (int32_t d = 0; d < W; ++d) {",
+        "            float acc = -0.0f;\n            for (int32_t d = 0; d < W; ++d) {"),
+    "pack_unused_weight_negative_zero": (
+        "                send_w[meta + j] = 0.0f;",
+        "                send_w[meta + j] = -0.0f;"),
+    "pack_no_pair_slot_zero": (
+        "                token_slot[t * W + d] = -1;\n                continue;",
+        "                token_slot[t * W + d] = 0;\n                continue;"),
+    "pack_slots_count_picks": (
+        "            count += 1;",
+        "            count += npicks;"),
     "expert_num_tokens_unclamped": (
         "        expert_num_tokens[e] = (int32_t)(n[e] < expert_cap ? n[e] : expert_cap);",
         "        expert_num_tokens[e] = (int32_t)n[e];"),
@@ -178,6 +193,7 @@ def _pin_battery():
         fp8pins.test_fp8_nonfinite_inputs,
         lambda: sanpins.test_sanitize_matches_brute_force_from_routing(4, 8, 3),
         pins.test_error_bits,
+        lambda: pins.test_reduce_sums_start_at_positive_zero("f32"),
         pins.test_golden_pick_ranks,
         pins.test_pick_ranks_random_micro,
         lambda: pins.test_pick_ranks_give_the_receive_rows(2),

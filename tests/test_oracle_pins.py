@@ -118,6 +118,30 @@ def test_golden_reduce(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_reduce_sums_start_at_positive_zero(dtype):
+    """The page's finalize() adds the weighted rows into a zeroed output, so
+    each slot's sum starts at +0.0 (reading A11): a slot whose only product
+    is -0.0, and a slot with no valid pick, both give +0.0 (bits 0), while
+    a negative product stays negative. W = 1, e_local = 1, K = 1, cap 4."""
+    cnt = np.array([4], np.int32)
+    eloc = np.array([[[0], [-1], [0], [0]]], np.int32)
+    w = np.array([[[1.0], [1.0], [0.0], [0.5]]], np.float32)
+    rows = np.array([[[0], [-1], [1], [2]]], np.int32)
+    Yf = np.array([[[-0.0, 2.0], [-1.0, -0.0], [-3.0, 0.0]]], np.float32)
+    Y = _bf16(Yf) if dtype == "bf16" else Yf
+    ret = oracle.combine_reduce(Y, cnt, eloc, w, rows, 1, 1, 1, 4)["ret"]
+    # slot 0: -0.0 * 1 = -0.0, +0.0 + -0.0 = +0.0; 2.0
+    # slot 1: no valid pick: +0.0, +0.0
+    # slot 2: -1.0 * 0.0 = -0.0 -> +0.0; -0.0 * 0.0 = -0.0 -> +0.0
+    # slot 3: -3.0 * 0.5 = -1.5; 0.0
+    exp = np.array([[[0.0, 2.0], [0.0, 0.0], [0.0, 0.0], [-1.5, 0.0]]], np.float32)
+    exp = _bf16(exp) if dtype == "bf16" else exp
+    got = ret.view(np.uint16 if dtype == "bf16" else np.uint32)
+    want = exp.view(np.uint16 if dtype == "bf16" else np.uint32)
+    assert np.array_equal(got, want), (got, want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_golden_unpack(dtype):
     G = _gold("worked_example.json")
     g = G["unpack"]
