@@ -97,6 +97,30 @@ MUTANTS = {
     "sanitize_keeps_negative_ids": (
         "if (e >= 0 && e < e_local)\n                        v = e;",
         "if (e < e_local)\n                        v = e;"),
+    "e4m3_saturates_to_nan": (
+        "    if (a >= 448.0)\n        return (uint8_t)(sign | 0x7Eu);",
+        "    if (a >= 448.0)\n        return (uint8_t)(sign | 0x7Fu);"),
+    "e2m1_nan_saturates": (
+        "    if (f != f)\n        return sign;",
+        "    if (f != f)\n        return (uint8_t)(sign | 7);"),
+    "capacities_slots_is_k": (
+        "    *slots = K < e_local ? K : e_local;",
+        "    *slots = K;"),
+    "capacities_expert_cap_is_cap": (
+        "    *expert_cap = max_num_tokens * (int64_t)W;",
+        "    *expert_cap = max_num_tokens;"),
+    "reduce_rounds_every_add_to_bf16": (
+        "                    acc = acc + prod;",
+        "                    acc = oracle_bf16_to_f32(oracle_f32_to_bf16(acc + prod));"),
+    "unpack_rounds_every_add_to_bf16": (
+        "                acc = acc + load_elem(back, dtype,\n                                      d * back_rank_stride + slot * back_row_stride + h);",
+        "                acc = oracle_bf16_to_f32(oracle_f32_to_bf16(acc + load_elem(back, dtype,\n                                      d * back_rank_stride + slot * back_row_stride + h)));"),
+    "sanitize_keeps_out_of_range_ids": (
+        "if (e >= 0 && e < e_local)\n                        v = e;\n                }\n                out[",
+        "if (e >= 0)\n                        v = e;\n                }\n                out["),
+    "sanitize_out_of_range_not_flagged": (
+        "                    if (e >= e_local)\n                        err |= ORACLE_ERR_ELOC;\n                    if (e >= 0 && e < e_local)\n                        v = e;",
+        "                    if (e >= 0 && e < e_local)\n                        v = e;"),
     "sanitize_keeps_row_past_count": (
         "                if (slot < cnt) {\n                    int32_t e = recv_eloc",
         "                if (slot <= cnt) {\n                    int32_t e = recv_eloc"),
@@ -121,6 +145,12 @@ MUTANTS = {
     "pick_ranks_one_based": (
         "                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];\n                send_ecnt[(int64_t)d * e_local + e] += 1;",
         "                send_ecnt[(int64_t)d * e_local + e] += 1;\n                send_rank[at] = send_ecnt[(int64_t)d * e_local + e];"),
+    "fp8_zero_group_scale_zero": (
+        "            const float s = amax > 0.0f ? amax / 448.0f : 1.0f;",
+        "            const float s = amax > 0.0f ? amax / 448.0f : 0.0f;"),
+    "fp8_amax_takes_nan": (
+        "                if (v > amax)\n                    amax = v;\n            }\n            const float s = amax",
+        "                if (!(v <= amax))\n                    amax = v;\n            }\n            const float s = amax"),
     "reduce_sum_starts_at_negative_zero": (
         "                float acc = 0.0f;\n                for (int32_t j = 0; j < slots; ++j) {",
         "                float acc = -0.0f;\n                for (int32_t j = 0; j < slots; ++j) {"),
