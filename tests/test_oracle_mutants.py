@@ -8,6 +8,7 @@ shows the pins are tight enough to catch what a plausible bug would change.
 """
 import multiprocessing as mp
 import subprocess
+import time
 
 import pytest
 
@@ -230,53 +231,108 @@ def _pin_battery():
     ]
 
 
-def _child(lib_path, q):
+def _child(libs, conn):
+    """Runs the pin battery against each (name, library) in turn and reports
+    ("start", name) before and ("done", name, failing pins) after each. The
+    reports go through a pipe, written at once, so none is lost when a
+    mutant crashes the process."""
     import faulthandler
     faulthandler.disable()          # a crashing mutant is an expected outcome
-    failed = 0
-    with oracle.use_library(lib_path):
-        for fn in _pin_battery():
-            try:
-                fn()
-            except Exception:       # an assertion or a rejected call
-                failed += 1
-    q.put(failed)
+    for name, lib_path in libs:
+        conn.send(("start", name))
+        failed = 0
+        with oracle.use_library(lib_path):
+            for fn in _pin_battery():
+                try:
+                    fn()
+                except Exception:   # an assertion or a rejected call
+                    failed += 1
+                    break           # one failing pin is enough
+        conn.send(("done", name, failed))
+    conn.close()
 
 
-def _failing_pins(lib_path):
-    """Number of failing pins; a mutant that crashes its (spawned, CPU-only)
-    process counts as caught. Spawned, not forked: the parent may already
-    run torch's CPU thread pool, which a forked child cannot use."""
+def _failing_pins(libs, limit_s=600):
+    """{name: failing pins} for each (name, library), all in one spawned,
+    CPU-only process, which saves starting one per mutant. A library that
+    crashes the process counts as caught (1000 failing pins), and the ones
+    after it run in a new process. Spawned, not forked: the parent may
+    already run torch's CPU thread pool, which a forked child cannot use."""
     ctx = mp.get_context("spawn")
-    q = ctx.Queue()
-    p = ctx.Process(target=_child, args=(lib_path, q))
-    p.start()
-    p.join(300)
-    if p.is_alive():
-        p.kill()
+    results = {}
+    pending = list(libs)
+    t0 = time.monotonic()
+    while pending:
+        rd, wr = ctx.Pipe(duplex=False)
+        p = ctx.Process(target=_child, args=(pending, wr))
+        p.start()
+        wr.close()                  # the child holds the only write end
+        current = None
+        while True:
+            if time.monotonic() - t0 > limit_s:
+                p.kill()
+                p.join()
+                raise AssertionError(f"pin batteries did not finish (at {current})")
+            if not rd.poll(1):
+                if p.is_alive():
+                    continue
+                if not rd.poll(0):
+                    break
+            try:
+                msg = rd.recv()
+            except EOFError:        # the child has ended and all is read
+                break
+            if msg[0] == "start":
+                current = msg[1]
+            else:
+                results[msg[1]] = msg[2]
+                current = None
         p.join()
-        raise AssertionError(f"pin battery did not finish for {lib_path}")
-    if p.exitcode != 0:
-        return 1_000
-    return q.get(timeout=10)
+        rd.close()
+        if current is not None:     # the process died inside this battery
+            results[current] = 1_000
+        left = [(n, lib) for n, lib in pending if n not in results]
+        if len(left) == len(pending):
+            raise AssertionError(f"the pin battery process ended without running "
+                                 f"(exit code {p.exitcode})")
+        pending = left
+    return results
+
+
+def _compile(name, src, tmp_dir):
+    c = tmp_dir / f"{name}.c"
+    c.write_text(src)
+    so = tmp_dir / f"{name}.so"
+    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c), "-lm"], check=True)
+    return str(so)
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    src = open(obuild.SRC).read()
+    tmp_dir = tmp_path_factory.mktemp("mutants")
+    libs, procs = [], []
+    for name in sorted(MUTANTS):    # the compilers run side by side
+        old, new = MUTANTS[name]
+        if src.count(old) != 1:
+            continue                # reported by the test of that mutant
+        c = tmp_dir / f"{name}.c"
+        c.write_text(src.replace(old, new))
+        so = tmp_dir / f"{name}.so"
+        procs.append(subprocess.Popen(["gcc", *obuild.CFLAGS, "-o", str(so), str(c), "-lm"]))
+        libs.append((name, str(so)))
+    for pr in procs:
+        assert pr.wait() == 0, "a mutant did not compile"
+    return _failing_pins(libs)
 
 
 def test_unmutated_copy_passes_battery(tmp_path):
-    src = open(obuild.SRC).read()
-    c = tmp_path / "m.c"
-    c.write_text(src)
-    so = tmp_path / "m.so"
-    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c), "-lm"], check=True)
-    assert _failing_pins(str(so)) == 0
+    so = _compile("unmutated", open(obuild.SRC).read(), tmp_path)
+    assert _failing_pins([("unmutated", so)]) == {"unmutated": 0}
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(name, tmp_path):
-    old, new = MUTANTS[name]
-    src = open(obuild.SRC).read()
-    assert src.count(old) == 1, f"mutation site of {name} not unique"
-    c = tmp_path / f"{name}.c"
-    c.write_text(src.replace(old, new))
-    so = tmp_path / f"{name}.so"
-    subprocess.run(["gcc", *obuild.CFLAGS, "-o", str(so), str(c), "-lm"], check=True)
-    assert _failing_pins(str(so)) > 0, f"no pin caught mutant {name}"
+def test_mutant_is_caught(name, mutant_results):
+    old, _ = MUTANTS[name]
+    assert open(obuild.SRC).read().count(old) == 1, f"mutation site of {name} not unique"
+    assert mutant_results[name] > 0, f"no pin caught mutant {name}"
