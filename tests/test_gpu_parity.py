@@ -118,6 +118,19 @@ def test_parity_ranked_many_experts(T):
     run_full_parity(w, salt=19, ranked=True)
 
 
+@pytest.mark.parametrize("ranked", [False, True])
+@pytest.mark.parametrize("H", [4104, 7000, 8192, 8200, 12000])
+def test_parity_rows_around_the_early_pass(H, ranked):
+    """Rows of one payload just above 8 KiB (513 vectors, where the batch
+    copy starts loading a row's first pass before planning), a ragged 875,
+    exactly the 1,024 vectors of that pass, one vector past it, and 1,500:
+    with the receiver's scan (guarded loads) and with the senders' ranks
+    (buffer loads whose range check stops at the row's end)."""
+    w = W1.scaled(W=4, E=16, K=4, T=300, cap=300, H=H)
+    say(f"[parity rows] H={H} ranked={ranked}")
+    run_full_parity(w, salt=41, ranked=ranked)
+
+
 @pytest.mark.parametrize("T", [200, 300])
 def test_parity_ranked_at_the_form_limits(T):
     """K = 16 picks and E = 4096 experts, the largest the ranked form takes
