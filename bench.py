@@ -348,6 +348,62 @@ def probe_copy(steps: int):
                       "gbps": gbps}), flush=True)
 
 
+def probe_stream(steps: int):
+    """HBM streams of 16-byte accesses in the read/write proportions of the
+    path's copy kernels (libmoe_ep_probe.so, built with the library): one
+    JSON line per stream with its rate over `steps` timed launches. These
+    are the practical ceilings the copy kernels are compared with."""
+    import ctypes
+    import torch
+    from combine_topk_ids_dest_amd import build as hb
+    if not os.path.exists(hb.PROBE_LIB):
+        raise SystemExit(f"{hb.PROBE_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(hb.PROBE_LIB)
+    f = lib.moe_ep_probe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    n = 1 << 31                                    # 2 GiB per buffer
+    dev = torch.device("cuda")
+    a = torch.full((n,), 1, dtype=torch.uint8, device=dev)
+    a2 = torch.full((n,), 2, dtype=torch.uint8, device=dev)
+    d = torch.empty(n, dtype=torch.uint8, device=dev)
+    d2 = torch.empty(n, dtype=torch.uint8, device=dev)
+    grid = 256 * 8
+    sink = torch.zeros(grid, dtype=torch.int32, device=dev)
+    chunk = 256 * 4 * 16
+    st = torch.cuda.current_stream()
+    # name, read main, extra read (fraction of n), write main, extra write
+    shapes = [("read", True, 0.0, False, 0.0), ("write", False, 0.0, True, 0.0),
+              ("copy_1_1", True, 0.0, True, 0.0),
+              ("copy_1_1.5 (batch_copy)", True, 0.0, True, 0.5),
+              ("copy_5_3 (combine_reduce)", True, 2.0 / 3.0, True, 0.0),
+              ("copy_1_2", True, 0.0, True, 1.0)]
+    for nt in (1, 0):
+        for name, rd, xr, wr, xw in shapes:
+            base = n
+            er = int(base * xr) // chunk * chunk
+            ew = int(base * xw) // chunk * chunk
+            args = (a.data_ptr() if rd else None, a2.data_ptr() if er else None, base, er,
+                    d.data_ptr() if wr else None, d2.data_ptr() if ew else None, ew,
+                    sink.data_ptr(), grid, nt, nt, ctypes.c_void_p(st.cuda_stream))
+            assert f(*args) == 0
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(steps):
+                f(*args)
+            e1.record(st)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            moved = (base if rd else 0) + er + (base if wr else 0) + ew
+            print(json.dumps({"probe": "stream", "shape": name, "nontemporal": bool(nt),
+                              "bytes_per_launch": moved, "ms": round(ms, 4),
+                              "gbps": round(moved / (ms / 1e3) / 1e9, 1)}), flush=True)
+    del a, a2, d, d2
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,7 +417,9 @@ def main():
                          "(profiles then see the warm calls only)")
     ap.add_argument("--cpu-shares", type=int, default=8,
                     help="logical-rank shares the CPU oracle is timed on")
-    ap.add_argument("--probe", choices=["copy"], default=None)
+    ap.add_argument("--probe", choices=["copy", "stream"], default=None,
+                    help="copy: torch's 1 GiB device copy (the counter scale); stream: HBM "
+                         "streams in the copy kernels' read/write proportions")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step in HIP graphs (one per phase and lane when the "
                          "ranks are spread over several lanes) and time their replays")
@@ -414,6 +472,9 @@ def main():
     torch.cuda.set_device(0)
     if args.probe == "copy":
         probe_copy(max(args.steps, 1))
+        return
+    if args.probe == "stream":
+        probe_stream(max(args.steps, 1))
         return
 
     w = wl.WORKLOADS[args.workload]

@@ -387,3 +387,38 @@ def test_combine_argument_checks():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         B.load(str(tmp_path / "absent.so"))
+
+
+def test_stream_probe_library_checks_its_arguments():
+    """The HBM stream probes of `bench.py --probe stream` live in their own
+    library, which exports the probe alone and rejects ranges that are not
+    whole 16 KiB chunks, extra ranges past the stream, missing buffers and
+    misaligned pointers before anything is launched."""
+    from combine_topk_ids_dest_amd import build as hb
+    assert os.path.exists(hb.PROBE_LIB), "run __graft_entry__.build() first"
+    out = subprocess.run(["nm", "-D", "--defined-only", hb.PROBE_LIB],
+                         capture_output=True, text=True, check=True).stdout
+    assert re.findall(r" T (moe_ep\w*)", out) == ["moe_ep_probe_stream"]
+    lib = ctypes.CDLL(hb.PROBE_LIB)
+    f = lib.moe_ep_probe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    P, C = 1 << 20, 16384          # a fake 16-byte-aligned address; one chunk
+    ok = dict(src=P, src2=None, n=4 * C, er=0, dst=P, dst2=None, ew=0, sink=P, grid=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["src"], a["src2"], a["n"], a["er"], a["dst"], a["dst2"], a["ew"],
+                 a["sink"], a["grid"], 1, 1, None)
+
+    assert call(n=4 * C + 16) == -1             # not whole chunks
+    assert call(n=0) == -1
+    assert call(er=C) == -1                     # extra read without src2
+    assert call(src2=P, er=5 * C) == -1         # extra read past the stream
+    assert call(ew=C) == -1                     # extra write without dst2
+    assert call(src=None, dst=None) == -1       # nothing to read or write
+    assert call(dst=None, sink=None) == -1      # a read needs its sink
+    assert call(dst=P + 8) == -1                # misaligned
+    assert call(grid=0) == -1
